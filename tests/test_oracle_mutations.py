@@ -1,0 +1,46 @@
+"""Plant plausible mistakes in copies of the oracle (on the CPU) and check that
+the pins catch each one.  This guards the pins themselves: a pin set that a
+dropped term or a swapped index survives would not prove the oracle right."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "pa_oracle.cpp")
+
+# (name, exact source text, planted replacement, pin tests expected to catch it)
+MUTATIONS = [
+    ("kv head = h % hkv", "h / G, hkv, d, bs, nb, scale, dtype);",
+     "h % hkv, hkv, d, bs, nb, scale, dtype);", "brute_force or head_groups"),
+    ("scale dropped", "s[j] = scale * acc;", "s[j] = acc;", "brute_force"),
+    ("slot offset shifted", "((static_cast<int64_t>(b) * bs + j % bs) * hkv + g) * d",
+     "((static_cast<int64_t>(b) * bs + (j + 1) % bs) * hkv + g) * d", "brute_force"),
+    ("K and V swapped in gather", "v_out[static_cast<int64_t>(j) * d + e] = widen(value_cache",
+     "v_out[static_cast<int64_t>(j) * d + e] = widen(key_cache", "brute_force"),
+    ("f16 exponent bias off by one", "static_cast<int>(expo) - 25", "static_cast<int>(expo) - 24",
+     "f16_widen"),
+    ("bf16 narrowing truncates", "const double r = std::nearbyint(units);\n    // r may",
+     "const double r = std::trunc(units);\n    // r may", "bf16_narrow or f16_narrow"),
+    ("merge weight dropped", "num = num + wp[p] * accp", "num = num + accp", "partitioned"),
+    ("cache write offset", "const int64_t dst = (b * bs + o) * row;",
+     "const int64_t dst = (o * bs + b) * row;", "cache_write or workload"),
+]
+
+
+@pytest.mark.parametrize("name,old,new,selector", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_planted_mistake_is_caught(tmp_path, name, old, new, selector):
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation anchor for '{name}' not found exactly once"
+    mutant = tmp_path / "pa_oracle.cpp"
+    mutant.write_text(src.replace(old, new))
+    (tmp_path / "pa_oracle.h").write_text(open(os.path.join(ROOT, "oracle", "pa_oracle.h")).read())
+    lib = tmp_path / "libmutant.so"
+    subprocess.run(["g++", "-O2", "-std=c++17", "-ffp-contract=off", "-fPIC", "-shared",
+                    "-pthread", str(mutant), "-o", str(lib)], check=True)
+    env = dict(os.environ, PA_ORACLE_LIB=str(lib))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py"), "-k", selector],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode == 1, f"planted mistake '{name}' survived the pins:\n{r.stdout[-2000:]}"
