@@ -1,0 +1,182 @@
+"""Paged decode attention benchmark on one MI355X.
+
+One step = the whole decode path for one batch: host block allocation and
+slot assignment (a1), the metadata copy to the GPU (a2), the cache write of
+the new tokens (a3) and the decode (split-context partitions + merge, or
+single pass, by workload).  Inputs are synthetic and seeded (workloads/),
+resident in HBM before the timed region.
+
+    python bench.py [--steps K] [--warmup W] [--config 3] [--block-size 16]
+
+Prints one JSON line on stdout.  value = algorithmic K/V bytes read by the
+timed steps' decodes / wall time of the timed steps (GB/s); the decode call
+alone is also timed with HIP events on the step's stream (roofline.achieved).
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "paged decode attention KV-read GB/s (% of HBM peak); seqs/s per layer"
+HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, AMD's published figure
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(w, budget_s):
+    """The oracle as it stands, timed on the host cores over whole sequences of
+    the same workload until about budget_s seconds of work."""
+    import oracle
+    from tests import oracle_side
+
+    o = oracle_side.build(w)
+    threads = len(os.sched_getaffinity(0))
+    per_tok = 2 * w.Hkv * w.D * w.elem_bytes
+    spent, done_bytes, seqs = 0.0, 0, []
+    order = np.random.default_rng(1234).permutation(w.S)
+    k = 0
+    while spent < budget_s and k < w.S:
+        batch = [int(i) for i in order[k:k + 4]]
+        k += len(batch)
+        pairs = np.array([[i, h] for i in batch for h in range(w.Hq)], np.int32)
+        t0 = time.perf_counter()
+        oracle.decode_pairs(o.q, o.key_cache, o.value_cache, o.block_tables, o.context_lens,
+                            w.scale, w.dtype, pairs, nthreads=threads)
+        spent += time.perf_counter() - t0
+        done_bytes += int(sum(int(w.lengths[i]) for i in batch)) * per_tok
+        seqs += batch
+    return {
+        "value": done_bytes / spent / 1e9,
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"{len(seqs)} of {w.S} sequences (all {w.Hq} q heads each, "
+                   f"{sum(int(w.lengths[i]) for i in seqs)} tokens), {spent:.1f} s; "
+                   "logical K/V bytes of the sample / oracle decode time"),
+        "seqs_per_s": len(seqs) / spent,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--block-size", type=int, default=None, choices=[16, 32])
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(decode attention would shard by sequence or by KV head; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from tests import gpu_side
+    from workloads import workload
+
+    torch.cuda.set_device(0)
+    overrides = {"block_size": args.block_size} if args.block_size else {}
+    w = workload(args.config, "full", **overrides)
+    log(f"[bench] {w.spec.name}; bs={w.bs}; S={w.S}; KV bytes/step ~{w.kv_bytes()/1e6:.1f} MB")
+    t0 = time.perf_counter()
+    g = gpu_side.build(w, extra_tokens=args.warmup + args.steps + 1)
+    log(f"[bench] inputs resident in HBM ({time.perf_counter() - t0:.1f} s)")
+    step = g.step
+    stream = step.stream
+    per_tok = g.cache.kv_bytes_per_token()
+    shared = (w.spec.prefix_seqs - 1) * w.spec.prefix_len if w.spec.prefix_seqs > 1 else 0
+
+    for _ in range(args.warmup):
+        step(g.q, g.k_new, g.v_new)
+    torch.cuda.synchronize()
+    log(f"[bench] {args.warmup} warmup steps done")
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    kv_bytes = 0
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for k in range(args.steps):
+        b = step.prepare()                                      # a1
+        step.upload(b)                                          # a2
+        ev[k][0].record(stream)
+        step.write_new(g.k_new, g.v_new)                        # a3
+        ev[k][1].record(stream)
+        step.attend(g.q)                                        # a4 | a5 + a6
+        ev[k][2].record(stream)
+        kv_bytes += (int(step.host_context_lens.astype(np.int64).sum()) - shared) * per_tok
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    log(f"[bench] {args.steps} timed steps done")
+
+    t_write = np.array([a.elapsed_time(b) for a, b, _ in ev]) * 1e-3      # s
+    t_decode = np.array([b.elapsed_time(c) for _, b, c in ev]) * 1e-3
+    kv_per_call = kv_bytes / args.steps
+    value = kv_bytes / elapsed / 1e9
+    dec_avg = float(t_decode.mean())
+    achieved = kv_per_call / dec_avg / 1e9
+    kernel_name = ("pa_decode_partitioned: partition kernel + merge kernel"
+                   if w.spec.kernel == "partitioned" else "pa_decode: single-pass kernel")
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "accumulate": "f32",
+        "data": "synthetic (seeded N(0,1) q/k/v, seeded lengths and block scatter)",
+        "config": {
+            "workload": w.spec.name,
+            "num_seqs": w.S, "num_q_heads": w.Hq, "num_kv_heads": w.Hkv, "head_dim": w.D,
+            "block_size": w.bs, "kernel": w.spec.kernel,
+            "partition_size": w.spec.partition_size if w.spec.kernel == "partitioned" else None,
+            "mean_context_len": float(step.host_context_lens.mean()),
+            "kv_bytes_per_step": int(kv_per_call),
+            "kv_bytes_counting": "unique (a shared prefix once)" if shared else "logical",
+        },
+        "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "seqs_per_s_per_layer": round(w.S * args.steps / elapsed, 1),
+        "decode_us": round(dec_avg * 1e6, 2),
+        "decode_us_p10_p90": [round(float(np.percentile(t_decode, 10)) * 1e6, 2),
+                              round(float(np.percentile(t_decode, 90)) * 1e6, 2)],
+        "cache_write_us": round(float(t_write.mean()) * 1e6, 2),
+        "decode_seqs_per_s": round(w.S / dec_avg, 1),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": kernel_name,
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+        },
+    }
+    del g
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a sample")
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,272 @@
+/*
+ * pa.h -- libpa: paged-KV-cache decode attention for AMD Instinct MI355X
+ * (gfx950), behind a plain C ABI.
+ *
+ * The method (pages cited by title and section):
+ *  - the KV cache is cut into fixed-size physical blocks and each sequence
+ *    reaches its tokens through a logical->physical block table; K and V live
+ *    in pools laid out [num_blocks][block_size][num_heads][head_dim]
+ *    ("LLM推理优化：vLLM PagedAttention深度解析与工程实践", §3.1 Block Table
+ *    and §4.1 注意力计算的修改; here num_heads is the number of KV heads);
+ *  - every decode step writes the new token's K/V into its slot and then the
+ *    new token's query attends over all cached tokens, softmax(q K^T s) V
+ *    (same page, §二; "vLLM 深度拆解：当大模型推理学会「分页注意力」",
+ *    §2.1, §3.1 and §3.3);
+ *  - a single-pass kernel for short contexts and a split-context kernel that
+ *    accumulates partial results per partition and merges them afterwards
+ *    (first page, §4.1: paged_attention_v1 / v2);
+ *  - query heads share KV heads in contiguous groups of G = Hq / Hkv
+ *    ("LLM推理优化技术地图：从KV Cache到量化与投机解码", §2.3 GQA);
+ *  - a host-side block manager: a free pool, per-sequence block tables,
+ *    blocks shared by reference with reference counts, copy-on-write
+ *    (first page, §3.2; second page, §3.3 BlockSpaceManager).
+ *
+ * Conventions for every call below:
+ *  - Device entry points take DEVICE pointers owned by the caller, enqueue
+ *    their kernels on `stream` (NULL = the null stream) and return without
+ *    synchronising.  libpa never allocates or frees device memory.
+ *  - Arguments are checked on the host before anything is enqueued; a bad
+ *    argument returns PA_ERR_INVALID_ARG (or PA_ERR_UNSUPPORTED for a valid
+ *    but unimplemented shape) and enqueues nothing.  Device-resident values
+ *    (slots, block ids, context lengths) cannot be checked on the host; the
+ *    kernels clamp or skip out-of-range values so that no access leaves the
+ *    caller's buffers, and the results for such inputs are unspecified.
+ *  - A failure reported by the HIP runtime at launch returns PA_ERR_HIP.
+ *  - pa_last_error() returns a message for the last non-OK status on the
+ *    calling thread.
+ *  - 16-bit float data (fp16 or bf16) is passed as raw 16-bit patterns; all
+ *    device buffers must be 16-byte aligned and densely packed in the stated
+ *    layout (row-major, innermost index last).
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = 1,
+  PA_ERR_OOM = 2,
+  PA_ERR_UNSUPPORTED = 3,
+  PA_ERR_HIP = 4
+} pa_status;
+
+typedef enum pa_dtype { PA_F16 = 0, PA_BF16 = 1 } pa_dtype;
+
+/* Message for the last non-OK status returned on this thread ("" if none).
+ * The string stays valid until the next libpa call on the same thread. */
+const char* pa_last_error(void);
+
+/* Library version string. */
+const char* pa_version(void);
+
+/* ------------------------------------------------------------------------
+ * Cache write (the new tokens' K/V into their slots).
+ * Follows: the new token's K/V are written back into the KV cache after
+ * each step ("vLLM 深度拆解：当大模型推理学会「分页注意力」", §3.1 data flow,
+ * and §3.3 append_slot: into the current block, or a fresh one when full).
+ *
+ *   key, value        [num_tokens][num_kv_heads][head_dim]   16-bit
+ *   key_cache,
+ *   value_cache       [num_blocks][block_size][num_kv_heads][head_dim]
+ *   slot_mapping      [num_tokens] int64; slot = block * block_size + offset.
+ *                     A negative slot means "write nothing for this token".
+ *
+ * Token t's K row and V row are copied bit for bit to
+ * cache[slot / block_size][slot % block_size][*][*].  Slots >= num_blocks *
+ * block_size are skipped on the device.  The same slot twice in one call is
+ * undefined (the allocator never produces it).  head_dim in {64, 128}; any
+ * positive block_size and num_kv_heads.  num_tokens == 0 is a no-op.
+ * ---------------------------------------------------------------------- */
+pa_status pa_reshape_and_cache(const void* key, const void* value,
+                               void* key_cache, void* value_cache,
+                               const int64_t* slot_mapping, int32_t num_tokens,
+                               int32_t num_kv_heads, int32_t head_dim,
+                               int32_t block_size, int32_t num_blocks,
+                               pa_dtype dtype, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Single-pass paged decode ("v1": the whole context of a sequence in one
+ * workgroup; meant for short contexts).
+ * Follows: softmax(Q K^T / sqrt(d)) V over the paged cache
+ * ("LLM推理优化：vLLM PagedAttention深度解析与工程实践", §二 formula and §4.1
+ * paged_attention_v1), for one query token per sequence.
+ *
+ *   out               [num_seqs][num_q_heads][head_dim]   16-bit (written)
+ *   query             [num_seqs][num_q_heads][head_dim]   16-bit
+ *   key_cache,
+ *   value_cache       [num_blocks][block_size][num_kv_heads][head_dim]
+ *   block_tables      [num_seqs][max_blocks_per_seq] int32 physical block ids
+ *   context_lens      [num_seqs] int32: tokens in the cache for each sequence,
+ *                     the new token included (it sits at position L-1)
+ *   max_context_len   an upper bound of every context_lens[i]
+ *                     (<= max_blocks_per_seq * block_size)
+ *   scale             multiplies q.k before the softmax (usually 1/sqrt(D))
+ *
+ * Query head h reads KV head h / (num_q_heads / num_kv_heads).
+ * out[i][h] = sum_j softmax_j(scale * q[i][h] . K_i[j]) V_i[j] over the
+ * context_lens[i] tokens of sequence i, gathered in logical order through
+ * block_tables[i]; computed in fp32 and rounded to nearest even at the end.
+ * A sequence with context_lens[i] == 0 gets an all-zero output row.
+ * Supported: head_dim in {64, 128}; block_size in {16, 32};
+ * num_q_heads % num_kv_heads == 0.
+ * ---------------------------------------------------------------------- */
+pa_status pa_decode(void* out, const void* query, const void* key_cache,
+                    const void* value_cache, const int32_t* block_tables,
+                    int32_t max_blocks_per_seq, const int32_t* context_lens,
+                    int32_t num_seqs, int32_t num_q_heads,
+                    int32_t num_kv_heads, int32_t head_dim,
+                    int32_t block_size, int32_t num_blocks,
+                    int32_t max_context_len, float scale, pa_dtype dtype,
+                    hipStream_t stream);
+
+/* Bytes of device workspace pa_decode_partitioned needs: per (sequence,
+ * q head, partition) an fp32 accumulator [head_dim], a max and a sum, for
+ * ceil(max_context_len / partition_size) partitions.  Returns 0 for invalid
+ * sizes. */
+size_t pa_decode_partitioned_workspace_size(int32_t num_seqs,
+                                            int32_t num_q_heads,
+                                            int32_t head_dim,
+                                            int32_t max_context_len,
+                                            int32_t partition_size);
+
+/* ------------------------------------------------------------------------
+ * Split-context paged decode ("v2": partial accumulation per partition,
+ * then a merge; first page, §4.1 paged_attention_v2).
+ * Arguments as pa_decode, plus:
+ *   partition_size    tokens per partition; a multiple of block_size,
+ *                     at most 1024.  Partition p of sequence i covers tokens
+ *                     [p*P, min(L_i, (p+1)*P)).
+ *   workspace         device buffer of at least
+ *                     pa_decode_partitioned_workspace_size(...) bytes,
+ *                     16-byte aligned; its contents on entry do not matter.
+ * Each partition computes, per q head, m = max of its logits,
+ * l = sum exp(logit - m) and acc = sum exp(logit - m) V; a second kernel
+ * merges: out = sum_p e^(m_p - M) acc_p / sum_p e^(m_p - M) l_p with
+ * M = max_p m_p.  Result as pa_decode up to fp32 rounding order.
+ * ---------------------------------------------------------------------- */
+pa_status pa_decode_partitioned(void* out, const void* query,
+                                const void* key_cache, const void* value_cache,
+                                const int32_t* block_tables,
+                                int32_t max_blocks_per_seq,
+                                const int32_t* context_lens, int32_t num_seqs,
+                                int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t block_size,
+                                int32_t num_blocks, int32_t max_context_len,
+                                float scale, pa_dtype dtype,
+                                int32_t partition_size, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Block copy for copy-on-write: for each pair k, block dst[k] of both pools
+ * becomes a bit-exact copy of block src[k] (all slots, heads and dims).
+ * Follows: a shared block is copied only when a sharer must modify it
+ * ("vLLM 深度拆解：当大模型推理学会「分页注意力」", §3.3 Copy-on-Write).
+ *   block_pairs       [num_pairs][2] int32 device array (src, dst)
+ * Pairs with an id outside [0, num_blocks) are skipped on the device.  A dst
+ * that is also another pair's src, or appears twice, is undefined.
+ * ---------------------------------------------------------------------- */
+pa_status pa_copy_blocks(void* key_cache, void* value_cache,
+                         const int32_t* block_pairs, int32_t num_pairs,
+                         int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, int32_t num_blocks,
+                         pa_dtype dtype, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Host block allocator (no device memory; not thread-safe: one caller at a
+ * time per handle).
+ * Follows: the BlockManager of "LLM推理优化：vLLM PagedAttention深度解析与
+ * 工程实践", §3.2 (free pool taken from its head, returned to its tail;
+ * allocate(seq, num_tokens) grows by ceil((num_tokens - have) / block_size)
+ * blocks and fails before taking any when the pool is short), with the
+ * append_slot / free / shared-block rules of "vLLM 深度拆解", §3.3 (blocks
+ * shared by reference carry a reference count and go back to the pool when
+ * it reaches zero; a shared block is copied before a sharer writes into it).
+ * Every call that returns PA_ERR_OOM or PA_ERR_INVALID_ARG leaves the
+ * allocator unchanged.
+ * ---------------------------------------------------------------------- */
+typedef struct pa_allocator pa_allocator;
+
+/* initial_free_order: a permutation of 0..num_blocks-1 giving the initial
+ * order of the free pool, or NULL for 0, 1, ..., num_blocks-1. */
+pa_status pa_alloc_create(int32_t num_blocks, int32_t block_size,
+                          const int32_t* initial_free_order,
+                          pa_allocator** out);
+void pa_alloc_destroy(pa_allocator* a);
+
+/* Make sequence seq_id (created if new) hold num_tokens tokens: take
+ * ceil((num_tokens - blocks_held * block_size) / block_size) blocks when its
+ * blocks do not cover num_tokens.  Never shrinks. */
+pa_status pa_alloc_allocate(pa_allocator* a, int64_t seq_id, int32_t num_tokens);
+
+/* Add one token to seq_id (created if new) and return its slot
+ * (block * block_size + offset).  If the token lands in a block shared with
+ * another sequence, the sequence gets a fresh block and *cow_src / *cow_dst
+ * name the block to copy (see pa_copy_blocks); otherwise both are -1.
+ * cow_src / cow_dst may be NULL. */
+pa_status pa_alloc_append_slot(pa_allocator* a, int64_t seq_id,
+                               int64_t* slot_out, int32_t* cow_src,
+                               int32_t* cow_dst);
+
+/* append_slot for n distinct sequences at once; all or nothing (PA_ERR_OOM
+ * before any change when the pool cannot serve the whole batch).
+ * slots_out [n]; cow_src / cow_dst [n] or NULL. */
+pa_status pa_alloc_append_slots(pa_allocator* a, const int64_t* seq_ids,
+                                int32_t n, int64_t* slots_out,
+                                int32_t* cow_src, int32_t* cow_dst);
+
+/* New sequence dst_seq references the first num_tokens tokens (a multiple
+ * of block_size, at most src's tokens) of src_seq: the same physical
+ * blocks, each reference count + 1. */
+pa_status pa_alloc_share_prefix(pa_allocator* a, int64_t src_seq,
+                                int64_t dst_seq, int32_t num_tokens);
+
+/* New sequence dst_seq references every block of src_seq (a partly filled
+ * last block included) and holds as many tokens. */
+pa_status pa_alloc_fork(pa_allocator* a, int64_t src_seq, int64_t dst_seq);
+
+/* Drop seq_id: each of its blocks loses a reference, in table order, and
+ * goes to the tail of the free pool when no reference is left. */
+pa_status pa_alloc_free(pa_allocator* a, int64_t seq_id);
+
+/* Copy seq_id's block table (physical ids in logical order) to out[0..cap);
+ * *n_out = number of blocks (PA_ERR_INVALID_ARG if cap is too small). */
+pa_status pa_alloc_block_table(const pa_allocator* a, int64_t seq_id,
+                               int32_t* out, int32_t cap, int32_t* n_out);
+
+/* Block tables of n sequences as a dense [n][max_blocks_per_seq] int32
+ * array, unused entries set to pad; context_lens_out [n] (may be NULL)
+ * receives each sequence's token count. */
+pa_status pa_alloc_block_tables(const pa_allocator* a, const int64_t* seq_ids,
+                                int32_t n, int32_t* out,
+                                int32_t max_blocks_per_seq, int32_t pad,
+                                int32_t* context_lens_out);
+
+/* Slots of positions [begin, end) of seq_id (each < its token count). */
+pa_status pa_alloc_slots(const pa_allocator* a, int64_t seq_id, int32_t begin,
+                         int32_t end, int64_t* out);
+
+/* Tokens held by seq_id, or -1 if unknown. */
+int32_t pa_alloc_num_tokens(const pa_allocator* a, int64_t seq_id);
+
+/* Blocks in the free pool. */
+int32_t pa_alloc_num_free(const pa_allocator* a);
+
+/* Reference count of a physical block, or -1 for an invalid id. */
+int32_t pa_alloc_refcount(const pa_allocator* a, int32_t block_id);
+
+/* The free pool in order (head first) into out[0..cap); *n_out = its size. */
+pa_status pa_alloc_free_list(const pa_allocator* a, int32_t* out, int32_t cap,
+                             int32_t* n_out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PA_H */

@@ -1,0 +1,27 @@
+"""Paged-KV-cache decode attention for AMD Instinct MI355X (gfx950).
+
+The product is libpa.so (HIP kernels + C ABI + host block allocator, declared
+in include/pa.h).  This package is its thin Python binding: the names follow
+the C ABI, torch tensors supply device memory and the current HIP stream.
+Importing fails loudly when libpa.so has not been built; there is no CPU
+fallback.
+"""
+from ._native import (  # noqa: F401
+    LIB_PATH,
+    PA_BF16,
+    PA_F16,
+    Allocator,
+    PaError,
+    PaOOM,
+    lib,
+    pa_copy_blocks,
+    pa_decode,
+    pa_decode_partitioned,
+    pa_decode_partitioned_workspace_size,
+    pa_reshape_and_cache,
+)
+
+__all__ = [
+    "Allocator", "PaError", "PaOOM", "PA_F16", "PA_BF16", "lib", "pa_copy_blocks", "pa_decode",
+    "pa_decode_partitioned", "pa_decode_partitioned_workspace_size", "pa_reshape_and_cache",
+]

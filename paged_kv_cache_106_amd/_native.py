@@ -1,0 +1,286 @@
+"""ctypes binding of libpa.so.  Argument marshalling only: every step of the
+decode path runs in libpa's HIP kernels or its C++ allocator.
+
+Device entry points take torch tensors that already live on the GPU (torch
+supplies device memory and the current stream) and keep the C names.
+The allocator is host-only and takes/returns numpy arrays.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpa.so")
+
+PA_OK, PA_ERR_INVALID_ARG, PA_ERR_OOM, PA_ERR_UNSUPPORTED, PA_ERR_HIP = range(5)
+PA_F16, PA_BF16 = 0, 1
+STATUS_NAMES = {0: "PA_OK", 1: "PA_ERR_INVALID_ARG", 2: "PA_ERR_OOM", 3: "PA_ERR_UNSUPPORTED",
+                4: "PA_ERR_HIP"}
+
+
+class PaError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+class PaOOM(PaError):
+    pass
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python paged_kv_cache_106_amd/build.py` "
+        "(there is no fallback implementation)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+_vp, _i32, _i64, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+_i32p = ctypes.POINTER(ctypes.c_int32)
+_i64p = ctypes.POINTER(ctypes.c_int64)
+
+
+def _sig(name, restype, argtypes):
+    f = getattr(_lib, name)
+    f.restype = restype
+    f.argtypes = argtypes
+    return f
+
+
+_sig("pa_last_error", ctypes.c_char_p, [])
+_sig("pa_version", ctypes.c_char_p, [])
+_sig("pa_reshape_and_cache", _i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp])
+_DEC = [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32]
+_sig("pa_decode", _i32, _DEC + [_vp])
+_sig("pa_decode_partitioned_workspace_size", _sz, [_i32, _i32, _i32, _i32, _i32])
+_sig("pa_decode_partitioned", _i32, _DEC + [_i32, _vp, _sz, _vp])
+_sig("pa_copy_blocks", _i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp])
+_sig("pa_alloc_create", _i32, [_i32, _i32, _i32p, ctypes.POINTER(_vp)])
+_sig("pa_alloc_destroy", None, [_vp])
+_sig("pa_alloc_allocate", _i32, [_vp, _i64, _i32])
+_sig("pa_alloc_append_slot", _i32, [_vp, _i64, _i64p, _i32p, _i32p])
+_sig("pa_alloc_append_slots", _i32, [_vp, _i64p, _i32, _i64p, _i32p, _i32p])
+_sig("pa_alloc_share_prefix", _i32, [_vp, _i64, _i64, _i32])
+_sig("pa_alloc_fork", _i32, [_vp, _i64, _i64])
+_sig("pa_alloc_free", _i32, [_vp, _i64])
+_sig("pa_alloc_block_table", _i32, [_vp, _i64, _i32p, _i32, _i32p])
+_sig("pa_alloc_block_tables", _i32, [_vp, _i64p, _i32, _i32p, _i32, _i32, _i32p])
+_sig("pa_alloc_slots", _i32, [_vp, _i64, _i32, _i32, _i64p])
+_sig("pa_alloc_num_tokens", _i32, [_vp, _i64])
+_sig("pa_alloc_num_free", _i32, [_vp])
+_sig("pa_alloc_refcount", _i32, [_vp, _i32])
+_sig("pa_alloc_free_list", _i32, [_vp, _i32p, _i32, _i32p])
+
+
+def lib():
+    return _lib
+
+
+def _check(status):
+    if status != PA_OK:
+        msg = _lib.pa_last_error().decode()
+        raise (PaOOM if status == PA_ERR_OOM else PaError)(status, msg)
+
+
+def _dtype_code(dtype):
+    if dtype in ("f16", PA_F16):
+        return PA_F16
+    if dtype in ("bf16", PA_BF16):
+        return PA_BF16
+    s = str(dtype)
+    if s == "torch.float16":
+        return PA_F16
+    if s == "torch.bfloat16":
+        return PA_BF16
+    raise ValueError(f"unsupported dtype {dtype!r}")
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def _dptr(t, name, elem_size=None):
+    if not getattr(t, "is_cuda", False):
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if elem_size is not None and t.element_size() != elem_size:
+        raise ValueError(f"{name} must have {elem_size}-byte elements")
+    return t.data_ptr()
+
+
+# ---------------------------------------------------------------------------
+# device entry points
+# ---------------------------------------------------------------------------
+
+def pa_reshape_and_cache(key, value, key_cache, value_cache, slot_mapping, dtype, stream=None):
+    """key/value [N][Hkv][D]; caches [NB][bs][Hkv][D]; slot_mapping int64 [N]."""
+    nb, bs, hkv, d = key_cache.shape
+    n = slot_mapping.shape[0]
+    if tuple(key.shape) != (n, hkv, d) or tuple(value.shape) != (n, hkv, d):
+        raise ValueError("key/value must be [N][Hkv][D] matching the caches and slot_mapping")
+    if tuple(value_cache.shape) != tuple(key_cache.shape):
+        raise ValueError("key_cache and value_cache shapes differ")
+    _check(_lib.pa_reshape_and_cache(
+        _dptr(key, "key", 2), _dptr(value, "value", 2), _dptr(key_cache, "key_cache", 2),
+        _dptr(value_cache, "value_cache", 2), _dptr(slot_mapping, "slot_mapping", 8), n, hkv, d,
+        bs, nb, _dtype_code(dtype), _stream(stream)))
+
+
+def _decode_args(out, query, key_cache, value_cache, block_tables, context_lens, max_context_len,
+                 scale, dtype):
+    s, hq, d = query.shape
+    nb, bs, hkv, d2 = key_cache.shape
+    if d2 != d or tuple(value_cache.shape) != tuple(key_cache.shape):
+        raise ValueError("cache shapes do not match the query")
+    if tuple(out.shape) != tuple(query.shape):
+        raise ValueError("out must have the query's shape")
+    if block_tables.dim() != 2 or block_tables.shape[0] != s or tuple(context_lens.shape) != (s,):
+        raise ValueError("block_tables must be [S][MB] and context_lens [S]")
+    mb = block_tables.shape[1]
+    return [_dptr(out, "out", 2), _dptr(query, "query", 2), _dptr(key_cache, "key_cache", 2),
+            _dptr(value_cache, "value_cache", 2), _dptr(block_tables, "block_tables", 4), mb,
+            _dptr(context_lens, "context_lens", 4), s, hq, hkv, d, bs, nb, int(max_context_len),
+            float(scale), _dtype_code(dtype)]
+
+
+def pa_decode(out, query, key_cache, value_cache, block_tables, context_lens, max_context_len,
+              scale, dtype, stream=None):
+    """Single-pass paged decode; writes out [S][Hq][D]."""
+    args = _decode_args(out, query, key_cache, value_cache, block_tables, context_lens,
+                        max_context_len, scale, dtype)
+    _check(_lib.pa_decode(*args, _stream(stream)))
+
+
+def pa_decode_partitioned_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len,
+                                         partition_size):
+    return int(_lib.pa_decode_partitioned_workspace_size(num_seqs, num_q_heads, head_dim,
+                                                         max_context_len, partition_size))
+
+
+def pa_decode_partitioned(out, query, key_cache, value_cache, block_tables, context_lens,
+                          max_context_len, scale, dtype, partition_size, workspace, stream=None):
+    """Split-context paged decode + merge; workspace is a uint8 GPU tensor."""
+    args = _decode_args(out, query, key_cache, value_cache, block_tables, context_lens,
+                        max_context_len, scale, dtype)
+    _check(_lib.pa_decode_partitioned(*args, int(partition_size), _dptr(workspace, "workspace"),
+                                      workspace.numel() * workspace.element_size(),
+                                      _stream(stream)))
+
+
+def pa_copy_blocks(key_cache, value_cache, block_pairs, dtype, stream=None):
+    """block_pairs: int32 GPU tensor [n][2] of (src, dst) block ids."""
+    nb, bs, hkv, d = key_cache.shape
+    n = block_pairs.shape[0]
+    _check(_lib.pa_copy_blocks(_dptr(key_cache, "key_cache", 2), _dptr(value_cache, "value_cache", 2),
+                               _dptr(block_pairs, "block_pairs", 4), n, hkv, d, bs, nb,
+                               _dtype_code(dtype), _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# host allocator
+# ---------------------------------------------------------------------------
+
+def _np_ptr(a, ctype):
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+class Allocator:
+    """Owns one pa_allocator handle; each method is one pa_alloc_* call."""
+
+    def __init__(self, num_blocks, block_size, initial_free_order=None):
+        self.num_blocks = int(num_blocks)
+        self.block_size = int(block_size)
+        h = _vp()
+        order = None
+        if initial_free_order is not None:
+            self._order = np.ascontiguousarray(initial_free_order, dtype=np.int32)
+            if self._order.shape != (self.num_blocks,):
+                raise ValueError("initial_free_order must have num_blocks entries")
+            order = _np_ptr(self._order, ctypes.c_int32)
+        _check(_lib.pa_alloc_create(self.num_blocks, self.block_size, order, ctypes.byref(h)))
+        self._h = h
+
+    def close(self):
+        if getattr(self, "_h", None):
+            _lib.pa_alloc_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+    def allocate(self, seq_id, num_tokens):
+        _check(_lib.pa_alloc_allocate(self._h, int(seq_id), int(num_tokens)))
+
+    def append_slot(self, seq_id):
+        """Returns (slot, cow) with cow None or (src_block, dst_block)."""
+        slot, src, dst = ctypes.c_int64(), ctypes.c_int32(), ctypes.c_int32()
+        _check(_lib.pa_alloc_append_slot(self._h, int(seq_id), ctypes.byref(slot),
+                                         ctypes.byref(src), ctypes.byref(dst)))
+        return slot.value, (None if src.value < 0 else (src.value, dst.value))
+
+    def append_slots(self, seq_ids, slots_out=None, cow_src=None, cow_dst=None):
+        """Batched append_slot; returns (slots int64[n], cow_src int32[n], cow_dst int32[n])."""
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        n = ids.shape[0]
+        slots = slots_out if slots_out is not None else np.empty(n, np.int64)
+        src = cow_src if cow_src is not None else np.empty(n, np.int32)
+        dst = cow_dst if cow_dst is not None else np.empty(n, np.int32)
+        _check(_lib.pa_alloc_append_slots(self._h, _np_ptr(ids, ctypes.c_int64), n,
+                                          _np_ptr(slots, ctypes.c_int64),
+                                          _np_ptr(src, ctypes.c_int32), _np_ptr(dst, ctypes.c_int32)))
+        return slots, src, dst
+
+    def share_prefix(self, src_seq, dst_seq, num_tokens):
+        _check(_lib.pa_alloc_share_prefix(self._h, int(src_seq), int(dst_seq), int(num_tokens)))
+
+    def fork(self, src_seq, dst_seq):
+        _check(_lib.pa_alloc_fork(self._h, int(src_seq), int(dst_seq)))
+
+    def free(self, seq_id):
+        _check(_lib.pa_alloc_free(self._h, int(seq_id)))
+
+    def block_table(self, seq_id):
+        n = ctypes.c_int32()
+        cap = self.num_blocks
+        out = np.empty(cap, np.int32)
+        _check(_lib.pa_alloc_block_table(self._h, int(seq_id), _np_ptr(out, ctypes.c_int32), cap,
+                                         ctypes.byref(n)))
+        return out[: n.value].copy()
+
+    def block_tables(self, seq_ids, max_blocks_per_seq, pad=0, out=None, context_lens_out=None):
+        """Dense [n][max_blocks_per_seq] int32 tables and int32 [n] token counts."""
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        n = ids.shape[0]
+        tbl = out if out is not None else np.empty((n, max_blocks_per_seq), np.int32)
+        lens = context_lens_out if context_lens_out is not None else np.empty(n, np.int32)
+        _check(_lib.pa_alloc_block_tables(self._h, _np_ptr(ids, ctypes.c_int64), n,
+                                          _np_ptr(tbl, ctypes.c_int32), int(max_blocks_per_seq),
+                                          int(pad), _np_ptr(lens, ctypes.c_int32)))
+        return tbl, lens
+
+    def slots(self, seq_id, begin, end):
+        out = np.empty(max(end - begin, 0), np.int64)
+        _check(_lib.pa_alloc_slots(self._h, int(seq_id), int(begin), int(end),
+                                   _np_ptr(out, ctypes.c_int64)))
+        return out
+
+    def num_tokens(self, seq_id):
+        return int(_lib.pa_alloc_num_tokens(self._h, int(seq_id)))
+
+    def num_free(self):
+        return int(_lib.pa_alloc_num_free(self._h))
+
+    def refcount(self, block_id):
+        return int(_lib.pa_alloc_refcount(self._h, int(block_id)))
+
+    def free_list(self):
+        n = ctypes.c_int32()
+        out = np.empty(self.num_blocks, np.int32)
+        _check(_lib.pa_alloc_free_list(self._h, _np_ptr(out, ctypes.c_int32), self.num_blocks,
+                                       ctypes.byref(n)))
+        return out[: n.value].copy()

@@ -1,0 +1,312 @@
+// pa_allocator.cpp -- libpa's host block allocator.
+//
+// The block manager of "LLM推理优化：vLLM PagedAttention深度解析与工程实践",
+// §3.2 (free pool, per-sequence physical block list, ceil growth, the pool
+// checked before any block is taken) with the sharing rules of
+// "vLLM 深度拆解：当大模型推理学会「分页注意力」", §3.3 (append_slot into the
+// current block or a fresh one, free returns blocks, shared blocks are
+// referenced and copied only before a sharer writes into one).
+//
+// Data structures, sized once at creation:
+//   free pool   ring buffer of num_blocks ids: pop at head, push at tail, O(1)
+//   refcount    one int32 per physical block (0 <=> the block is in the pool)
+//   sequences   hash map seq_id -> {block ids in logical order, token count}
+// Every failing call returns before changing anything.
+
+#include <cstdint>
+#include <cstring>
+#include <new>
+#include <string>
+#include <unordered_map>
+#include <unordered_set>
+#include <vector>
+
+#include "pa.h"
+#include "pa_internal.h"
+
+struct pa_allocator {
+  int32_t num_blocks = 0;
+  int32_t block_size = 0;
+  std::vector<int32_t> ring;  // free pool storage
+  int64_t head = 0;           // index of the pool's first id in ring
+  int64_t count = 0;          // ids in the pool
+  std::vector<int32_t> refcount;
+  struct Seq {
+    std::vector<int32_t> blocks;
+    int32_t tokens = 0;
+  };
+  std::unordered_map<int64_t, Seq> seqs;
+
+  int32_t pop_front() {
+    const int32_t id = ring[static_cast<size_t>(head)];
+    head = (head + 1) % num_blocks;
+    --count;
+    return id;
+  }
+  void push_back(int32_t id) {
+    ring[static_cast<size_t>((head + count) % num_blocks)] = id;
+    ++count;
+  }
+  int64_t capacity_of(const Seq& s) const {
+    return static_cast<int64_t>(s.blocks.size()) * block_size;
+  }
+  // blocks allocate(seq, n) would take
+  int64_t blocks_needed(const Seq* s, int64_t n) const {
+    const int64_t have = s ? capacity_of(*s) : 0;
+    if (have >= n) return 0;
+    return (n - have + block_size - 1) / block_size;
+  }
+  // does one more token of s need a block from the pool (new or copy-on-write)?
+  bool append_needs_block(const Seq* s) const {
+    if (!s) return true;
+    const int64_t p = s->tokens;
+    const int64_t idx = p / block_size;
+    if (idx >= static_cast<int64_t>(s->blocks.size())) return true;
+    return refcount[static_cast<size_t>(s->blocks[static_cast<size_t>(idx)])] > 1;
+  }
+  // append one token; the caller has checked that the pool can serve it
+  int64_t append(int64_t seq_id, int32_t* cow_src, int32_t* cow_dst) {
+    Seq& s = seqs[seq_id];
+    const int64_t p = s.tokens;
+    const size_t idx = static_cast<size_t>(p / block_size);
+    int32_t src = -1, dst = -1;
+    if (idx >= s.blocks.size()) {
+      const int32_t id = pop_front();
+      refcount[static_cast<size_t>(id)] = 1;
+      s.blocks.push_back(id);
+    } else if (refcount[static_cast<size_t>(s.blocks[idx])] > 1) {
+      src = s.blocks[idx];
+      dst = pop_front();
+      refcount[static_cast<size_t>(src)] -= 1;
+      refcount[static_cast<size_t>(dst)] = 1;
+      s.blocks[idx] = dst;
+    }
+    s.tokens = static_cast<int32_t>(p + 1);
+    if (cow_src) *cow_src = src;
+    if (cow_dst) *cow_dst = dst;
+    return static_cast<int64_t>(s.blocks[idx]) * block_size + p % block_size;
+  }
+};
+
+namespace {
+
+pa_status invalid(const char* msg) { return pa::fail(PA_ERR_INVALID_ARG, msg); }
+
+const pa_allocator::Seq* find(const pa_allocator* a, int64_t seq_id) {
+  auto it = a->seqs.find(seq_id);
+  return it == a->seqs.end() ? nullptr : &it->second;
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_alloc_create(int32_t num_blocks, int32_t block_size,
+                          const int32_t* initial_free_order,
+                          pa_allocator** out) {
+  pa::clear_error();
+  if (!out) return invalid("pa_alloc_create: out is NULL");
+  *out = nullptr;
+  if (num_blocks <= 0 || block_size <= 0)
+    return invalid("pa_alloc_create: num_blocks and block_size must be positive");
+  pa_allocator* a = new (std::nothrow) pa_allocator();
+  if (!a) return pa::fail(PA_ERR_OOM, "pa_alloc_create: host allocation failed");
+  a->num_blocks = num_blocks;
+  a->block_size = block_size;
+  a->ring.resize(static_cast<size_t>(num_blocks));
+  a->refcount.assign(static_cast<size_t>(num_blocks), 0);
+  if (initial_free_order) {
+    std::vector<char> seen(static_cast<size_t>(num_blocks), 0);
+    for (int32_t i = 0; i < num_blocks; ++i) {
+      const int32_t id = initial_free_order[i];
+      if (id < 0 || id >= num_blocks || seen[static_cast<size_t>(id)]) {
+        delete a;
+        return invalid("pa_alloc_create: initial_free_order is not a permutation");
+      }
+      seen[static_cast<size_t>(id)] = 1;
+      a->ring[static_cast<size_t>(i)] = id;
+    }
+  } else {
+    for (int32_t i = 0; i < num_blocks; ++i) a->ring[static_cast<size_t>(i)] = i;
+  }
+  a->head = 0;
+  a->count = num_blocks;
+  *out = a;
+  return PA_OK;
+}
+
+void pa_alloc_destroy(pa_allocator* a) { delete a; }
+
+pa_status pa_alloc_allocate(pa_allocator* a, int64_t seq_id, int32_t num_tokens) {
+  pa::clear_error();
+  if (!a) return invalid("pa_alloc_allocate: allocator is NULL");
+  if (num_tokens < 0) return invalid("pa_alloc_allocate: num_tokens < 0");
+  const pa_allocator::Seq* s = find(a, seq_id);
+  const int64_t need = a->blocks_needed(s, num_tokens);
+  if (need > a->count) return pa::fail(PA_ERR_OOM, "pa_alloc_allocate: not enough free blocks");
+  pa_allocator::Seq& seq = a->seqs[seq_id];
+  for (int64_t k = 0; k < need; ++k) {
+    const int32_t id = a->pop_front();
+    a->refcount[static_cast<size_t>(id)] = 1;
+    seq.blocks.push_back(id);
+  }
+  if (num_tokens > seq.tokens) seq.tokens = num_tokens;
+  return PA_OK;
+}
+
+pa_status pa_alloc_append_slot(pa_allocator* a, int64_t seq_id, int64_t* slot_out,
+                               int32_t* cow_src, int32_t* cow_dst) {
+  pa::clear_error();
+  if (!a || !slot_out) return invalid("pa_alloc_append_slot: NULL argument");
+  const pa_allocator::Seq* s = find(a, seq_id);
+  if (s && s->tokens == INT32_MAX) return invalid("pa_alloc_append_slot: sequence full");
+  if (a->append_needs_block(s) && a->count < 1)
+    return pa::fail(PA_ERR_OOM, "pa_alloc_append_slot: not enough free blocks");
+  *slot_out = a->append(seq_id, cow_src, cow_dst);
+  return PA_OK;
+}
+
+pa_status pa_alloc_append_slots(pa_allocator* a, const int64_t* seq_ids, int32_t n,
+                                int64_t* slots_out, int32_t* cow_src, int32_t* cow_dst) {
+  pa::clear_error();
+  if (!a || n < 0 || (n > 0 && (!seq_ids || !slots_out)))
+    return invalid("pa_alloc_append_slots: bad argument");
+  std::unordered_set<int64_t> distinct;
+  distinct.reserve(static_cast<size_t>(n) * 2);
+  int64_t need = 0;
+  for (int32_t k = 0; k < n; ++k) {
+    if (!distinct.insert(seq_ids[k]).second)
+      return invalid("pa_alloc_append_slots: sequence ids must be distinct");
+    const pa_allocator::Seq* s = find(a, seq_ids[k]);
+    if (s && s->tokens == INT32_MAX) return invalid("pa_alloc_append_slots: sequence full");
+    need += a->append_needs_block(s) ? 1 : 0;
+  }
+  if (need > a->count)
+    return pa::fail(PA_ERR_OOM, "pa_alloc_append_slots: not enough free blocks");
+  for (int32_t k = 0; k < n; ++k)
+    slots_out[k] = a->append(seq_ids[k], cow_src ? cow_src + k : nullptr,
+                             cow_dst ? cow_dst + k : nullptr);
+  return PA_OK;
+}
+
+pa_status pa_alloc_share_prefix(pa_allocator* a, int64_t src_seq, int64_t dst_seq,
+                                int32_t num_tokens) {
+  pa::clear_error();
+  if (!a) return invalid("pa_alloc_share_prefix: allocator is NULL");
+  const pa_allocator::Seq* s = find(a, src_seq);
+  if (!s) return invalid("pa_alloc_share_prefix: unknown source sequence");
+  if (find(a, dst_seq)) return invalid("pa_alloc_share_prefix: destination exists");
+  if (num_tokens <= 0 || num_tokens % a->block_size != 0 || num_tokens > s->tokens)
+    return invalid("pa_alloc_share_prefix: prefix must be block-aligned and within the source");
+  const size_t nblk = static_cast<size_t>(num_tokens / a->block_size);
+  std::vector<int32_t> blocks(s->blocks.begin(), s->blocks.begin() + static_cast<long>(nblk));
+  for (int32_t id : blocks) a->refcount[static_cast<size_t>(id)] += 1;
+  pa_allocator::Seq& d = a->seqs[dst_seq];
+  d.blocks = std::move(blocks);
+  d.tokens = num_tokens;
+  return PA_OK;
+}
+
+pa_status pa_alloc_fork(pa_allocator* a, int64_t src_seq, int64_t dst_seq) {
+  pa::clear_error();
+  if (!a) return invalid("pa_alloc_fork: allocator is NULL");
+  const pa_allocator::Seq* s = find(a, src_seq);
+  if (!s) return invalid("pa_alloc_fork: unknown source sequence");
+  if (find(a, dst_seq)) return invalid("pa_alloc_fork: destination exists");
+  pa_allocator::Seq copy = *s;
+  for (int32_t id : copy.blocks) a->refcount[static_cast<size_t>(id)] += 1;
+  a->seqs[dst_seq] = std::move(copy);
+  return PA_OK;
+}
+
+pa_status pa_alloc_free(pa_allocator* a, int64_t seq_id) {
+  pa::clear_error();
+  if (!a) return invalid("pa_alloc_free: allocator is NULL");
+  auto it = a->seqs.find(seq_id);
+  if (it == a->seqs.end()) return PA_OK;
+  for (int32_t id : it->second.blocks) {
+    int32_t& rc = a->refcount[static_cast<size_t>(id)];
+    rc -= 1;
+    if (rc == 0) a->push_back(id);
+  }
+  a->seqs.erase(it);
+  return PA_OK;
+}
+
+pa_status pa_alloc_block_table(const pa_allocator* a, int64_t seq_id, int32_t* out,
+                               int32_t cap, int32_t* n_out) {
+  pa::clear_error();
+  if (!a || !n_out) return invalid("pa_alloc_block_table: NULL argument");
+  const pa_allocator::Seq* s = find(a, seq_id);
+  if (!s) return invalid("pa_alloc_block_table: unknown sequence");
+  const int32_t n = static_cast<int32_t>(s->blocks.size());
+  *n_out = n;
+  if (n > cap || (n > 0 && !out)) return invalid("pa_alloc_block_table: output too small");
+  if (n) std::memcpy(out, s->blocks.data(), sizeof(int32_t) * static_cast<size_t>(n));
+  return PA_OK;
+}
+
+pa_status pa_alloc_block_tables(const pa_allocator* a, const int64_t* seq_ids, int32_t n,
+                                int32_t* out, int32_t max_blocks_per_seq, int32_t pad,
+                                int32_t* context_lens_out) {
+  pa::clear_error();
+  if (!a || n < 0 || max_blocks_per_seq <= 0 || (n > 0 && (!seq_ids || !out)))
+    return invalid("pa_alloc_block_tables: bad argument");
+  for (int32_t k = 0; k < n; ++k) {
+    const pa_allocator::Seq* s = find(a, seq_ids[k]);
+    if (!s) return invalid("pa_alloc_block_tables: unknown sequence");
+    if (static_cast<int64_t>(s->blocks.size()) > max_blocks_per_seq)
+      return invalid("pa_alloc_block_tables: a table is longer than max_blocks_per_seq");
+  }
+  for (int32_t k = 0; k < n; ++k) {
+    const pa_allocator::Seq* s = find(a, seq_ids[k]);
+    int32_t* row = out + static_cast<int64_t>(k) * max_blocks_per_seq;
+    const size_t nb = s->blocks.size();
+    if (nb) std::memcpy(row, s->blocks.data(), sizeof(int32_t) * nb);
+    for (size_t j = nb; j < static_cast<size_t>(max_blocks_per_seq); ++j) row[j] = pad;
+    if (context_lens_out) context_lens_out[k] = s->tokens;
+  }
+  return PA_OK;
+}
+
+pa_status pa_alloc_slots(const pa_allocator* a, int64_t seq_id, int32_t begin, int32_t end,
+                         int64_t* out) {
+  pa::clear_error();
+  if (!a) return invalid("pa_alloc_slots: allocator is NULL");
+  const pa_allocator::Seq* s = find(a, seq_id);
+  if (!s) return invalid("pa_alloc_slots: unknown sequence");
+  if (begin < 0 || end < begin || end > s->tokens || (end > begin && !out))
+    return invalid("pa_alloc_slots: range outside the sequence");
+  for (int32_t p = begin; p < end; ++p)
+    out[p - begin] = static_cast<int64_t>(s->blocks[static_cast<size_t>(p / a->block_size)]) *
+                         a->block_size + p % a->block_size;
+  return PA_OK;
+}
+
+int32_t pa_alloc_num_tokens(const pa_allocator* a, int64_t seq_id) {
+  if (!a) return -1;
+  const pa_allocator::Seq* s = find(a, seq_id);
+  return s ? s->tokens : -1;
+}
+
+int32_t pa_alloc_num_free(const pa_allocator* a) {
+  return a ? static_cast<int32_t>(a->count) : -1;
+}
+
+int32_t pa_alloc_refcount(const pa_allocator* a, int32_t block_id) {
+  if (!a || block_id < 0 || block_id >= a->num_blocks) return -1;
+  return a->refcount[static_cast<size_t>(block_id)];
+}
+
+pa_status pa_alloc_free_list(const pa_allocator* a, int32_t* out, int32_t cap, int32_t* n_out) {
+  pa::clear_error();
+  if (!a || !n_out) return invalid("pa_alloc_free_list: NULL argument");
+  *n_out = static_cast<int32_t>(a->count);
+  if (a->count > cap || (a->count > 0 && !out))
+    return invalid("pa_alloc_free_list: output too small");
+  for (int64_t k = 0; k < a->count; ++k)
+    out[k] = a->ring[static_cast<size_t>((a->head + k) % a->num_blocks)];
+  return PA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,256 @@
+// pa_api.hip -- libpa's C ABI for the device entry points: host-side argument
+// checks, workspace layout and kernel dispatch.  No device memory is
+// allocated here and no stream is synchronised.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <string>
+
+#include "pa.h"
+#include "pa_internal.h"
+
+namespace pa {
+
+namespace {
+thread_local std::string g_last_error;
+
+constexpr int32_t kSingleChunk = 512;     // tokens per LDS pass of the single-pass kernel
+constexpr int32_t kMaxPartition = 1024;
+constexpr int32_t kMaxGrid = 65535;        // grid y / z limit
+
+bool aligned(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
+
+int log2_exact(int32_t v) {
+  int k = 0;
+  while ((1 << k) < v) ++k;
+  return (1 << k) == v ? k : -1;
+}
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+struct Workspace {
+  size_t acc_off, max_off, sum_off, total;
+};
+
+Workspace workspace_layout(int64_t num_seqs, int64_t num_q_heads, int64_t head_dim,
+                           int64_t num_parts) {
+  const size_t rows = static_cast<size_t>(num_seqs * num_q_heads * num_parts);
+  Workspace w{};
+  w.acc_off = 0;
+  w.max_off = round_up(rows * static_cast<size_t>(head_dim) * sizeof(float), 256);
+  w.sum_off = w.max_off + round_up(rows * sizeof(float), 256);
+  w.total = w.sum_off + round_up(rows * sizeof(float), 256);
+  return w;
+}
+
+int (*attn_launcher(pa_dtype dtype, int32_t head_dim))(int, const AttnParams&, hipStream_t) {
+  if (dtype == PA_F16) return head_dim == 64 ? launch_attn_f16_d64 : launch_attn_f16_d128;
+  return head_dim == 64 ? launch_attn_bf16_d64 : launch_attn_bf16_d128;
+}
+
+// Shared checks of pa_decode / pa_decode_partitioned; fills p on success.
+pa_status check_decode(void* out, const void* query, const void* key_cache,
+                       const void* value_cache, const int32_t* block_tables,
+                       int32_t max_blocks_per_seq, const int32_t* context_lens,
+                       int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                       int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                       int32_t max_context_len, float scale, pa_dtype dtype, AttnParams* p) {
+  if (dtype != PA_F16 && dtype != PA_BF16) return fail(PA_ERR_INVALID_ARG, "unknown dtype");
+  if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "num_seqs < 0");
+  if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0)
+    return fail(PA_ERR_INVALID_ARG, "num_q_heads must be a positive multiple of num_kv_heads");
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PA_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (block_size != 16 && block_size != 32)
+    return fail(PA_ERR_UNSUPPORTED, "block_size must be 16 or 32");
+  if (num_blocks <= 0) return fail(PA_ERR_INVALID_ARG, "num_blocks must be positive");
+  if (max_blocks_per_seq <= 0) return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq must be positive");
+  if (max_context_len < 0 ||
+      static_cast<int64_t>(max_context_len) > static_cast<int64_t>(max_blocks_per_seq) * block_size)
+    return fail(PA_ERR_INVALID_ARG, "max_context_len outside [0, max_blocks_per_seq * block_size]");
+  if (static_cast<int64_t>(max_blocks_per_seq) * block_size > INT32_MAX)
+    return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq * block_size overflows int32");
+  if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale is not finite");
+  if (num_seqs > kMaxGrid) return fail(PA_ERR_UNSUPPORTED, "num_seqs above 65535");
+  if (static_cast<int64_t>(num_seqs) * num_q_heads > INT32_MAX)
+    return fail(PA_ERR_UNSUPPORTED, "num_seqs * num_q_heads overflows int32");
+  if (num_seqs > 0) {
+    if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens)
+      return fail(PA_ERR_INVALID_ARG, "NULL device pointer");
+    if (!aligned(out, 16) || !aligned(query, 16) || !aligned(key_cache, 16) ||
+        !aligned(value_cache, 16) || !aligned(block_tables, 4) || !aligned(context_lens, 4))
+      return fail(PA_ERR_INVALID_ARG, "device buffers must be 16-byte aligned (metadata 4-byte)");
+  }
+  const int32_t group = num_q_heads / num_kv_heads;
+  const int32_t chunks = (group + 7) / 8;
+  const int32_t gt = (group + chunks - 1) / chunks;
+  if (static_cast<int64_t>(num_kv_heads) * chunks > kMaxGrid)
+    return fail(PA_ERR_UNSUPPORTED, "num_kv_heads * head chunks above 65535");
+
+  *p = AttnParams{};
+  p->out = out;
+  p->q = query;
+  p->k_cache = key_cache;
+  p->v_cache = value_cache;
+  p->block_tables = block_tables;
+  p->context_lens = context_lens;
+  p->block_stride = static_cast<int64_t>(block_size) * num_kv_heads * head_dim;
+  p->mb = max_blocks_per_seq;
+  p->num_seqs = num_seqs;
+  p->num_q_heads = num_q_heads;
+  p->num_kv_heads = num_kv_heads;
+  p->group = group;
+  p->heads_per_wg = gt;
+  p->head_chunks = chunks;
+  p->block_size = block_size;
+  p->log2_block_size = log2_exact(block_size);
+  p->num_blocks = num_blocks;
+  p->scale_log2 = scale * 1.4426950408889634f;
+  return PA_OK;
+}
+
+pa_status launched(int err, const char* what) {
+  if (err != 0) {
+    std::string msg = std::string(what) + ": " + hipGetErrorString(static_cast<hipError_t>(err));
+    g_last_error = msg;
+    return PA_ERR_HIP;
+  }
+  return PA_OK;
+}
+
+}  // namespace
+
+pa_status fail(pa_status st, const char* msg) {
+  g_last_error = msg;
+  return st;
+}
+
+void clear_error() { g_last_error.clear(); }
+
+}  // namespace pa
+
+using pa::fail;
+
+extern "C" {
+
+const char* pa_last_error(void) { return pa::g_last_error.c_str(); }
+
+const char* pa_version(void) { return "libpa 0.1 (gfx950)"; }
+
+pa_status pa_reshape_and_cache(const void* key, const void* value, void* key_cache,
+                               void* value_cache, const int64_t* slot_mapping, int32_t num_tokens,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               int32_t num_blocks, pa_dtype dtype, hipStream_t stream) {
+  pa::clear_error();
+  if (dtype != PA_F16 && dtype != PA_BF16) return fail(PA_ERR_INVALID_ARG, "unknown dtype");
+  if (num_tokens < 0) return fail(PA_ERR_INVALID_ARG, "num_tokens < 0");
+  if (num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
+    return fail(PA_ERR_INVALID_ARG, "num_kv_heads, head_dim, block_size, num_blocks must be positive");
+  if (head_dim % 8 != 0) return fail(PA_ERR_UNSUPPORTED, "head_dim must be a multiple of 8");
+  if (num_tokens == 0) return PA_OK;
+  if (!key || !value || !key_cache || !value_cache || !slot_mapping)
+    return fail(PA_ERR_INVALID_ARG, "NULL device pointer");
+  if (!pa::aligned(key, 16) || !pa::aligned(value, 16) || !pa::aligned(key_cache, 16) ||
+      !pa::aligned(value_cache, 16) || !pa::aligned(slot_mapping, 8))
+    return fail(PA_ERR_INVALID_ARG, "device buffers must be 16-byte aligned (slots 8-byte)");
+  const int64_t row = static_cast<int64_t>(num_kv_heads) * head_dim;   // elements per token
+  const int64_t chunks_per_tok = row / 8;
+  if (chunks_per_tok > INT32_MAX) return fail(PA_ERR_UNSUPPORTED, "token row too large");
+  const int64_t num_chunks = static_cast<int64_t>(num_tokens) * chunks_per_tok;
+  if ((num_chunks + 255) / 256 > INT32_MAX) return fail(PA_ERR_UNSUPPORTED, "too many tokens");
+  const int64_t num_slots = static_cast<int64_t>(num_blocks) * block_size;
+  return pa::launched(pa::launch_cache_write(key, value, key_cache, value_cache, slot_mapping,
+                                             num_tokens, static_cast<int32_t>(chunks_per_tok),
+                                             num_slots, stream),
+                      "pa_reshape_and_cache");
+}
+
+pa_status pa_decode(void* out, const void* query, const void* key_cache, const void* value_cache,
+                    const int32_t* block_tables, int32_t max_blocks_per_seq,
+                    const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                    int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                    int32_t num_blocks, int32_t max_context_len, float scale, pa_dtype dtype,
+                    hipStream_t stream) {
+  pa::clear_error();
+  pa::AttnParams p;
+  const pa_status st = pa::check_decode(out, query, key_cache, value_cache, block_tables,
+                                        max_blocks_per_seq, context_lens, num_seqs, num_q_heads,
+                                        num_kv_heads, head_dim, block_size, num_blocks,
+                                        max_context_len, scale, dtype, &p);
+  if (st != PA_OK) return st;
+  if (num_seqs == 0) return PA_OK;
+  p.chunk = pa::kSingleChunk;
+  return pa::launched(pa::attn_launcher(dtype, head_dim)(0, p, stream), "pa_decode");
+}
+
+size_t pa_decode_partitioned_workspace_size(int32_t num_seqs, int32_t num_q_heads,
+                                            int32_t head_dim, int32_t max_context_len,
+                                            int32_t partition_size) {
+  if (num_seqs < 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len < 0 ||
+      partition_size <= 0)
+    return 0;
+  const int64_t parts = (static_cast<int64_t>(max_context_len) + partition_size - 1) / partition_size;
+  return pa::workspace_layout(num_seqs, num_q_heads, head_dim, parts).total;
+}
+
+pa_status pa_decode_partitioned(void* out, const void* query, const void* key_cache,
+                                const void* value_cache, const int32_t* block_tables,
+                                int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                int32_t max_context_len, float scale, pa_dtype dtype,
+                                int32_t partition_size, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream) {
+  pa::clear_error();
+  pa::AttnParams p;
+  const pa_status st = pa::check_decode(out, query, key_cache, value_cache, block_tables,
+                                        max_blocks_per_seq, context_lens, num_seqs, num_q_heads,
+                                        num_kv_heads, head_dim, block_size, num_blocks,
+                                        max_context_len, scale, dtype, &p);
+  if (st != PA_OK) return st;
+  if (partition_size < block_size || partition_size > pa::kMaxPartition ||
+      partition_size % block_size != 0)
+    return fail(PA_ERR_INVALID_ARG,
+                "partition_size must be a multiple of block_size in [block_size, 1024]");
+  if (num_seqs == 0) return PA_OK;
+  const int64_t parts = (static_cast<int64_t>(max_context_len) + partition_size - 1) / partition_size;
+  const pa::Workspace w = pa::workspace_layout(num_seqs, num_q_heads, head_dim, parts);
+  if (!workspace || !pa::aligned(workspace, 16))
+    return fail(PA_ERR_INVALID_ARG, "workspace must be a 16-byte aligned device buffer");
+  if (workspace_bytes < w.total) return fail(PA_ERR_INVALID_ARG, "workspace too small");
+  char* ws = static_cast<char*>(workspace);
+  p.part_acc = reinterpret_cast<float*>(ws + w.acc_off);
+  p.part_max = reinterpret_cast<float*>(ws + w.max_off);
+  p.part_sum = reinterpret_cast<float*>(ws + w.sum_off);
+  p.chunk = partition_size;
+  p.num_parts = static_cast<int32_t>(parts);
+  auto launch = pa::attn_launcher(dtype, head_dim);
+  if (parts > 0) {
+    const pa_status s1 = pa::launched(launch(1, p, stream), "pa_decode_partitioned (partitions)");
+    if (s1 != PA_OK) return s1;
+  }
+  return pa::launched(launch(2, p, stream), "pa_decode_partitioned (merge)");
+}
+
+pa_status pa_copy_blocks(void* key_cache, void* value_cache, const int32_t* block_pairs,
+                         int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, int32_t num_blocks, pa_dtype dtype,
+                         hipStream_t stream) {
+  pa::clear_error();
+  if (dtype != PA_F16 && dtype != PA_BF16) return fail(PA_ERR_INVALID_ARG, "unknown dtype");
+  if (num_pairs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
+    return fail(PA_ERR_INVALID_ARG, "bad size");
+  if (head_dim % 8 != 0) return fail(PA_ERR_UNSUPPORTED, "head_dim must be a multiple of 8");
+  if (num_pairs == 0) return PA_OK;
+  if (num_pairs > pa::kMaxGrid) return fail(PA_ERR_UNSUPPORTED, "more than 65535 pairs");
+  if (!key_cache || !value_cache || !block_pairs) return fail(PA_ERR_INVALID_ARG, "NULL pointer");
+  if (!pa::aligned(key_cache, 16) || !pa::aligned(value_cache, 16) || !pa::aligned(block_pairs, 4))
+    return fail(PA_ERR_INVALID_ARG, "misaligned device buffer");
+  const int64_t chunks_per_block = static_cast<int64_t>(block_size) * num_kv_heads * head_dim / 8;
+  return pa::launched(pa::launch_copy_blocks(key_cache, value_cache, block_pairs, num_pairs,
+                                             chunks_per_block, num_blocks, stream),
+                      "pa_copy_blocks");
+}
+
+}  // extern "C"

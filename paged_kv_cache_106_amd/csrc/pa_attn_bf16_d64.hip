@@ -1,0 +1,8 @@
+// Attention kernels instantiated for bf16, head_dim 64.
+#include "pa_attn.h"
+
+namespace pa {
+int launch_attn_bf16_d64(int kind, const AttnParams& p, hipStream_t stream) {
+  return launch_attn<PA_BF16, 64>(kind, p, stream);
+}
+}  // namespace pa

@@ -1,0 +1,69 @@
+// pa_cache.hip -- the cache write and the copy-on-write block copy.
+//
+// Cache write: the new token's K/V go into its slot of the paged pools
+// ("vLLM 深度拆解：当大模型推理学会「分页注意力」", §3.1 data flow and §3.3
+// append_slot).  A token row of one pool is Hkv*D 16-bit values, contiguous
+// in the input [N][Hkv][D] and in the pool [NB][bs][Hkv][D] (slot s starts
+// at element s*Hkv*D), so each lane moves one 16-byte chunk: a coalesced
+// read and a coalesced write, no arithmetic on the values.
+#include <hip/hip_runtime.h>
+
+#include "pa_internal.h"
+
+namespace pa {
+
+__global__ __launch_bounds__(256) void cache_write_kernel(
+    const uint4* __restrict__ key, const uint4* __restrict__ value, uint4* __restrict__ k_cache,
+    uint4* __restrict__ v_cache, const int64_t* __restrict__ slots, int64_t num_chunks,
+    int32_t chunks_per_tok, int64_t num_slots) {
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (gid >= num_chunks) return;
+  const int64_t t = gid / chunks_per_tok;
+  const int64_t c = gid - t * chunks_per_tok;
+  const int64_t s = slots[t];
+  if (s < 0 || s >= num_slots) return;   // padding token, or out of range: no write
+  const int64_t dst = s * chunks_per_tok + c;
+  k_cache[dst] = key[gid];
+  v_cache[dst] = value[gid];
+}
+
+// Copy-on-write: block pair k copies src -> dst in both pools, 16 bytes per
+// lane; blockIdx.y selects the pair.
+__global__ __launch_bounds__(256) void copy_blocks_kernel(uint4* __restrict__ k_cache,
+                                                          uint4* __restrict__ v_cache,
+                                                          const int32_t* __restrict__ pairs,
+                                                          int64_t chunks_per_block,
+                                                          int32_t num_blocks) {
+  const int32_t src = pairs[2 * blockIdx.y];
+  const int32_t dst = pairs[2 * blockIdx.y + 1];
+  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
+  for (int64_t c = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+       c < chunks_per_block; c += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    k_cache[dst * chunks_per_block + c] = k_cache[src * chunks_per_block + c];
+    v_cache[dst * chunks_per_block + c] = v_cache[src * chunks_per_block + c];
+  }
+}
+
+int launch_cache_write(const void* key, const void* value, void* k_cache, void* v_cache,
+                       const int64_t* slots, int32_t n, int32_t chunks_per_tok,
+                       int64_t num_slots, hipStream_t stream) {
+  const int64_t num_chunks = static_cast<int64_t>(n) * chunks_per_tok;
+  const int64_t blocks = (num_chunks + 255) / 256;
+  hipLaunchKernelGGL(cache_write_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, stream,
+                     static_cast<const uint4*>(key), static_cast<const uint4*>(value),
+                     static_cast<uint4*>(k_cache), static_cast<uint4*>(v_cache), slots,
+                     num_chunks, chunks_per_tok, num_slots);
+  return static_cast<int>(hipGetLastError());
+}
+
+int launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int32_t num_pairs,
+                       int64_t chunks_per_block, int32_t num_blocks, hipStream_t stream) {
+  const int64_t want = (chunks_per_block + 255) / 256;
+  const uint32_t gx = static_cast<uint32_t>(want < 64 ? want : 64);
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3(gx, static_cast<uint32_t>(num_pairs)), dim3(256), 0,
+                     stream, static_cast<uint4*>(k_cache), static_cast<uint4*>(v_cache), pairs,
+                     chunks_per_block, num_blocks);
+  return static_cast<int>(hipGetLastError());
+}
+
+}  // namespace pa

@@ -1,0 +1,55 @@
+// pa_internal.h -- declarations shared by libpa's translation units (not
+// installed; the public interface is include/pa.h).
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "pa.h"
+
+namespace pa {
+
+// thread-local last-error message
+pa_status fail(pa_status st, const char* msg);
+void clear_error();
+
+// Parameters of the attention kernels, passed by value as one kernel argument.
+struct AttnParams {
+  void* out;                  // [S][Hq][D] 16-bit (single pass) or unused
+  const void* q;              // [S][Hq][D] 16-bit
+  const void* k_cache;        // [NB][bs][Hkv][D]
+  const void* v_cache;
+  const int32_t* block_tables;  // [S][mb]
+  const int32_t* context_lens;  // [S]
+  float* part_acc;            // [S][Hq][nP_max][D]   (split-context only)
+  float* part_max;            // [S][Hq][nP_max]
+  float* part_sum;            // [S][Hq][nP_max]
+  int64_t block_stride;       // elements per physical block = bs * Hkv * D
+  int32_t mb;                 // row stride of block_tables
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t group;              // G = Hq / Hkv
+  int32_t heads_per_wg;       // query heads one workgroup serves (<= 8)
+  int32_t head_chunks;        // ceil(G / heads_per_wg)
+  int32_t block_size;
+  int32_t log2_block_size;
+  int32_t num_blocks;
+  int32_t chunk;              // tokens per pass over LDS (= partition size)
+  int32_t num_parts;          // nP_max (split-context)
+  float scale_log2;           // scale * log2(e): logits live in the base-2 domain
+};
+
+// Launchers; each returns the hipError_t of its launch.
+// kind: 0 = single-pass decode, 1 = split-context partitions, 2 = merge.
+int launch_attn_f16_d64(int kind, const AttnParams& p, hipStream_t stream);
+int launch_attn_f16_d128(int kind, const AttnParams& p, hipStream_t stream);
+int launch_attn_bf16_d64(int kind, const AttnParams& p, hipStream_t stream);
+int launch_attn_bf16_d128(int kind, const AttnParams& p, hipStream_t stream);
+int launch_cache_write(const void* key, const void* value, void* k_cache, void* v_cache,
+                       const int64_t* slots, int32_t n, int32_t chunks_per_tok,
+                       int64_t num_slots, hipStream_t stream);
+int launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int32_t num_pairs,
+                       int64_t chunks_per_block, int32_t num_blocks, hipStream_t stream);
+
+}  // namespace pa

@@ -1,0 +1,167 @@
+"""A paged KV cache on one GPU and its decode step.
+
+``PagedKVCache`` owns the two device pools ([num_blocks][block_size][Hkv][D],
+16-bit) and the host block allocator.  ``DecodeStep`` runs one decode step for
+a fixed batch of sequences, in the order the pages describe for a step
+("vLLM 深度拆解：当大模型推理学会「分页注意力」", §3.1 data flow and §3.3):
+
+  a1  host: append_slot for every sequence -> slot mapping, block tables and
+      context lengths (libpa's allocator, written straight into pinned
+      host buffers);
+  a2  one async host-to-device copy of that metadata on the step's stream;
+  a3  pa_reshape_and_cache: the new tokens' K/V into their slots;
+  a4  pa_decode (single pass)  or  a5+a6  pa_decode_partitioned (+ merge).
+
+Pinned metadata buffers are double-buffered: the host prepares step k+1
+while the GPU still runs step k, and waits on an event only before reusing
+a buffer whose copy may not have run yet.
+"""
+import numpy as np
+import torch
+
+from . import _native as pa
+
+POISON = {"f16": 0x7E00, "bf16": 0x7FC0}   # quiet-NaN patterns for unused slots
+
+
+def _dtype(dtype):
+    return "f16" if pa._dtype_code(dtype) == pa.PA_F16 else "bf16"
+
+
+class PagedKVCache:
+    def __init__(self, num_blocks, block_size, num_kv_heads, head_dim, dtype,
+                 initial_free_order=None, device="cuda", poison=True):
+        self.num_blocks = int(num_blocks)
+        self.block_size = int(block_size)
+        self.num_kv_heads = int(num_kv_heads)
+        self.head_dim = int(head_dim)
+        self.dtype = _dtype(dtype)
+        self.device = torch.device(device)
+        shape = (self.num_blocks, self.block_size, self.num_kv_heads, self.head_dim)
+        fill = POISON[self.dtype] if poison else 0
+        self.key_cache = torch.full(shape, fill, dtype=torch.int16, device=self.device)
+        self.value_cache = torch.full(shape, fill, dtype=torch.int16, device=self.device)
+        self.allocator = pa.Allocator(self.num_blocks, self.block_size, initial_free_order)
+
+    # -- writing tokens that are already in the sequence (history) ----------------
+    def write_positions(self, spans, keys, values, stream=None):
+        """spans: list of (seq_id, begin, end); keys/values: [sum(end-begin)][Hkv][D]
+        16-bit arrays (numpy uint16/int16 or GPU tensors) in span order."""
+        slots = np.concatenate([self.allocator.slots(s, b, e) for s, b, e in spans]) \
+            if spans else np.empty(0, np.int64)
+        if slots.size == 0:
+            return
+        dev = self.device
+        k = keys if torch.is_tensor(keys) else torch.from_numpy(np.ascontiguousarray(keys).view(np.int16))
+        v = values if torch.is_tensor(values) else torch.from_numpy(np.ascontiguousarray(values).view(np.int16))
+        k = k.to(dev, non_blocking=False)
+        v = v.to(dev, non_blocking=False)
+        sl = torch.from_numpy(slots).to(dev)
+        pa.pa_reshape_and_cache(k, v, self.key_cache, self.value_cache, sl, self.dtype, stream)
+
+    def kv_bytes_per_token(self):
+        return 2 * self.num_kv_heads * self.head_dim * 2
+
+
+class DecodeStep:
+    """One decode step for the sequences ``seq_ids`` (fixed order)."""
+
+    def __init__(self, cache, seq_ids, num_q_heads, kernel="partitioned", partition_size=512,
+                 max_context_len=None, scale=None, stream=None):
+        self.cache = cache
+        self.seq_ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        self.S = int(self.seq_ids.shape[0])
+        self.num_q_heads = int(num_q_heads)
+        if kernel not in ("partitioned", "single"):
+            raise ValueError(kernel)
+        self.kernel = kernel
+        self.partition_size = int(partition_size)
+        bs = cache.block_size
+        if max_context_len is None:
+            max_context_len = cache.num_blocks * bs
+        self.max_context_len = int(max_context_len)
+        self.mb = -(-self.max_context_len // bs)
+        self.scale = float(np.float32(1.0 / np.sqrt(cache.head_dim))) if scale is None else float(scale)
+        self.stream = stream if stream is not None else torch.cuda.current_stream(cache.device)
+        dev = cache.device
+
+        # pinned host metadata, double-buffered, and its device twins
+        self._host = []
+        for _ in range(2):
+            meta = torch.empty(self._meta_bytes(), dtype=torch.uint8, pin_memory=True)
+            self._host.append(meta)
+        self._events = [None, None]
+        self._turn = 0
+        self._dev_meta = torch.empty(self._meta_bytes(), dtype=torch.uint8, device=dev)
+        self.slot_mapping, self.context_lens, self.block_tables = self._views(self._dev_meta)
+        self.out = torch.empty((self.S, self.num_q_heads, cache.head_dim), dtype=torch.int16,
+                               device=dev)
+        ws = pa.pa_decode_partitioned_workspace_size(self.S, self.num_q_heads, cache.head_dim,
+                                                     self.max_context_len, self.partition_size)
+        self.workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=dev)
+        self.host_context_lens = np.zeros(self.S, np.int32)
+
+    # metadata layout: slot_mapping int64 [S] | context_lens int32 [S] (+pad) | tables int32 [S][mb]
+    def _meta_bytes(self):
+        return 8 * self.S + 4 * (self.S + (self.S & 1)) + 4 * self.S * self.mb
+
+    def _views(self, buf):
+        S, mb = self.S, self.mb
+        o1 = 8 * S
+        o2 = o1 + 4 * (S + (S & 1))
+        sm = buf[:o1].view(torch.int64)
+        cl = buf[o1:o1 + 4 * S].view(torch.int32)
+        bt = buf[o2:o2 + 4 * S * mb].view(torch.int32).view(S, mb)
+        return sm, cl, bt
+
+    def prepare(self):
+        """a1: append one slot per sequence on the host and stage the metadata.
+        Returns the index of the pinned buffer holding it."""
+        b = self._turn
+        self._turn ^= 1
+        if self._events[b] is not None:
+            self._events[b].synchronize()          # its previous copy has run
+        sm, cl, bt = (t.numpy() for t in self._views(self._host[b]))
+        self.cache.allocator.append_slots(self.seq_ids, slots_out=sm)
+        self.cache.allocator.block_tables(self.seq_ids, self.mb, pad=0, out=bt, context_lens_out=cl)
+        self.host_context_lens[:] = cl
+        if int(cl.max(initial=0)) > self.max_context_len:
+            raise ValueError("a sequence outgrew max_context_len")
+        return b
+
+    def upload(self, b):
+        """a2: async copy of the staged metadata to the device, on the step's stream."""
+        with torch.cuda.stream(self.stream):
+            self._dev_meta.copy_(self._host[b], non_blocking=True)
+            ev = torch.cuda.Event()
+            ev.record(self.stream)
+        self._events[b] = ev
+
+    def write_new(self, k_new, v_new):
+        """a3: the new tokens' K/V ([S][Hkv][D] GPU tensors) into their slots."""
+        c = self.cache
+        pa.pa_reshape_and_cache(k_new, v_new, c.key_cache, c.value_cache, self.slot_mapping,
+                                c.dtype, self.stream)
+
+    def attend(self, q):
+        """a4 or a5+a6: decode for q [S][Hq][D] into self.out."""
+        c = self.cache
+        if self.kernel == "single":
+            pa.pa_decode(self.out, q, c.key_cache, c.value_cache, self.block_tables,
+                         self.context_lens, self.max_context_len, self.scale, c.dtype, self.stream)
+        else:
+            pa.pa_decode_partitioned(self.out, q, c.key_cache, c.value_cache, self.block_tables,
+                                     self.context_lens, self.max_context_len, self.scale, c.dtype,
+                                     self.partition_size, self.workspace, self.stream)
+        return self.out
+
+    def __call__(self, q, k_new, v_new):
+        """The whole step: a1, a2, a3, then the decode.  Asynchronous on the stream."""
+        b = self.prepare()
+        self.upload(b)
+        self.write_new(k_new, v_new)
+        return self.attend(q)
+
+    def kv_bytes(self):
+        """Logical K+V bytes the last prepared step's decode reads."""
+        return int(self.host_context_lens.astype(np.int64).sum()) * self.cache.kv_bytes_per_token()

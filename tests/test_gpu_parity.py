@@ -1,0 +1,265 @@
+"""GPU parity: libpa (through its C ABI) against the CPU oracle on the same
+seeded inputs.
+
+Bars: cache writes, slots and block tables bit-exact (whole pools compared,
+NaN-poisoned unused slots included); decode outputs within max|d| <= 1e-2 of
+the oracle's fp32 result and within 1 unit in the last place of its
+16-bit rounding.
+"""
+import gc
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_106_amd as pa
+from workloads import POISON, spec, workload, make_workload
+from tests import gpu_side, oracle_side
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-2
+
+
+def ordered(bits):
+    b = bits.astype(np.int32)
+    return np.where(b & 0x8000, -(b & 0x7FFF), b)
+
+
+def check_outputs(got_bits, ref32, ref_bits, dtype, label):
+    got = oracle.widen(got_bits, dtype)
+    assert np.isfinite(got).all(), f"{label}: non-finite output"
+    err = np.abs(got.astype(np.float64) - ref32.astype(np.float64)).max()
+    ulp = np.abs(ordered(got_bits) - ordered(ref_bits)).max()
+    print(f"[{label}] max|d|={err:.3e} max|out|={np.abs(ref32).max():.3f} max_ulp={ulp}", flush=True)
+    assert err <= TOL, f"{label}: max|d| {err} > {TOL}"
+    assert ulp <= 1, f"{label}: {ulp} ulp from the oracle's rounding"
+
+
+def free_gpu():
+    gc.collect()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def run_partitioned(g, w, P, max_context_len=None):
+    mcl = int(w.lengths.max()) if max_context_len is None else max_context_len
+    ws = torch.empty(max(pa.pa_decode_partitioned_workspace_size(w.S, w.Hq, w.D, mcl, P), 16),
+                     dtype=torch.uint8, device="cuda")
+    out = torch.full((w.S, w.Hq, w.D), 0x7FFF, dtype=torch.int16, device="cuda")
+    c, st = g.cache, g.step
+    pa.pa_decode_partitioned(out, g.q, c.key_cache, c.value_cache, st.block_tables, st.context_lens,
+                             mcl, w.scale, w.dtype, P, ws)
+    torch.cuda.synchronize()
+    return gpu_side.to_host16(out)
+
+
+def run_single(g, w):
+    out = torch.full((w.S, w.Hq, w.D), 0x7FFF, dtype=torch.int16, device="cuda")
+    c, st = g.cache, g.step
+    pa.pa_decode(out, g.q, c.key_cache, c.value_cache, st.block_tables, st.context_lens,
+                 int(w.lengths.max()), w.scale, w.dtype)
+    torch.cuda.synchronize()
+    return gpu_side.to_host16(out)
+
+
+def check_state(g, o, w, label):
+    """a1 + a3: tables, lengths, slots and both whole pools, bit for bit."""
+    st = g.step
+    mb = st.mb
+    tbl = st.block_tables.cpu().numpy()
+    assert np.array_equal(tbl[:, : o.block_tables.shape[1]], o.block_tables), f"{label}: tables"
+    assert np.array_equal(st.context_lens.cpu().numpy(), o.context_lens), f"{label}: lengths"
+    assert np.array_equal(st.slot_mapping.cpu().numpy(), o.new_slots), f"{label}: slots"
+    assert np.array_equal(gpu_side.to_host16(g.cache.key_cache), o.key_cache), f"{label}: K pool"
+    assert np.array_equal(gpu_side.to_host16(g.cache.value_cache), o.value_cache), f"{label}: V pool"
+    assert mb >= o.block_tables.shape[1]
+
+
+# ---------------------------------------------------------------------------
+# small variants of every workload: all outputs compared
+# ---------------------------------------------------------------------------
+
+SMALL = [(1, None), (2, None), (3, None), (4, None), (5, 16), (5, 32)]
+
+
+@pytest.mark.parametrize("cfg,bs", SMALL, ids=[f"cfg{c}-bs{b or 16}" for c, b in SMALL])
+def test_small_workloads(cfg, bs):
+    w = workload(cfg, "small", **({"block_size": bs} if bs else {}))
+    label = f"cfg{cfg} small bs{w.bs}"
+    print(f"\n[{label}] S={w.S} Hq={w.Hq} Hkv={w.Hkv} D={w.D} {w.dtype} lens={w.lengths.tolist()}",
+          flush=True)
+    g = gpu_side.build(w)
+    o = oracle_side.build(w)
+    check_state(g, o, w, label)
+    ref32, refT = oracle.decode(o.q, o.key_cache, o.value_cache, o.block_tables, o.context_lens,
+                                w.scale, w.dtype, nthreads=0)
+    check_outputs(run_single(g, w), ref32, refT, w.dtype, label + " single")
+    for P in sorted({w.bs, 3 * w.bs, 512}):
+        check_outputs(run_partitioned(g, w, P), ref32, refT, w.dtype, label + f" P={P}")
+    del g
+    free_gpu()
+
+
+# ---------------------------------------------------------------------------
+# edge cases: lengths around block and partition boundaries, head groupings
+# ---------------------------------------------------------------------------
+
+EDGE = [
+    # Hq, Hkv, D, bs, dtype
+    (4, 4, 64, 16, "f16"),
+    (8, 1, 128, 16, "bf16"),      # MQA, G = 8
+    (14, 2, 128, 32, "bf16"),     # G = 7, bs 32
+    (6, 2, 64, 16, "f16"),        # G = 3
+    (10, 2, 128, 16, "bf16"),     # G = 5
+    (12, 2, 64, 32, "f16"),       # G = 6
+    (24, 2, 128, 16, "bf16"),     # G = 12: two head chunks of 6
+    (32, 1, 128, 32, "f16"),      # G = 32: four head chunks of 8
+    (40, 40, 128, 16, "f16"),     # MHA, 40 heads
+]
+
+
+@pytest.mark.parametrize("Hq,Hkv,D,bs,dtype", EDGE,
+                         ids=[f"hq{a}-hkv{b}-d{c}-bs{d}-{e}" for a, b, c, d, e in EDGE])
+def test_edge_lengths(Hq, Hkv, D, bs, dtype):
+    P = 4 * bs
+    lens = (1, bs - 1, bs, bs + 1, P - 1, P, P + 1, 2 * P, 2 * P + 3, 5 * P - 1)
+    s = spec(1, "full", num_seqs=len(lens), num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+             block_size=bs, dtype=dtype, fixed_lengths=lens, num_blocks=0, seed=17 + Hq)
+    w = make_workload(s)
+    label = f"edge Hq{Hq} Hkv{Hkv} D{D} bs{bs} {dtype}"
+    print(f"\n[{label}] lens={list(lens)}", flush=True)
+    g = gpu_side.build(w)
+    o = oracle_side.build(w)
+    check_state(g, o, w, label)
+    ref32, refT = oracle.decode(o.q, o.key_cache, o.value_cache, o.block_tables, o.context_lens,
+                                w.scale, w.dtype, nthreads=0)
+    check_outputs(run_single(g, w), ref32, refT, dtype, label + " single")
+    for PP in (bs, P, 1024):
+        check_outputs(run_partitioned(g, w, PP), ref32, refT, dtype, label + f" P={PP}")
+    del g
+    free_gpu()
+
+
+def test_zero_length_and_empty_batch():
+    w = workload(3, "small")
+    g = gpu_side.build(w)
+    o = oracle_side.build(w)
+    ref32, refT = oracle.decode(o.q, o.key_cache, o.value_cache, o.block_tables, o.context_lens,
+                                w.scale, w.dtype, nthreads=0)
+    # sequence 2 reports no tokens: its rows become zeros, the others are unchanged
+    g.step.context_lens[2] = 0
+    torch.cuda.synchronize()
+    for out in (run_single(g, w), run_partitioned(g, w, 512)):
+        assert np.all(out[2] == 0)
+        keep = [i for i in range(w.S) if i != 2]
+        check_outputs(out[keep], ref32[keep], refT[keep], w.dtype, "L=0 neighbours")
+    # an empty batch enqueues nothing and succeeds
+    c = g.cache
+    empty = torch.empty((0, w.Hq, w.D), dtype=torch.int16, device="cuda")
+    pa.pa_decode(empty, empty, c.key_cache, c.value_cache,
+                 torch.empty((0, 4), dtype=torch.int32, device="cuda"),
+                 torch.empty(0, dtype=torch.int32, device="cuda"), 64, w.scale, w.dtype)
+    del g
+    free_gpu()
+
+
+def test_negative_slots_write_nothing():
+    w = workload(1, "full")
+    g = gpu_side.build(w)
+    before = gpu_side.to_host16(g.cache.key_cache).copy()
+    c = g.cache
+    slots = torch.tensor([-1, -5, -1, -1], dtype=torch.int64, device="cuda")
+    pa.pa_reshape_and_cache(g.k_new, g.v_new, c.key_cache, c.value_cache, slots, w.dtype)
+    torch.cuda.synchronize()
+    assert np.array_equal(gpu_side.to_host16(c.key_cache), before)
+    del g
+    free_gpu()
+
+
+def test_copy_on_write_blocks():
+    """fork, then append: the allocator reports (src, dst) and pa_copy_blocks
+    copies the shared block bit for bit before the new token lands."""
+    w = workload(1, "full")
+    g = gpu_side.build(w)
+    c = g.cache
+    a = c.allocator
+    a.fork(3, 100)                                  # seq 3 has 37 tokens: last block shared
+    slot, cow = a.append_slot(100)
+    assert cow is not None and slot // w.bs == cow[1]
+    before = gpu_side.to_host16(c.key_cache).copy()
+    vbefore = gpu_side.to_host16(c.value_cache).copy()
+    pairs = torch.tensor([cow], dtype=torch.int32, device="cuda")
+    pa.pa_copy_blocks(c.key_cache, c.value_cache, pairs, w.dtype)
+    torch.cuda.synchronize()
+    after = gpu_side.to_host16(c.key_cache)
+    vafter = gpu_side.to_host16(c.value_cache)
+    expect = before.copy(); expect[cow[1]] = before[cow[0]]
+    vexpect = vbefore.copy(); vexpect[cow[1]] = vbefore[cow[0]]
+    assert np.array_equal(after, expect) and np.array_equal(vafter, vexpect)
+    del g
+    free_gpu()
+
+
+def test_decode_steps_across_block_boundaries():
+    """Three whole decode steps (a1..a6) of the engine against the oracle
+    replaying the same appends: positions cross block boundaries."""
+    w = workload(3, "small")
+    g = gpu_side.build(w, extra_tokens=4)
+    o = oracle_side.build(w)
+    step = g.step
+    for k in range(3):
+        out = step(g.q, g.k_new, g.v_new)
+        slots = np.array([o.model.append_slot(i)[0] for i in range(w.S)], np.int64)
+        oracle.cache_write(o.k_new, o.v_new, o.key_cache, o.value_cache, slots)
+        torch.cuda.synchronize()
+        mb = step.mb
+        bt = oracle_side.tables_of(o.model, w.S, mb)
+        cl = np.array([o.model.num_tokens[i] for i in range(w.S)], np.int32)
+        assert np.array_equal(step.block_tables.cpu().numpy(), bt)
+        assert np.array_equal(step.context_lens.cpu().numpy(), cl)
+        ref32, refT = oracle.decode(o.q, o.key_cache, o.value_cache, bt, cl, w.scale, w.dtype,
+                                    nthreads=0)
+        check_outputs(gpu_side.to_host16(out), ref32, refT, w.dtype, f"engine step {k}")
+    assert np.array_equal(gpu_side.to_host16(g.cache.key_cache), o.key_cache)
+    del g
+    free_gpu()
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads in the benchmark's launch configuration: sampled outputs
+# ---------------------------------------------------------------------------
+
+FULL = [(2, None), (3, None), (4, None), (5, 16), (5, 32)]
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("cfg,bs", FULL, ids=[f"cfg{c}-bs{b or 16}" for c, b in FULL])
+def test_full_size_sampled(cfg, bs):
+    w = workload(cfg, "full", **({"block_size": bs} if bs else {}))
+    label = f"cfg{cfg} full bs{w.bs}"
+    print(f"\n[{label}] S={w.S} KV bytes={w.kv_bytes()} blocks={w.num_blocks}", flush=True)
+    g = gpu_side.build(w)
+    out = g.step.attend(g.q)
+    torch.cuda.synchronize()
+    got = gpu_side.to_host16(out)
+    print(f"[{label}] GPU done", flush=True)
+    o = oracle_side.build(w)
+    check_state(g, o, w, label)
+    del g
+    free_gpu()
+    rng = np.random.default_rng(cfg)
+    order = np.argsort(w.lengths)
+    seqs = sorted(set([int(order[0]), int(order[-1]), int(order[len(order) // 2])] +
+                      [int(x) for x in rng.choice(w.S, min(5, w.S), replace=False)]))
+    pairs = np.array([[i, h] for i in seqs for h in rng.choice(w.Hq, 3, replace=False)], np.int32)
+    ref32, refT = oracle.decode_pairs(o.q, o.key_cache, o.value_cache, o.block_tables,
+                                      o.context_lens, w.scale, w.dtype, pairs, nthreads=0)
+    sub = np.stack([got[i, h] for i, h in pairs])
+    check_outputs(sub, ref32, refT, w.dtype, label + " sampled")
+    # properties at any size: every output finite and within the range of V
+    allv = oracle.widen(got, w.dtype)
+    assert np.isfinite(allv).all()
+    assert np.abs(allv).max() <= 8.0          # convex combinations of N(0,1) samples
