@@ -152,3 +152,13 @@ def test_binding_raises_on_error_status():
         _native._check(_native.PA_ERR_INVALID_ARG)
     with pytest.raises(pa.PaOOM):
         _native._check(_native.PA_ERR_OOM)
+
+
+def test_one_hip_runtime_in_the_process():
+    """libpa and torch must share one HIP runtime, whatever the import order."""
+    code = ("import paged_kv_cache_106_amd, torch\n"
+            "paths = {l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}\n"
+            "print(len(paths))\n")
+    r = subprocess.run([os.sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.strip() == "1"
