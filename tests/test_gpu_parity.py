@@ -3,8 +3,8 @@ seeded inputs.
 
 Bars: cache writes, slots and block tables bit-exact (whole pools compared,
 NaN-poisoned unused slots included); decode outputs within max|d| <= 1e-2 of
-the oracle's fp32 result and within 1 unit in the last place of its
-16-bit rounding.
+the oracle's fp32 result, and each output within half a unit in the last
+place of the 16-bit format (plus 1e-4 of fp32 summation noise) of it.
 """
 import gc
 import math
@@ -28,14 +28,32 @@ def ordered(bits):
     return np.where(b & 0x8000, -(b & 0x7FFF), b)
 
 
+def half_ulp(x, dtype):
+    """Half a unit in the last place of the 16-bit format at |x|."""
+    mant, emin = (10, -14) if dtype == "f16" else (7, -126)
+    a = np.abs(x.astype(np.float64))
+    _, e = np.frexp(a)
+    e = np.where(a == 0, emin, np.maximum(e - 1, emin))
+    return np.ldexp(0.5, e - mant)
+
+
+FP32_NOISE = 1e-4   # allowance for fp32 summation-order differences (outputs are O(1))
+
+
 def check_outputs(got_bits, ref32, ref_bits, dtype, label):
+    """Required bar: max|d| <= 1e-2 against the oracle's fp32 result.  Stricter
+    check: every output is the oracle's fp32 value correctly rounded, up to
+    fp32 summation noise."""
     got = oracle.widen(got_bits, dtype)
     assert np.isfinite(got).all(), f"{label}: non-finite output"
-    err = np.abs(got.astype(np.float64) - ref32.astype(np.float64)).max()
+    d = np.abs(got.astype(np.float64) - ref32.astype(np.float64))
+    err = d.max()
     ulp = np.abs(ordered(got_bits) - ordered(ref_bits)).max()
-    print(f"[{label}] max|d|={err:.3e} max|out|={np.abs(ref32).max():.3f} max_ulp={ulp}", flush=True)
+    excess = (d - half_ulp(ref32, dtype)).max()
+    print(f"[{label}] max|d|={err:.3e} max|out|={np.abs(ref32).max():.3f} max_ulp={ulp} "
+          f"excess_over_half_ulp={excess:.2e}", flush=True)
     assert err <= TOL, f"{label}: max|d| {err} > {TOL}"
-    assert ulp <= 1, f"{label}: {ulp} ulp from the oracle's rounding"
+    assert excess <= FP32_NOISE, f"{label}: {excess} beyond correct rounding + fp32 noise"
 
 
 def free_gpu():
