@@ -165,6 +165,30 @@ pa_status pa_decode_partitioned(void* out, const void* query,
                                 size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Decode-step update of device-resident block tables.
+ * Follows: append_slot puts the new token into the sequence's current block
+ * or a fresh one ("vLLM 深度拆解：当大模型推理学会「分页注意力」", §3.3), and
+ * the block table maps each logical block to its physical block
+ * ("LLM推理优化：vLLM PagedAttention深度解析与工程实践", §3.1).  After one
+ * append per sequence, the only entry that can differ from the previous
+ * table is the one holding the new token, at position L-1:
+ *   block_tables[i][(context_lens[i] - 1) / block_size] = slot_mapping[i] / block_size
+ * (a fresh block, a copy-on-write replacement, or the unchanged block).
+ *   block_tables      [num_seqs][max_blocks_per_seq] int32, updated in place
+ *   context_lens      [num_seqs] int32, the new token included
+ *   slot_mapping      [num_seqs] int64, the new token's slot (< 0: skip)
+ * Entries whose slot is outside [0, num_blocks * block_size), whose length
+ * is <= 0 or whose index reaches max_blocks_per_seq are skipped on the
+ * device.  Lets a caller keep tables on the GPU and send only 12 bytes per
+ * sequence per step.
+ * ---------------------------------------------------------------------- */
+pa_status pa_update_block_tables(int32_t* block_tables, int32_t max_blocks_per_seq,
+                                 const int32_t* context_lens,
+                                 const int64_t* slot_mapping, int32_t num_seqs,
+                                 int32_t block_size, int32_t num_blocks,
+                                 hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Block copy for copy-on-write: for each pair k, block dst[k] of both pools
  * becomes a bit-exact copy of block src[k] (all slots, heads and dims).
  * Follows: a shared block is copied only when a sharer must modify it
@@ -217,10 +241,12 @@ pa_status pa_alloc_append_slot(pa_allocator* a, int64_t seq_id,
 
 /* append_slot for n distinct sequences at once; all or nothing (PA_ERR_OOM
  * before any change when the pool cannot serve the whole batch).
- * slots_out [n]; cow_src / cow_dst [n] or NULL. */
+ * slots_out [n]; context_lens_out [n] (tokens held after the append, or
+ * NULL); cow_src / cow_dst [n] or NULL. */
 pa_status pa_alloc_append_slots(pa_allocator* a, const int64_t* seq_ids,
                                 int32_t n, int64_t* slots_out,
-                                int32_t* cow_src, int32_t* cow_dst);
+                                int32_t* context_lens_out, int32_t* cow_src,
+                                int32_t* cow_dst);
 
 /* New sequence dst_seq references the first num_tokens tokens (a multiple
  * of block_size, at most src's tokens) of src_seq: the same physical

@@ -66,7 +66,8 @@ _sig("pa_alloc_create", _i32, [_i32, _i32, _i32p, ctypes.POINTER(_vp)])
 _sig("pa_alloc_destroy", None, [_vp])
 _sig("pa_alloc_allocate", _i32, [_vp, _i64, _i32])
 _sig("pa_alloc_append_slot", _i32, [_vp, _i64, _i64p, _i32p, _i32p])
-_sig("pa_alloc_append_slots", _i32, [_vp, _i64p, _i32, _i64p, _i32p, _i32p])
+_sig("pa_alloc_append_slots", _i32, [_vp, _i64p, _i32, _i64p, _i32p, _i32p, _i32p])
+_sig("pa_update_block_tables", _i32, [_vp, _i32, _vp, _vp, _i32, _i32, _i32, _vp])
 _sig("pa_alloc_share_prefix", _i32, [_vp, _i64, _i64, _i32])
 _sig("pa_alloc_fork", _i32, [_vp, _i64, _i64])
 _sig("pa_alloc_free", _i32, [_vp, _i64])
@@ -178,6 +179,18 @@ def pa_decode_partitioned(out, query, key_cache, value_cache, block_tables, cont
                                       _stream(stream)))
 
 
+def pa_update_block_tables(block_tables, context_lens, slot_mapping, block_size, num_blocks,
+                           stream=None):
+    """block_tables int32 [S][MB] (updated in place); context_lens int32 [S]; slot_mapping int64 [S]."""
+    s, mb = block_tables.shape
+    if tuple(context_lens.shape) != (s,) or tuple(slot_mapping.shape) != (s,):
+        raise ValueError("context_lens and slot_mapping must be [S]")
+    _check(_lib.pa_update_block_tables(_dptr(block_tables, "block_tables", 4), mb,
+                                       _dptr(context_lens, "context_lens", 4),
+                                       _dptr(slot_mapping, "slot_mapping", 8), s, int(block_size),
+                                       int(num_blocks), _stream(stream)))
+
+
 def pa_copy_blocks(key_cache, value_cache, block_pairs, dtype, stream=None):
     """block_pairs: int32 GPU tensor [n][2] of (src, dst) block ids."""
     nb, bs, hkv, d = key_cache.shape
@@ -212,9 +225,9 @@ class Allocator:
         self._h = h
 
     def close(self):
-        if getattr(self, "_h", None):
+        if getattr(self, "_h", None) and _lib is not None:
             _lib.pa_alloc_destroy(self._h)
-            self._h = None
+        self._h = None
 
     def __del__(self):
         self.close()
@@ -229,17 +242,21 @@ class Allocator:
                                          ctypes.byref(src), ctypes.byref(dst)))
         return slot.value, (None if src.value < 0 else (src.value, dst.value))
 
-    def append_slots(self, seq_ids, slots_out=None, cow_src=None, cow_dst=None):
-        """Batched append_slot; returns (slots int64[n], cow_src int32[n], cow_dst int32[n])."""
+    def append_slots(self, seq_ids, slots_out=None, context_lens_out=None, cow_src=None,
+                     cow_dst=None):
+        """Batched append_slot; returns (slots int64[n], context_lens int32[n],
+        cow_src int32[n], cow_dst int32[n])."""
         ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
         n = ids.shape[0]
         slots = slots_out if slots_out is not None else np.empty(n, np.int64)
+        lens = context_lens_out if context_lens_out is not None else np.empty(n, np.int32)
         src = cow_src if cow_src is not None else np.empty(n, np.int32)
         dst = cow_dst if cow_dst is not None else np.empty(n, np.int32)
         _check(_lib.pa_alloc_append_slots(self._h, _np_ptr(ids, ctypes.c_int64), n,
                                           _np_ptr(slots, ctypes.c_int64),
+                                          _np_ptr(lens, ctypes.c_int32),
                                           _np_ptr(src, ctypes.c_int32), _np_ptr(dst, ctypes.c_int32)))
-        return slots, src, dst
+        return slots, lens, src, dst
 
     def share_prefix(self, src_seq, dst_seq, num_tokens):
         _check(_lib.pa_alloc_share_prefix(self._h, int(src_seq), int(dst_seq), int(num_tokens)))

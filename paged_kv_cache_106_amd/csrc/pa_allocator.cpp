@@ -167,7 +167,8 @@ pa_status pa_alloc_append_slot(pa_allocator* a, int64_t seq_id, int64_t* slot_ou
 }
 
 pa_status pa_alloc_append_slots(pa_allocator* a, const int64_t* seq_ids, int32_t n,
-                                int64_t* slots_out, int32_t* cow_src, int32_t* cow_dst) {
+                                int64_t* slots_out, int32_t* context_lens_out, int32_t* cow_src,
+                                int32_t* cow_dst) {
   pa::clear_error();
   if (!a || n < 0 || (n > 0 && (!seq_ids || !slots_out)))
     return invalid("pa_alloc_append_slots: bad argument");
@@ -183,9 +184,11 @@ pa_status pa_alloc_append_slots(pa_allocator* a, const int64_t* seq_ids, int32_t
   }
   if (need > a->count)
     return pa::fail(PA_ERR_OOM, "pa_alloc_append_slots: not enough free blocks");
-  for (int32_t k = 0; k < n; ++k)
+  for (int32_t k = 0; k < n; ++k) {
     slots_out[k] = a->append(seq_ids[k], cow_src ? cow_src + k : nullptr,
                              cow_dst ? cow_dst + k : nullptr);
+    if (context_lens_out) context_lens_out[k] = a->seqs[seq_ids[k]].tokens;
+  }
   return PA_OK;
 }
 

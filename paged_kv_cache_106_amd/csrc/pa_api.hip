@@ -233,6 +233,26 @@ pa_status pa_decode_partitioned(void* out, const void* query, const void* key_ca
   return pa::launched(launch(2, p, stream), "pa_decode_partitioned (merge)");
 }
 
+pa_status pa_update_block_tables(int32_t* block_tables, int32_t max_blocks_per_seq,
+                                 const int32_t* context_lens, const int64_t* slot_mapping,
+                                 int32_t num_seqs, int32_t block_size, int32_t num_blocks,
+                                 hipStream_t stream) {
+  pa::clear_error();
+  if (num_seqs < 0 || max_blocks_per_seq <= 0 || block_size <= 0 || num_blocks <= 0)
+    return fail(PA_ERR_INVALID_ARG, "bad size");
+  if (num_seqs == 0) return PA_OK;
+  if (!block_tables || !context_lens || !slot_mapping)
+    return fail(PA_ERR_INVALID_ARG, "NULL device pointer");
+  if (!pa::aligned(block_tables, 4) || !pa::aligned(context_lens, 4) ||
+      !pa::aligned(slot_mapping, 8))
+    return fail(PA_ERR_INVALID_ARG, "misaligned device buffer");
+  return pa::launched(pa::launch_update_tables(block_tables, max_blocks_per_seq, context_lens,
+                                               slot_mapping, num_seqs, block_size,
+                                               static_cast<int64_t>(num_blocks) * block_size,
+                                               stream),
+                      "pa_update_block_tables");
+}
+
 pa_status pa_copy_blocks(void* key_cache, void* value_cache, const int32_t* block_pairs,
                          int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
                          int32_t block_size, int32_t num_blocks, pa_dtype dtype,

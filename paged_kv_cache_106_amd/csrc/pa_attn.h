@@ -415,23 +415,30 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
   }
 }
 
-// Merge of the partitions of one (sequence, q head) per wave:
+// Merge of the partitions of one (sequence, q head) per workgroup:
 //   M = max_p m_p,  w_p = 2^(m_p - M),  out = sum_p w_p acc_p / sum_p w_p l_p
+// Wave w takes partitions w, w+4, ...: the partition index is wave-uniform, so
+// m_p and l_p arrive through scalar loads and each lane streams its E dims of
+// acc_p, several partitions in flight at once.  The waves' sums meet in LDS.
 template <int DT, int D>
 __global__ __launch_bounds__(kThreads) void merge_kernel(AttnParams p) {
   using F = Fmt<DT>;
   constexpr int E = D / 64;   // dims per lane
-  const int lane = threadIdx.x & 63;
-  const int pair = blockIdx.x * kWaves + (threadIdx.x >> 6);
-  if (pair >= p.num_seqs * p.num_q_heads) return;   // no barriers below
+  constexpr int UNROLL = 4;
+  __shared__ float red_acc[kWaves][D];
+  __shared__ float red_l[kWaves];
+  __shared__ float red_m[kWaves];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int pair = blockIdx.x;
   const int seq = pair / p.num_q_heads;
   int L = p.context_lens[seq];
   L = max(0, min(L, p.mb * p.block_size));
   const int np = min((L + p.chunk - 1) / p.chunk, p.num_parts);
-  uint16_t* out = static_cast<uint16_t*>(p.out) + static_cast<int64_t>(pair) * D + lane * E;
-  if (np == 0) {
-#pragma unroll
-    for (int e = 0; e < E; ++e) out[e] = 0;
+  uint16_t* out = static_cast<uint16_t*>(p.out) + static_cast<int64_t>(pair) * D;
+  if (np == 0) {                                   // uniform: whole workgroup
+    for (int d = tid; d < D; d += kThreads) out[d] = 0;
     return;
   }
   const int64_t base = static_cast<int64_t>(pair) * p.num_parts;
@@ -440,29 +447,46 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(AttnParams p) {
   const float* pa = p.part_acc + base * D + lane * E;
 
   float m = -__builtin_inff();
-  for (int k = lane; k < np; k += 64) m = fmaxf(m, pm[k]);
+  for (int k = tid; k < np; k += kThreads) m = fmaxf(m, pm[k]);
   m = wave_max_from(m, 1);
+  if (lane == 0) red_m[wave] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(red_m[0], red_m[1]), fmaxf(red_m[2], red_m[3]));
 
   float l = 0.f;
   float acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.f;
-  for (int k0 = 0; k0 < np; k0 += 64) {
-    const int k = k0 + lane;
-    const float w = k < np ? fast_exp2(pm[k] - m) : 0.f;
-    l += k < np ? w * ps[k] : 0.f;
-    const int cnt = min(64, np - k0);
-    for (int j = 0; j < cnt; ++j) {
-      const float wj = __builtin_bit_cast(
-          float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j));
-      const float* src = pa + static_cast<int64_t>(k0 + j) * D;
+  for (int k0 = wave; k0 < np; k0 += kWaves * UNROLL) {
+    float x[UNROLL][E];
+    float wk[UNROLL];
 #pragma unroll
-      for (int e = 0; e < E; ++e) acc[e] = fmaf(wj, src[e], acc[e]);
+    for (int u = 0; u < UNROLL; ++u) {
+      const int k = min(k0 + u * kWaves, np - 1);  // clamped: loads stay in range
+      wk[u] = (k0 + u * kWaves < np) ? fast_exp2(pm[k] - m) : 0.f;
+      const float* src = pa + static_cast<int64_t>(k) * D;
+      if constexpr (E == 2) {
+        const float2 v = *reinterpret_cast<const float2*>(src);
+        x[u][0] = v.x; x[u][1] = v.y;
+      } else {
+        x[u][0] = src[0];
+      }
+      l += wk[u] * ps[k];
     }
-  }
-  l = wave_sum_from(l, 1);
 #pragma unroll
-  for (int e = 0; e < E; ++e) out[e] = F::narrow(acc[e] / l);
+    for (int u = 0; u < UNROLL; ++u)
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] = fmaf(wk[u], x[u][e], acc[e]);
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) red_acc[wave][lane * E + e] = acc[e];
+  if (lane == 0) red_l[wave] = l;
+  __syncthreads();
+  const float lt = red_l[0] + red_l[1] + red_l[2] + red_l[3];
+  for (int d = tid; d < D; d += kThreads) {
+    const float v = red_acc[0][d] + red_acc[1][d] + red_acc[2][d] + red_acc[3][d];
+    out[d] = F::narrow(v / lt);
+  }
 }
 
 template <int DT, int D, int GT>
@@ -483,8 +507,7 @@ int launch_attn_gt(int kind, const AttnParams& p, hipStream_t stream) {
 template <int DT, int D>
 int launch_attn(int kind, const AttnParams& p, hipStream_t stream) {
   if (kind == 2) {
-    const int pairs = p.num_seqs * p.num_q_heads;
-    const dim3 grid((pairs + kWaves - 1) / kWaves);
+    const dim3 grid(p.num_seqs * p.num_q_heads);
     hipLaunchKernelGGL((merge_kernel<DT, D>), grid, dim3(kThreads), 0, stream, p);
     return static_cast<int>(hipGetLastError());
   }

@@ -44,6 +44,34 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(uint4* __restrict__ k_
   }
 }
 
+// Decode-step table update: sequence i's new token sits at position L_i - 1
+// in slot s_i, so the table entry that holds it is (L_i - 1) / bs and its
+// block is s_i / bs.  Appending never moves earlier blocks, and a copy-on-write
+// replaces exactly this entry, so one store per sequence keeps a
+// device-resident table equal to the allocator's.
+__global__ __launch_bounds__(256) void update_tables_kernel(int32_t* __restrict__ tables,
+                                                            int32_t mb,
+                                                            const int32_t* __restrict__ lens,
+                                                            const int64_t* __restrict__ slots,
+                                                            int32_t n, int32_t bs,
+                                                            int64_t num_slots) {
+  const int32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const int64_t s = slots[i];
+  const int32_t L = lens[i];
+  if (s < 0 || s >= num_slots || L <= 0) return;
+  const int32_t idx = (L - 1) / bs;
+  if (idx >= mb) return;
+  tables[static_cast<int64_t>(i) * mb + idx] = static_cast<int32_t>(s / bs);
+}
+
+int launch_update_tables(int32_t* tables, int32_t mb, const int32_t* lens, const int64_t* slots,
+                         int32_t n, int32_t bs, int64_t num_slots, hipStream_t stream) {
+  hipLaunchKernelGGL(update_tables_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, tables, mb,
+                     lens, slots, n, bs, num_slots);
+  return static_cast<int>(hipGetLastError());
+}
+
 int launch_cache_write(const void* key, const void* value, void* k_cache, void* v_cache,
                        const int64_t* slots, int32_t n, int32_t chunks_per_tok,
                        int64_t num_slots, hipStream_t stream) {

@@ -49,6 +49,8 @@ int launch_attn_bf16_d128(int kind, const AttnParams& p, hipStream_t stream);
 int launch_cache_write(const void* key, const void* value, void* k_cache, void* v_cache,
                        const int64_t* slots, int32_t n, int32_t chunks_per_tok,
                        int64_t num_slots, hipStream_t stream);
+int launch_update_tables(int32_t* tables, int32_t mb, const int32_t* lens, const int64_t* slots,
+                         int32_t n, int32_t bs, int64_t num_slots, hipStream_t stream);
 int launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int32_t num_pairs,
                        int64_t chunks_per_block, int32_t num_blocks, hipStream_t stream);
 

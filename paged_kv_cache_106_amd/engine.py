@@ -5,11 +5,13 @@
 a fixed batch of sequences, in the order the pages describe for a step
 ("vLLM 深度拆解：当大模型推理学会「分页注意力」", §3.1 data flow and §3.3):
 
-  a1  host: append_slot for every sequence -> slot mapping, block tables and
-      context lengths (libpa's allocator, written straight into pinned
-      host buffers);
-  a2  one async host-to-device copy of that metadata on the step's stream;
-  a3  pa_reshape_and_cache: the new tokens' K/V into their slots;
+  a1  host: append_slot for every sequence -> slot mapping and context
+      lengths (libpa's allocator, written straight into pinned host buffers);
+  a2  one async host-to-device copy of that metadata (12 bytes per sequence,
+      plus copy-on-write pairs when there are any) on the step's stream;
+  a3  pa_copy_blocks for copy-on-write, pa_update_block_tables (the device-
+      resident tables gain each new token's block), pa_reshape_and_cache (the
+      new tokens' K/V into their slots);
   a4  pa_decode (single pass)  or  a5+a6  pa_decode_partitioned (+ merge).
 
 Pinned metadata buffers are double-buffered: the host prepares step k+1
@@ -64,7 +66,14 @@ class PagedKVCache:
 
 
 class DecodeStep:
-    """One decode step for the sequences ``seq_ids`` (fixed order)."""
+    """One decode step for the sequences ``seq_ids`` (fixed order).
+
+    The block tables live on the GPU: they are uploaded whole once (and again
+    by ``sync_tables`` after any allocator change other than this step's own
+    appends); each step then sends only the new tokens' slots, the context
+    lengths and any copy-on-write pairs, and pa_update_block_tables records
+    each new token's block in place.
+    """
 
     def __init__(self, cache, seq_ids, num_q_heads, kernel="partitioned", partition_size=512,
                  max_context_len=None, scale=None, stream=None):
@@ -85,61 +94,86 @@ class DecodeStep:
         self.stream = stream if stream is not None else torch.cuda.current_stream(cache.device)
         dev = cache.device
 
-        # pinned host metadata, double-buffered, and its device twins
-        self._host = []
-        for _ in range(2):
-            meta = torch.empty(self._meta_bytes(), dtype=torch.uint8, pin_memory=True)
-            self._host.append(meta)
+        # per-step metadata: pinned host staging (double-buffered) and its device twin
+        self._host = [torch.empty(self._meta_bytes(), dtype=torch.uint8, pin_memory=True)
+                      for _ in range(2)]
         self._events = [None, None]
         self._turn = 0
         self._dev_meta = torch.empty(self._meta_bytes(), dtype=torch.uint8, device=dev)
-        self.slot_mapping, self.context_lens, self.block_tables = self._views(self._dev_meta)
+        self.slot_mapping, self.context_lens, self.cow_pairs = self._views(self._dev_meta)
+        self._num_cow = [0, 0]
+        self.block_tables = torch.zeros((self.S, self.mb), dtype=torch.int32, device=dev)
         self.out = torch.empty((self.S, self.num_q_heads, cache.head_dim), dtype=torch.int16,
                                device=dev)
         ws = pa.pa_decode_partitioned_workspace_size(self.S, self.num_q_heads, cache.head_dim,
                                                      self.max_context_len, self.partition_size)
         self.workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=dev)
         self.host_context_lens = np.zeros(self.S, np.int32)
+        self.sync_tables()
 
-    # metadata layout: slot_mapping int64 [S] | context_lens int32 [S] (+pad) | tables int32 [S][mb]
+    # layout: slots int64 [S] | context_lens int32 [S] (+pad to 8 bytes) | cow pairs int32 [S][2]
     def _meta_bytes(self):
-        return 8 * self.S + 4 * (self.S + (self.S & 1)) + 4 * self.S * self.mb
+        return 8 * self.S + 4 * (self.S + (self.S & 1)) + 8 * self.S
 
     def _views(self, buf):
-        S, mb = self.S, self.mb
+        S = self.S
         o1 = 8 * S
         o2 = o1 + 4 * (S + (S & 1))
         sm = buf[:o1].view(torch.int64)
         cl = buf[o1:o1 + 4 * S].view(torch.int32)
-        bt = buf[o2:o2 + 4 * S * mb].view(torch.int32).view(S, mb)
-        return sm, cl, bt
+        cow = buf[o2:o2 + 8 * S].view(torch.int32).view(S, 2)
+        return sm, cl, cow
+
+    def sync_tables(self):
+        """Upload the allocator's current tables and lengths (blocking)."""
+        tbl, lens = self.cache.allocator.block_tables(self.seq_ids, self.mb, pad=0)
+        if int(lens.max(initial=0)) > self.max_context_len:
+            raise ValueError("a sequence is longer than max_context_len")
+        with torch.cuda.stream(self.stream):
+            self.block_tables.copy_(torch.from_numpy(tbl))
+            self.context_lens.copy_(torch.from_numpy(lens))
+        self.stream.synchronize()
+        self.host_context_lens[:] = lens
 
     def prepare(self):
-        """a1: append one slot per sequence on the host and stage the metadata.
-        Returns the index of the pinned buffer holding it."""
+        """a1: one slot per sequence from the host allocator, staged in pinned
+        memory.  Returns the index of the staging buffer."""
         b = self._turn
         self._turn ^= 1
         if self._events[b] is not None:
             self._events[b].synchronize()          # its previous copy has run
-        sm, cl, bt = (t.numpy() for t in self._views(self._host[b]))
-        self.cache.allocator.append_slots(self.seq_ids, slots_out=sm)
-        self.cache.allocator.block_tables(self.seq_ids, self.mb, pad=0, out=bt, context_lens_out=cl)
-        self.host_context_lens[:] = cl
-        if int(cl.max(initial=0)) > self.max_context_len:
-            raise ValueError("a sequence outgrew max_context_len")
+        sm, cl, cow = (t.numpy() for t in self._views(self._host[b]))
+        if int(self.host_context_lens.max(initial=0)) >= self.max_context_len:
+            raise ValueError("a sequence would outgrow max_context_len")
+        _, _, src, dst = self.cache.allocator.append_slots(
+            self.seq_ids, slots_out=sm, context_lens_out=self.host_context_lens)
+        cl[:] = self.host_context_lens
+        k = np.flatnonzero(src >= 0)
+        self._num_cow[b] = int(k.size)
+        if k.size:
+            cow[: k.size, 0] = src[k]
+            cow[: k.size, 1] = dst[k]
         return b
 
     def upload(self, b):
         """a2: async copy of the staged metadata to the device, on the step's stream."""
+        n = 8 * self.S + 4 * (self.S + (self.S & 1)) + 8 * self._num_cow[b]
+        self._ncow_dev = self._num_cow[b]
         with torch.cuda.stream(self.stream):
-            self._dev_meta.copy_(self._host[b], non_blocking=True)
+            self._dev_meta[:n].copy_(self._host[b][:n], non_blocking=True)
             ev = torch.cuda.Event()
             ev.record(self.stream)
         self._events[b] = ev
 
     def write_new(self, k_new, v_new):
-        """a3: the new tokens' K/V ([S][Hkv][D] GPU tensors) into their slots."""
+        """a3: copy-on-write copies (if any), the table entries of the new
+        tokens' blocks, then the new tokens' K/V ([S][Hkv][D]) into their slots."""
         c = self.cache
+        if self._ncow_dev:
+            pa.pa_copy_blocks(c.key_cache, c.value_cache, self.cow_pairs[: self._ncow_dev],
+                              c.dtype, self.stream)
+        pa.pa_update_block_tables(self.block_tables, self.context_lens, self.slot_mapping,
+                                  c.block_size, c.num_blocks, self.stream)
         pa.pa_reshape_and_cache(k_new, v_new, c.key_cache, c.value_cache, self.slot_mapping,
                                 c.dtype, self.stream)
 

@@ -134,9 +134,10 @@ def test_random_ops_match_model(seed):
                 ok = False
                 m.free_blocks, m.tables, m.num_tokens, m.refcount = snap   # all or nothing
             if ok:
-                slots, src, dst = a.append_slots(op[1])
+                slots, lens, src, dst = a.append_slots(op[1])
                 for k, (slot, cow) in enumerate(want):
                     assert slots[k] == slot
+                    assert lens[k] == m.num_tokens[op[1][k]]
                     assert (None if src[k] < 0 else (src[k], dst[k])) == cow
             else:
                 with pytest.raises(pa.PaOOM):
@@ -167,7 +168,8 @@ def test_workload_replay_matches_model(cfg, variant, bs):
             a.allocate(op[1], op[2])
         elif op[0] == "share_prefix":
             a.share_prefix(op[1], op[2], op[3])
-    slots, src, dst = a.append_slots(np.arange(w.S))
+    slots, lens, src, dst = a.append_slots(np.arange(w.S))
+    assert np.array_equal(lens, w.lengths)
     assert np.array_equal(slots, new_slots)
     assert np.all(src == -1) and np.all(dst == -1)         # no copy-on-write in these scripts
     mb = w.max_blocks_per_seq()
