@@ -75,6 +75,9 @@ def main():
     ap.add_argument("--block-size", type=int, default=None, choices=[16, 32])
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy 5 times (for scaling "
+                         "the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -88,6 +91,15 @@ def main():
     from workloads import workload
 
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        src = torch.empty(1 << 28, dtype=torch.int32, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": 1 << 30, "bytes_written": 1 << 30,
+                          "launches": 5}), flush=True)
+        return
     overrides = {"block_size": args.block_size} if args.block_size else {}
     w = workload(args.config, "full", **overrides)
     log(f"[bench] {w.spec.name}; bs={w.bs}; S={w.S}; KV bytes/step ~{w.kv_bytes()/1e6:.1f} MB")

@@ -115,33 +115,87 @@ __device__ inline float wave_sum_from(float x, int first_stride) {
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Token layout inside a workgroup.  Work is cut into units of 16 tokens (one
+// block of 16, or one half of a block of 32), and wave w takes units w, w+4,
+// ... of the chunk.
+//  QK: 8 lanes per token, each holding KC = D/64 16-byte chunks of the K row
+//      (dims c*64 + kcol*8 .. +8): a wave load covers 8 tokens x 128 bytes,
+//      and a 3-step DPP sum finishes each dot product.
+//  PV: VL = D/8 lanes per token, each holding 8 consecutive dims: a wave
+//      load covers VTOK = 64/VL tokens; each lane accumulates its 8 dims for
+//      every head of the group.
 template <int D, int GT>
 struct Tile {
-  static constexpr int LPT = D / 8;               // lanes per token row
-  static constexpr int TPI = 64 / LPT;            // tokens per wave load
+  static constexpr int UNIT = 16;
+  static constexpr int KC = D / 64;
+  static constexpr int KTOK = 8;
+  static constexpr int KGROUPS = UNIT / KTOK;       // 2
+  static constexpr int KLOADS = KGROUPS * KC;       // 16-byte loads per lane per unit
+  static constexpr int VL = D / 8;
+  static constexpr int VTOK = 64 / VL;
+  static constexpr int VLOADS = UNIT / VTOK;
   static constexpr int GTP = GT == 1 ? 1 : (GT == 2 ? 2 : (GT <= 4 ? 4 : 8));
-  static constexpr int U = 32 / TPI;              // wave loads in flight
 };
 
-// LDS (floats): probabilities [chunk][GTP], wave partial outputs
+// LDS (floats): logits / probabilities [chunk][GTP], wave partial outputs
 // [kWaves][GT][D], wave maxima and sums [kWaves][GTP] each.
 __host__ __device__ constexpr size_t lds_floats(int D, int GT, int GTP, int chunk) {
   return static_cast<size_t>(chunk) * GTP + static_cast<size_t>(kWaves) * GT * D +
          2 * static_cast<size_t>(kWaves) * GTP;
 }
 
+template <int N>
+__device__ inline void lds_store(float* dst, const float (&v)[N]) {
+  if constexpr (N >= 4) {
+#pragma unroll
+    for (int k = 0; k < N; k += 4)
+      *reinterpret_cast<float4*>(dst + k) = make_float4(v[k], v[k + 1], v[k + 2], v[k + 3]);
+  } else if constexpr (N == 2) {
+    *reinterpret_cast<float2*>(dst) = make_float2(v[0], v[1]);
+  } else {
+    dst[0] = v[0];
+  }
+}
+
+template <int N>
+__device__ inline void lds_load(float (&v)[N], const float* src) {
+  if constexpr (N >= 4) {
+#pragma unroll
+    for (int k = 0; k < N; k += 4) {
+      const float4 f = *reinterpret_cast<const float4*>(src + k);
+      v[k] = f.x; v[k + 1] = f.y; v[k + 2] = f.z; v[k + 3] = f.w;
+    }
+  } else if constexpr (N == 2) {
+    const float2 f = *reinterpret_cast<const float2*>(src);
+    v[0] = f.x; v[1] = f.y;
+  } else {
+    v[0] = src[0];
+  }
+}
+
+// Buffer resource over one physical block (the base is wave-uniform).
+__device__ inline __amdgpu_buffer_rsrc_t block_rsrc(const char* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, 0x7fffffff, 0x00020000);
+}
+
+__device__ inline uint4 load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 template <int DT, int D, int GT, bool SPLIT>
 __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
   using F = Fmt<DT>;
   using TL = Tile<D, GT>;
-  constexpr int LPT = TL::LPT, TPI = TL::TPI, GTP = TL::GTP, U = TL::U;
+  constexpr int UNIT = TL::UNIT, KC = TL::KC, KGROUPS = TL::KGROUPS, KLOADS = TL::KLOADS;
+  constexpr int VL = TL::VL, VTOK = TL::VTOK, VLOADS = TL::VLOADS, GTP = TL::GTP;
   extern __shared__ float lds[];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
-  const int row = lane / LPT;   // token of a wave load
-  const int col = lane % LPT;   // 16-byte column of the head vector
+  const int krow = lane >> 3, kcol = lane & 7;      // QK: token row, 16-byte column
+  const int vrow = lane / VL, vcol = lane % VL;     // PV: token row, 16-byte column
 
   const int seq = blockIdx.z;
   const int kvh = blockIdx.y / p.head_chunks;
@@ -168,24 +222,14 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
     }
   }
 
-  // q slices: lane (row, col) holds elements col*8 .. col*8+7 of every head
-  uint4 q4[GT];
-  {
-    const uint16_t* q = static_cast<const uint16_t*>(p.q);
-#pragma unroll
-    for (int hh = 0; hh < GT; ++hh) {
-      q4[hh] = hh < nact ? *reinterpret_cast<const uint4*>(q + (out_row0 + hh) * D + col * 8)
-                         : make_uint4(0, 0, 0, 0);
-    }
-  }
-
   const int32_t* bt = p.block_tables + static_cast<int64_t>(seq) * p.mb;
   const char* kbase = static_cast<const char*>(p.k_cache);
   const char* vbase = static_cast<const char*>(p.v_cache);
   const int64_t block_bytes = p.block_stride * 2;
   const uint32_t tok_bytes = static_cast<uint32_t>(p.num_kv_heads) * D * 2;
-  const uint32_t lane_off =
-      static_cast<uint32_t>(row) * tok_bytes + static_cast<uint32_t>(kvh * D + col * 8) * 2;
+  const uint32_t head_off = static_cast<uint32_t>(kvh) * D * 2;
+  const uint32_t koff = static_cast<uint32_t>(krow) * tok_bytes + head_off + kcol * 16;
+  const uint32_t voff = static_cast<uint32_t>(vrow) * tok_bytes + head_off + vcol * 16;
   const int bs_mask = p.block_size - 1;
 
   float* s_lds = lds;                                       // [chunk][GTP]
@@ -199,68 +243,133 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
   for (int hh = 0; hh < GT; ++hh) {
     m_run[hh] = -__builtin_inff();
     l_run[hh] = 0.f;
+    if constexpr (!SPLIT) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[hh][e] = 0.f;
+      for (int e = 0; e < 8; ++e) acc[hh][e] = 0.f;
+    }
   }
 
-  for (int c0 = t_begin; c0 < t_end; c0 += p.chunk) {
-    const int n = min(p.chunk, t_end - c0);
-    const int ng = (n + TPI - 1) / TPI;   // wave loads covering the chunk
-    const int last_g = ng - 1;
+  // One chunk of n tokens from c0: logits, softmax statistics, P.V.  The
+  // split kernel runs it once (q is dead after the logits and acc is born at
+  // P.V, so the two never share registers); the single-pass kernel loops.
+  auto run_chunk = [&](const int c0, const int n) {
+    // q slices for the QK layout: chunk c of head hh = dims c*64 + kcol*8 .. +8
+    uint4 qv[GT][KC];
+    {
+      const uint16_t* q = static_cast<const uint16_t*>(p.q);
+#pragma unroll
+      for (int hh = 0; hh < GT; ++hh)
+#pragma unroll
+        for (int c = 0; c < KC; ++c)
+          qv[hh][c] = hh < nact
+                          ? *reinterpret_cast<const uint4*>(q + (out_row0 + hh) * D + c * 64 + kcol * 8)
+                          : make_uint4(0, 0, 0, 0);
+    }
+    const int nunits = (n + UNIT - 1) / UNIT;
+    const int cnt = nunits > wave ? (nunits - wave + kWaves - 1) / kWaves : 0;  // units of this wave
 
-    // ---------------- phase 1: logits ----------------
-    float mloc[GT];
+    // base of the i-th unit of this wave (clamped to its last unit: extra
+    // prefetches at the end of a loop re-read a unit already in cache)
+    auto unit_base = [&](const char* pool, int i) -> const char* {
+      const int u = wave + kWaves * min(i, cnt - 1);
+      const int t0 = c0 + u * UNIT;
+      int blk = __builtin_amdgcn_readfirstlane(bt[t0 >> p.log2_block_size]);
+      blk = (static_cast<unsigned>(blk) < static_cast<unsigned>(p.num_blocks)) ? blk : 0;
+      return pool + blk * block_bytes + static_cast<int64_t>(t0 & bs_mask) * tok_bytes;
+    };
+    auto load_k = [&](uint4 (&dst)[KLOADS], int i) {
+      const auto r = block_rsrc(unit_base(kbase, i));
 #pragma unroll
-    for (int hh = 0; hh < GT; ++hh) mloc[hh] = -__builtin_inff();
-
-    for (int g0 = wave * U; g0 < ng; g0 += kWaves * U) {
-      uint4 kv[U];
+      for (int j = 0; j < KGROUPS; ++j)
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int g = min(g0 + u, last_g);            // clamped: loads stay in range
-        const int tok0 = c0 + g * TPI;
-        int blk = __builtin_amdgcn_readfirstlane(bt[tok0 >> p.log2_block_size]);
-        blk = (static_cast<unsigned>(blk) < static_cast<unsigned>(p.num_blocks)) ? blk : 0;
-        const char* base = kbase + blk * block_bytes +
-                           static_cast<int64_t>(tok0 & bs_mask) * tok_bytes;
-        kv[u] = *reinterpret_cast<const uint4*>(base + lane_off);
-      }
+        for (int c = 0; c < KC; ++c)
+          dst[j * KC + c] = load16(r, koff + c * 128, j * 8 * tok_bytes);
+    };
+    auto load_v = [&](uint4 (&dst)[VLOADS], int i) {
+      const auto r = block_rsrc(unit_base(vbase, i));
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if (g0 + u > last_g) break;                   // uniform
-        const int tok = (g0 + u) * TPI + row;         // chunk-local token
-        const bool valid = tok < n;
+      for (int j = 0; j < VLOADS; ++j) dst[j] = load16(r, voff, j * VTOK * tok_bytes);
+    };
+    // logits of one unit: raw q.k (scaled later), written by the lane holding
+    // column 0 of each token
+    auto qk_unit = [&](const uint4 (&kx)[KLOADS], int i) {
+      const int u = wave + kWaves * i;
+#pragma unroll
+      for (int j = 0; j < KGROUPS; ++j) {
         float sv[GTP];
 #pragma unroll
         for (int hh = 0; hh < GT; ++hh) {
-          float a = F::dot2(q4[hh].x, kv[u].x, 0.f);
-          a = F::dot2(q4[hh].y, kv[u].y, a);
-          a = F::dot2(q4[hh].z, kv[u].z, a);
-          a = F::dot2(q4[hh].w, kv[u].w, a);
-          const float s = group_sum<LPT>(a) * p.scale_log2;
-          mloc[hh] = valid ? fmaxf(mloc[hh], s) : mloc[hh];
-          sv[hh] = s;
+          float a = 0.f;
+#pragma unroll
+          for (int c = 0; c < KC; ++c) {
+            const uint4 k = kx[j * KC + c];
+            a = F::dot2(qv[hh][c].x, k.x, a);
+            a = F::dot2(qv[hh][c].y, k.y, a);
+            a = F::dot2(qv[hh][c].z, k.z, a);
+            a = F::dot2(qv[hh][c].w, k.w, a);
+          }
+          sv[hh] = group_sum<8>(a);
         }
 #pragma unroll
         for (int hh = GT; hh < GTP; ++hh) sv[hh] = 0.f;
-        if (valid && col == 0) {
-          float* dst = s_lds + tok * GTP;
-          if constexpr (GTP >= 4) {
-#pragma unroll
-            for (int k = 0; k < GTP; k += 4)
-              *reinterpret_cast<float4*>(dst + k) = make_float4(sv[k], sv[k + 1], sv[k + 2], sv[k + 3]);
-          } else if constexpr (GTP == 2) {
-            *reinterpret_cast<float2*>(dst) = make_float2(sv[0], sv[1]);
-          } else {
-            dst[0] = sv[0];
-          }
-        }
+        if (kcol == 0) lds_store(s_lds + (u * UNIT + j * 8 + krow) * GTP, sv);
       }
+    };
+    // P.V of one unit; tokens past the chunk end get V = 0 (their p is 0 and
+    // their slots may hold NaN)
+    auto pv_unit = [&](const uint4 (&vx)[VLOADS], int i) {
+      const int u = wave + kWaves * i;
+      const bool tail = (u + 1) * UNIT > n;
+#pragma unroll
+      for (int j = 0; j < VLOADS; ++j) {
+        const int t = u * UNIT + j * VTOK + vrow;
+        uint4 x = vx[j];
+        if (tail && t >= n) x = make_uint4(0, 0, 0, 0);
+        float pr[GTP];
+        lds_load(pr, s_lds + t * GTP);
+        float vf[8];
+        vf[0] = F::lo(x.x); vf[1] = F::hi(x.x);
+        vf[2] = F::lo(x.y); vf[3] = F::hi(x.y);
+        vf[4] = F::lo(x.z); vf[5] = F::hi(x.z);
+        vf[6] = F::lo(x.w); vf[7] = F::hi(x.w);
+#pragma unroll
+        for (int hh = 0; hh < GT; ++hh)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[hh][e] = fmaf(pr[hh], vf[e], acc[hh][e]);
+      }
+    };
+
+    // ---------------- phase 1: logits, double-buffered units ----------------
+    uint4 va[VLOADS];
+    if (cnt > 0) {
+      uint4 ka[KLOADS], kb[KLOADS];
+      load_k(ka, 0);
+      for (int i = 0; i < cnt; i += 2) {
+        load_k(kb, i + 1);
+        qk_unit(ka, i);
+        load_k(ka, i + 2);
+        if (i + 1 < cnt) qk_unit(kb, i + 1);
+      }
+      load_v(va, 0);                       // first V unit streams in during phase 2
     }
 
-    // ---------------- phase 2: chunk max, probabilities, sums ----------------
+    // ---------------- phase 2: scale, chunk max, probabilities, sums ----------------
+    __syncthreads();
+    float mloc[GT];
 #pragma unroll
-    for (int hh = 0; hh < GT; ++hh) mloc[hh] = wave_max_from(mloc[hh], LPT);
+    for (int hh = 0; hh < GT; ++hh) mloc[hh] = -__builtin_inff();
+    for (int t = tid; t < n; t += kThreads) {
+      float v[GTP];
+      lds_load(v, s_lds + t * GTP);
+#pragma unroll
+      for (int hh = 0; hh < GT; ++hh) {
+        v[hh] *= p.scale_log2;
+        mloc[hh] = v[hh] > mloc[hh] ? v[hh] : mloc[hh];
+      }
+      lds_store(s_lds + t * GTP, v);
+    }
+#pragma unroll
+    for (int hh = 0; hh < GT; ++hh) mloc[hh] = wave_max_from(mloc[hh], 1);
     if (lane == 0) {
 #pragma unroll
       for (int hh = 0; hh < GT; ++hh) wmax[wave * GTP + hh] = mloc[hh];
@@ -279,37 +388,16 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
     float lsum[GT];
 #pragma unroll
     for (int hh = 0; hh < GT; ++hh) lsum[hh] = 0.f;
-    const int npad = ng * TPI;
-    for (int t = tid; t < npad; t += kThreads) {
+    for (int t = tid; t < nunits * UNIT; t += kThreads) {
       float v[GTP];
-      float* src = s_lds + t * GTP;
-      if constexpr (GTP >= 4) {
-#pragma unroll
-        for (int k = 0; k < GTP; k += 4) {
-          const float4 f = *reinterpret_cast<const float4*>(src + k);
-          v[k] = f.x; v[k + 1] = f.y; v[k + 2] = f.z; v[k + 3] = f.w;
-        }
-      } else if constexpr (GTP == 2) {
-        const float2 f = *reinterpret_cast<const float2*>(src);
-        v[0] = f.x; v[1] = f.y;
-      } else {
-        v[0] = src[0];
-      }
+      lds_load(v, s_lds + t * GTP);
 #pragma unroll
       for (int hh = 0; hh < GT; ++hh) {
         const float pr = t < n ? fast_exp2(v[hh] - m_new[hh]) : 0.f;
         v[hh] = pr;
         lsum[hh] += pr;
       }
-      if constexpr (GTP >= 4) {
-#pragma unroll
-        for (int k = 0; k < GTP; k += 4)
-          *reinterpret_cast<float4*>(src + k) = make_float4(v[k], v[k + 1], v[k + 2], v[k + 3]);
-      } else if constexpr (GTP == 2) {
-        *reinterpret_cast<float2*>(src) = make_float2(v[0], v[1]);
-      } else {
-        src[0] = v[0];
-      }
+      lds_store(s_lds + t * GTP, v);
     }
 #pragma unroll
     for (int hh = 0; hh < GT; ++hh) lsum[hh] = wave_sum_from(lsum[hh], 1);
@@ -325,69 +413,39 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
       for (int w = 0; w < kWaves; ++w) lc += wsum[w * GTP + hh];
       l_run[hh] = l_run[hh] * alpha[hh] + lc;
     }
-    if constexpr (!SPLIT) {
 #pragma unroll
-      for (int hh = 0; hh < GT; ++hh)
+    for (int hh = 0; hh < GT; ++hh)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[hh][e] *= alpha[hh];
-    }
+      for (int e = 0; e < 8; ++e) acc[hh][e] = SPLIT ? 0.f : acc[hh][e] * alpha[hh];
 
-    // ---------------- phase 3: P . V ----------------
-    for (int g0 = wave * U; g0 < ng; g0 += kWaves * U) {
-      uint4 vv[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int g = min(g0 + u, last_g);
-        const int tok0 = c0 + g * TPI;
-        int blk = __builtin_amdgcn_readfirstlane(bt[tok0 >> p.log2_block_size]);
-        blk = (static_cast<unsigned>(blk) < static_cast<unsigned>(p.num_blocks)) ? blk : 0;
-        const char* base = vbase + blk * block_bytes +
-                           static_cast<int64_t>(tok0 & bs_mask) * tok_bytes;
-        vv[u] = *reinterpret_cast<const uint4*>(base + lane_off);
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if (g0 + u > last_g) break;                   // uniform
-        const int tok = (g0 + u) * TPI + row;
-        uint4 x = vv[u];
-        if (tok >= n) x = make_uint4(0, 0, 0, 0);     // unused slots may hold NaN
-        float pr[GTP];
-        const float* src = s_lds + tok * GTP;
-        if constexpr (GTP >= 4) {
-#pragma unroll
-          for (int k = 0; k < GTP; k += 4) {
-            const float4 f = *reinterpret_cast<const float4*>(src + k);
-            pr[k] = f.x; pr[k + 1] = f.y; pr[k + 2] = f.z; pr[k + 3] = f.w;
-          }
-        } else if constexpr (GTP == 2) {
-          const float2 f = *reinterpret_cast<const float2*>(src);
-          pr[0] = f.x; pr[1] = f.y;
-        } else {
-          pr[0] = src[0];
-        }
-        float vf[8];
-        vf[0] = F::lo(x.x); vf[1] = F::hi(x.x);
-        vf[2] = F::lo(x.y); vf[3] = F::hi(x.y);
-        vf[4] = F::lo(x.z); vf[5] = F::hi(x.z);
-        vf[6] = F::lo(x.w); vf[7] = F::hi(x.w);
-#pragma unroll
-        for (int hh = 0; hh < GT; ++hh)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) acc[hh][e] = fmaf(pr[hh], vf[e], acc[hh][e]);
+    // ---------------- phase 3: P . V, double-buffered units ----------------
+    if (cnt > 0) {
+      uint4 vb[VLOADS];
+      for (int i = 0; i < cnt; i += 2) {
+        load_v(vb, i + 1);
+        pv_unit(va, i);
+        load_v(va, i + 2);
+        if (i + 1 < cnt) pv_unit(vb, i + 1);
       }
     }
     __syncthreads();   // the next chunk reuses s_lds
+  };
+
+  if constexpr (SPLIT) {
+    run_chunk(t_begin, t_end - t_begin);
+  } else {
+    for (int c0 = t_begin; c0 < t_end; c0 += p.chunk) run_chunk(c0, min(p.chunk, t_end - c0));
   }
 
-  // ---------------- reduce over the tokens of the waves ----------------
+  // ---------------- reduce over the token rows of the waves ----------------
 #pragma unroll
   for (int hh = 0; hh < GT; ++hh)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[hh][e] = wave_sum_from(acc[hh][e], LPT);
-  if (row == 0) {
+    for (int e = 0; e < 8; ++e) acc[hh][e] = wave_sum_from(acc[hh][e], VL);
+  if (vrow == 0) {
 #pragma unroll
     for (int hh = 0; hh < GT; ++hh) {
-      float* dst = red + (wave * GT + hh) * D + col * 8;
+      float* dst = red + (wave * GT + hh) * D + vcol * 8;
       *reinterpret_cast<float4*>(dst) = make_float4(acc[hh][0], acc[hh][1], acc[hh][2], acc[hh][3]);
       *reinterpret_cast<float4*>(dst + 4) = make_float4(acc[hh][4], acc[hh][5], acc[hh][6], acc[hh][7]);
     }
