@@ -13,6 +13,7 @@ timed steps' decodes / wall time of the timed steps (GB/s); the decode call
 alone is also timed with HIP events on the step's stream (roofline.achieved).
 """
 import argparse
+import gc
 import json
 import os
 import sys
@@ -75,6 +76,8 @@ def main():
     ap.add_argument("--block-size", type=int, default=None, choices=[16, 32])
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--gc", dest="no_gc", action="store_false",
+                    help="keep Python's garbage collector on during the timed steps")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (for scaling "
                          "the FETCH_SIZE / WRITE_SIZE counters)")
@@ -119,19 +122,31 @@ def main():
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
            torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     kv_bytes = 0
+    host = np.zeros((args.steps, 4))                            # host seconds per phase
     torch.cuda.synchronize()
+    gc.collect()
+    gc_was_enabled = gc.isenabled()
+    if args.no_gc:
+        gc.disable()       # a collection pass over this large heap stalls the host for ~30 ms
     t_start = time.perf_counter()
     for k in range(args.steps):
+        h0 = time.perf_counter()
         b = step.prepare()                                      # a1
+        h1 = time.perf_counter()
         step.upload(b)                                          # a2
         ev[k][0].record(stream)
+        h2 = time.perf_counter()
         step.write_new(g.k_new, g.v_new)                        # a3
         ev[k][1].record(stream)
+        h3 = time.perf_counter()
         step.attend(g.q)                                        # a4 | a5 + a6
         ev[k][2].record(stream)
+        host[k] = (h1 - h0, h2 - h1, h3 - h2, time.perf_counter() - h3)
         kv_bytes += (int(step.host_context_lens.astype(np.int64).sum()) - shared) * per_tok
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
+    if gc_was_enabled:
+        gc.enable()
     log(f"[bench] {args.steps} timed steps done")
 
     t_write = np.array([a.elapsed_time(b) for a, b, _ in ev]) * 1e-3      # s
@@ -172,6 +187,10 @@ def main():
                               round(float(np.percentile(t_decode, 90)) * 1e6, 2)],
         "cache_write_us": round(float(t_write.mean()) * 1e6, 2),
         "decode_seqs_per_s": round(w.S / dec_avg, 1),
+        "host_us_per_step": dict(zip(("prepare", "upload", "write", "attend"),
+                                     (round(float(x) * 1e6, 1) for x in host.mean(axis=0)))),
+        "host_prepare_us_p50_max": [round(float(np.median(host[:, 0])) * 1e6, 1),
+                                    round(float(host[:, 0].max()) * 1e6, 1)],
         "roofline": {
             "bound": "hbm",
             "kernel": kernel_name,

@@ -144,6 +144,17 @@ size_t pa_decode_partitioned_workspace_size(int32_t num_seqs,
  *   partition_size    tokens per partition; a multiple of block_size,
  *                     at most 1024.  Partition p of sequence i covers tokens
  *                     [p*P, min(L_i, (p+1)*P)).
+ *   work_items        NULL, or a device array [num_work_items][2] int32 of
+ *                     (sequence, partition) pairs naming every partition to
+ *                     compute: each p < ceil(context_lens[i] / P) of every
+ *                     sequence exactly once, in any order.  A caller that
+ *                     knows the context lengths on the host (a scheduler
+ *                     does) passes it so that only live partitions are
+ *                     launched; with NULL the kernel covers all
+ *                     ceil(max_context_len / P) partitions of every sequence
+ *                     and the ones past a sequence's end exit at once.
+ *                     Pairs out of range are skipped; a missing or repeated
+ *                     pair gives unspecified output for that sequence.
  *   workspace         device buffer of at least
  *                     pa_decode_partitioned_workspace_size(...) bytes,
  *                     16-byte aligned; its contents on entry do not matter.
@@ -161,7 +172,9 @@ pa_status pa_decode_partitioned(void* out, const void* query,
                                 int32_t head_dim, int32_t block_size,
                                 int32_t num_blocks, int32_t max_context_len,
                                 float scale, pa_dtype dtype,
-                                int32_t partition_size, void* workspace,
+                                int32_t partition_size,
+                                const int32_t* work_items,
+                                int32_t num_work_items, void* workspace,
                                 size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------

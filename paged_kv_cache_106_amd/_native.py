@@ -60,7 +60,7 @@ _sig("pa_reshape_and_cache", _i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _
 _DEC = [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32]
 _sig("pa_decode", _i32, _DEC + [_vp])
 _sig("pa_decode_partitioned_workspace_size", _sz, [_i32, _i32, _i32, _i32, _i32])
-_sig("pa_decode_partitioned", _i32, _DEC + [_i32, _vp, _sz, _vp])
+_sig("pa_decode_partitioned", _i32, _DEC + [_i32, _vp, _i32, _vp, _sz, _vp])
 _sig("pa_copy_blocks", _i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp])
 _sig("pa_alloc_create", _i32, [_i32, _i32, _i32p, ctypes.POINTER(_vp)])
 _sig("pa_alloc_destroy", None, [_vp])
@@ -170,13 +170,37 @@ def pa_decode_partitioned_workspace_size(num_seqs, num_q_heads, head_dim, max_co
 
 
 def pa_decode_partitioned(out, query, key_cache, value_cache, block_tables, context_lens,
-                          max_context_len, scale, dtype, partition_size, workspace, stream=None):
-    """Split-context paged decode + merge; workspace is a uint8 GPU tensor."""
+                          max_context_len, scale, dtype, partition_size, workspace,
+                          work_items=None, stream=None):
+    """Split-context paged decode + merge; workspace is a uint8 GPU tensor;
+    work_items an optional int32 GPU tensor [n][2] of (sequence, partition)."""
     args = _decode_args(out, query, key_cache, value_cache, block_tables, context_lens,
                         max_context_len, scale, dtype)
-    _check(_lib.pa_decode_partitioned(*args, int(partition_size), _dptr(workspace, "workspace"),
+    if work_items is None:
+        wi, nwi = None, 0
+    else:
+        if work_items.dim() != 2 or work_items.shape[1] != 2:
+            raise ValueError("work_items must be [n][2]")
+        wi, nwi = (_dptr(work_items, "work_items", 4) if work_items.shape[0] else None), work_items.shape[0]
+    _check(_lib.pa_decode_partitioned(*args, int(partition_size), wi, int(nwi),
+                                      _dptr(workspace, "workspace"),
                                       workspace.numel() * workspace.element_size(),
                                       _stream(stream)))
+
+
+def partition_work_items(context_lens, partition_size, max_parts=None):
+    """Host-side work list for pa_decode_partitioned: (sequence, partition)
+    for every live partition, sequence-major.  context_lens: int array [S]."""
+    L = np.asarray(context_lens, dtype=np.int64)
+    nP = (L + partition_size - 1) // partition_size
+    if max_parts is not None:
+        nP = np.minimum(nP, max_parts)
+    total = int(nP.sum())
+    out = np.empty((total, 2), np.int32)
+    out[:, 0] = np.repeat(np.arange(L.shape[0], dtype=np.int32), nP)
+    start = np.repeat(np.cumsum(nP) - nP, nP)
+    out[:, 1] = np.arange(total, dtype=np.int64) - start
+    return out
 
 
 def pa_update_block_tables(block_tables, context_lens, slot_mapping, block_size, num_blocks,

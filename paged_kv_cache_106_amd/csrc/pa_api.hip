@@ -200,7 +200,8 @@ pa_status pa_decode_partitioned(void* out, const void* query, const void* key_ca
                                 int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                 int32_t head_dim, int32_t block_size, int32_t num_blocks,
                                 int32_t max_context_len, float scale, pa_dtype dtype,
-                                int32_t partition_size, void* workspace, size_t workspace_bytes,
+                                int32_t partition_size, const int32_t* work_items,
+                                int32_t num_work_items, void* workspace, size_t workspace_bytes,
                                 hipStream_t stream) {
   pa::clear_error();
   pa::AttnParams p;
@@ -213,8 +214,14 @@ pa_status pa_decode_partitioned(void* out, const void* query, const void* key_ca
       partition_size % block_size != 0)
     return fail(PA_ERR_INVALID_ARG,
                 "partition_size must be a multiple of block_size in [block_size, 1024]");
+  if (num_work_items < 0 || (num_work_items > 0 && !work_items) ||
+      (work_items && !pa::aligned(work_items, 4)))
+    return fail(PA_ERR_INVALID_ARG, "work_items must be NULL or a 4-byte aligned device array");
+  if (static_cast<int64_t>(num_work_items) * p.num_kv_heads * p.head_chunks > INT32_MAX)
+    return fail(PA_ERR_UNSUPPORTED, "num_work_items * num_kv_heads * head chunks overflows int32");
   if (num_seqs == 0) return PA_OK;
   const int64_t parts = (static_cast<int64_t>(max_context_len) + partition_size - 1) / partition_size;
+  if (parts >= pa::kMaxGrid) return fail(PA_ERR_UNSUPPORTED, "more than 65534 partitions");
   const pa::Workspace w = pa::workspace_layout(num_seqs, num_q_heads, head_dim, parts);
   if (!workspace || !pa::aligned(workspace, 16))
     return fail(PA_ERR_INVALID_ARG, "workspace must be a 16-byte aligned device buffer");
@@ -225,8 +232,12 @@ pa_status pa_decode_partitioned(void* out, const void* query, const void* key_ca
   p.part_sum = reinterpret_cast<float*>(ws + w.sum_off);
   p.chunk = partition_size;
   p.num_parts = static_cast<int32_t>(parts);
+  p.grid_parts = static_cast<int32_t>(parts | 1);
+  p.work_items = num_work_items > 0 ? work_items : nullptr;
+  p.num_work_items = num_work_items;
   auto launch = pa::attn_launcher(dtype, head_dim);
-  if (parts > 0) {
+  const bool any = work_items ? num_work_items > 0 : parts > 0;
+  if (any) {
     const pa_status s1 = pa::launched(launch(1, p, stream), "pa_decode_partitioned (partitions)");
     if (s1 != PA_OK) return s1;
   }

@@ -197,9 +197,41 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
   const int krow = lane >> 3, kcol = lane & 7;      // QK: token row, 16-byte column
   const int vrow = lane / VL, vcol = lane % VL;     // PV: token row, 16-byte column
 
-  const int seq = blockIdx.z;
-  const int kvh = blockIdx.y / p.head_chunks;
-  const int hc = blockIdx.y - kvh * p.head_chunks;
+  // Which (sequence, KV head x head chunk, partition) this workgroup serves.
+  //  single pass:  grid (KV heads x chunks, sequences)
+  //  split, list:  1-D grid over work items x (KV heads x chunks), the KV head
+  //                innermost, so the workgroups reading one token row run
+  //                together; items come from the caller, one per live
+  //                (sequence, partition), so no workgroup is empty
+  //  split, dense: grid (partitions, KV heads x chunks, sequences), partitions
+  //                fastest and their count odd: workgroups go to the 8 XCDs
+  //                round-robin by linear id, and an odd stride rotates each
+  //                sequence's partition p across them (partition p exists only
+  //                for sequences longer than p * P, so a fixed mapping would
+  //                load the XCDs unevenly)
+  int seq, kvhc, part = 0;
+  if constexpr (!SPLIT) {
+    kvhc = blockIdx.x;
+    seq = blockIdx.y;
+  } else {
+    if (p.work_items) {
+      const int nkv = p.num_kv_heads * p.head_chunks;
+      const int item = blockIdx.x / nkv;
+      kvhc = blockIdx.x - item * nkv;
+      seq = p.work_items[2 * item];
+      part = p.work_items[2 * item + 1];
+      if (static_cast<unsigned>(seq) >= static_cast<unsigned>(p.num_seqs) ||
+          static_cast<unsigned>(part) >= static_cast<unsigned>(p.num_parts))
+        return;                                     // uniform: whole workgroup
+    } else {
+      part = blockIdx.x;
+      kvhc = blockIdx.y;
+      seq = blockIdx.z;
+      if (part >= p.num_parts) return;
+    }
+  }
+  const int kvh = kvhc / p.head_chunks;
+  const int hc = kvhc - kvh * p.head_chunks;
   const int head0 = kvh * p.group + hc * GT;
   const int nact = min(GT, p.group - hc * GT);    // active heads of this chunk
 
@@ -207,7 +239,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
   L = max(0, min(L, p.mb * p.block_size));         // never past the table row
   int t_begin = 0, t_end = L;
   if constexpr (SPLIT) {
-    t_begin = blockIdx.x * p.chunk;
+    t_begin = part * p.chunk;
     if (t_begin >= L) return;                       // uniform: whole workgroup
     t_end = min(L, t_begin + p.chunk);
   }
@@ -460,7 +492,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) v += red[(w * GT + hh) * D + d];
       if constexpr (SPLIT) {
-        const int64_t slot = (out_row0 + hh) * p.num_parts + blockIdx.x;
+        const int64_t slot = (out_row0 + hh) * p.num_parts + part;
         p.part_acc[slot * D + d] = v;
         if (d == 0) {
           p.part_max[slot] = m_run[hh];
@@ -552,11 +584,13 @@ int launch_attn_gt(int kind, const AttnParams& p, hipStream_t stream) {
   using TL = Tile<D, GT>;
   const size_t lds = lds_floats(D, GT, TL::GTP, p.chunk) * sizeof(float);
   const dim3 block(kThreads);
+  const int nkv = p.num_kv_heads * p.head_chunks;
   if (kind == 0) {
-    const dim3 grid(1, p.num_kv_heads * p.head_chunks, p.num_seqs);
+    const dim3 grid(nkv, p.num_seqs, 1);
     hipLaunchKernelGGL((attn_kernel<DT, D, GT, false>), grid, block, lds, stream, p);
   } else {
-    const dim3 grid(p.num_parts, p.num_kv_heads * p.head_chunks, p.num_seqs);
+    const dim3 grid = p.work_items ? dim3(p.num_work_items * nkv, 1, 1)
+                                   : dim3(p.grid_parts, nkv, p.num_seqs);
     hipLaunchKernelGGL((attn_kernel<DT, D, GT, true>), grid, block, lds, stream, p);
   }
   return static_cast<int>(hipGetLastError());

@@ -37,6 +37,9 @@ struct AttnParams {
   int32_t num_blocks;
   int32_t chunk;              // tokens per pass over LDS (= partition size)
   int32_t num_parts;          // nP_max (split-context)
+  int32_t grid_parts;         // partitions in the dense grid (nP_max rounded up to odd)
+  const int32_t* work_items;  // [num_work_items][2] (seq, partition), or NULL: dense grid
+  int32_t num_work_items;
   float scale_log2;           // scale * log2(e): logits live in the base-2 domain
 };
 

@@ -8,7 +8,9 @@ a fixed batch of sequences, in the order the pages describe for a step
   a1  host: append_slot for every sequence -> slot mapping and context
       lengths (libpa's allocator, written straight into pinned host buffers);
   a2  one async host-to-device copy of that metadata (12 bytes per sequence,
-      plus copy-on-write pairs when there are any) on the step's stream;
+      copy-on-write pairs when there are any, and the list of live
+      (sequence, partition) work items for the split kernel) on the step's
+      stream;
   a3  pa_copy_blocks for copy-on-write, pa_update_block_tables (the device-
       resident tables gain each new token's block), pa_reshape_and_cache (the
       new tokens' K/V into their slots);
@@ -90,17 +92,23 @@ class DecodeStep:
             max_context_len = cache.num_blocks * bs
         self.max_context_len = int(max_context_len)
         self.mb = -(-self.max_context_len // bs)
+        self.max_parts = -(-self.max_context_len // self.partition_size)
+        self._num_items = [0, 0]
         self.scale = float(np.float32(1.0 / np.sqrt(cache.head_dim))) if scale is None else float(scale)
         self.stream = stream if stream is not None else torch.cuda.current_stream(cache.device)
         dev = cache.device
 
-        # per-step metadata: pinned host staging (double-buffered) and its device twin
+        # per-step metadata: built in ordinary (cached) host memory, copied in one
+        # memcpy into pinned staging (double-buffered; CPU stores straight into
+        # pinned pages can be very slow), then to the device twin
+        self._stage = np.zeros(self._meta_bytes(), np.uint8)
         self._host = [torch.empty(self._meta_bytes(), dtype=torch.uint8, pin_memory=True)
                       for _ in range(2)]
         self._events = [None, None]
         self._turn = 0
         self._dev_meta = torch.empty(self._meta_bytes(), dtype=torch.uint8, device=dev)
-        self.slot_mapping, self.context_lens, self.cow_pairs = self._views(self._dev_meta)
+        self.slot_mapping, self.context_lens, self.cow_pairs, self.work_items = \
+            self._views(self._dev_meta)
         self._num_cow = [0, 0]
         self.block_tables = torch.zeros((self.S, self.mb), dtype=torch.int32, device=dev)
         self.out = torch.empty((self.S, self.num_q_heads, cache.head_dim), dtype=torch.int16,
@@ -111,18 +119,26 @@ class DecodeStep:
         self.host_context_lens = np.zeros(self.S, np.int32)
         self.sync_tables()
 
-    # layout: slots int64 [S] | context_lens int32 [S] (+pad to 8 bytes) | cow pairs int32 [S][2]
-    def _meta_bytes(self):
-        return 8 * self.S + 4 * (self.S + (self.S & 1)) + 8 * self.S
-
-    def _views(self, buf):
+    # layout: slots int64 [S] | context_lens int32 [S] (+pad to 8 bytes) |
+    #         cow pairs int32 [S][2] | work items int32 [S * max_parts][2]
+    def _offsets(self):
         S = self.S
         o1 = 8 * S
         o2 = o1 + 4 * (S + (S & 1))
+        o3 = o2 + 8 * S
+        return o1, o2, o3
+
+    def _meta_bytes(self):
+        return self._offsets()[2] + 8 * self.S * self.max_parts
+
+    def _views(self, buf):
+        S = self.S
+        o1, o2, o3 = self._offsets()
         sm = buf[:o1].view(torch.int64)
         cl = buf[o1:o1 + 4 * S].view(torch.int32)
-        cow = buf[o2:o2 + 8 * S].view(torch.int32).view(S, 2)
-        return sm, cl, cow
+        cow = buf[o2:o3].view(torch.int32).view(S, 2)
+        items = buf[o3:].view(torch.int32).view(-1, 2)
+        return sm, cl, cow, items
 
     def sync_tables(self):
         """Upload the allocator's current tables and lengths (blocking)."""
@@ -142,7 +158,7 @@ class DecodeStep:
         self._turn ^= 1
         if self._events[b] is not None:
             self._events[b].synchronize()          # its previous copy has run
-        sm, cl, cow = (t.numpy() for t in self._views(self._host[b]))
+        sm, cl, cow, items = (t.numpy() for t in self._views(torch.from_numpy(self._stage)))
         if int(self.host_context_lens.max(initial=0)) >= self.max_context_len:
             raise ValueError("a sequence would outgrow max_context_len")
         _, _, src, dst = self.cache.allocator.append_slots(
@@ -153,12 +169,21 @@ class DecodeStep:
         if k.size:
             cow[: k.size, 0] = src[k]
             cow[: k.size, 1] = dst[k]
+        n = self._offsets()[1] + 8 * int(k.size)
+        if self.kernel == "partitioned":
+            wl = pa.partition_work_items(self.host_context_lens, self.partition_size, self.max_parts)
+            items[: wl.shape[0]] = wl
+            self._num_items[b] = int(wl.shape[0])
+            n = self._offsets()[2] + 8 * int(wl.shape[0])
+        self._host[b].numpy()[:n] = self._stage[:n]
+        self._nbytes = n
         return b
 
     def upload(self, b):
         """a2: async copy of the staged metadata to the device, on the step's stream."""
-        n = 8 * self.S + 4 * (self.S + (self.S & 1)) + 8 * self._num_cow[b]
+        n = self._nbytes
         self._ncow_dev = self._num_cow[b]
+        self._nitems_dev = self._num_items[b]
         with torch.cuda.stream(self.stream):
             self._dev_meta[:n].copy_(self._host[b][:n], non_blocking=True)
             ev = torch.cuda.Event()
@@ -186,7 +211,8 @@ class DecodeStep:
         else:
             pa.pa_decode_partitioned(self.out, q, c.key_cache, c.value_cache, self.block_tables,
                                      self.context_lens, self.max_context_len, self.scale, c.dtype,
-                                     self.partition_size, self.workspace, self.stream)
+                                     self.partition_size, self.workspace,
+                                     self.work_items[: self._nitems_dev], self.stream)
         return self.out
 
     def __call__(self, q, k_new, v_new):

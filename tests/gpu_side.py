@@ -48,7 +48,8 @@ def history_arrays(w: Workload):
     return spans, keys, values
 
 
-def build(w: Workload, kernel=None, partition_size=None, extra_tokens=0, poison=True) -> GpuState:
+def build(w: Workload, kernel=None, partition_size=None, extra_tokens=0, poison=True,
+          mcl=None) -> GpuState:
     cache = PagedKVCache(w.num_blocks, w.bs, w.Hkv, w.D, w.dtype, w.initial_free_order,
                          poison=poison)
     for op in w.alloc_ops:
@@ -61,7 +62,7 @@ def build(w: Workload, kernel=None, partition_size=None, extra_tokens=0, poison=
     del keys, values
     step = DecodeStep(cache, np.arange(w.S), w.Hq, kernel or w.spec.kernel,
                       partition_size or w.spec.partition_size,
-                      max_context_len=int(w.lengths.max()) + extra_tokens, scale=w.scale)
+                      max_context_len=int(w.lengths.max()) + extra_tokens if mcl is None else mcl, scale=w.scale)
     q, k_new, v_new = dev16(w.query()), dev16(w.new_tokens("k")), dev16(w.new_tokens("v"))
     b = step.prepare()
     step.upload(b)

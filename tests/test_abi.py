@@ -64,7 +64,7 @@ def decode(**kw):
                        a["NB"], a["maxlen"], a["scale"], a["dtype"], None)
 
 
-def decode_part(P=512, ws=BAD, ws_bytes=1 << 30, **kw):
+def decode_part(P=512, ws=BAD, ws_bytes=1 << 30, items=None, nitems=0, **kw):
     a = dict(out=BAD, query=BAD, key_cache=BAD, value_cache=BAD, block_tables=BAD, mb=64,
              context_lens=BAD, S=2, Hq=8, Hkv=2, D=128, bs=16, NB=10, maxlen=1024, scale=0.088,
              dtype=1)
@@ -72,7 +72,7 @@ def decode_part(P=512, ws=BAD, ws_bytes=1 << 30, **kw):
     return L.pa_decode_partitioned(a["out"], a["query"], a["key_cache"], a["value_cache"],
                                    a["block_tables"], a["mb"], a["context_lens"], a["S"], a["Hq"],
                                    a["Hkv"], a["D"], a["bs"], a["NB"], a["maxlen"], a["scale"],
-                                   a["dtype"], P, ws, ws_bytes, None)
+                                   a["dtype"], P, items, nitems, ws, ws_bytes, None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -106,9 +106,18 @@ def test_decode_empty_batch_is_a_noop():
     (dict(ws=None), _native.PA_ERR_INVALID_ARG),
     (dict(ws=MIS), _native.PA_ERR_INVALID_ARG),
     (dict(ws_bytes=100), _native.PA_ERR_INVALID_ARG),
+    (dict(items=None, nitems=4), _native.PA_ERR_INVALID_ARG),
+    (dict(items=MIS, nitems=4), _native.PA_ERR_INVALID_ARG),
+    (dict(nitems=-1), _native.PA_ERR_INVALID_ARG),
 ])
 def test_partitioned_rejects_on_host(kw, status):
     assert decode_part(**kw) == status
+
+
+def test_partition_work_items():
+    wl = pa.partition_work_items([1, 1024, 1025, 0, 512], 512)
+    assert wl.tolist() == [[0, 0], [1, 0], [1, 1], [2, 0], [2, 1], [2, 2], [4, 0]]
+    assert pa.partition_work_items([5000], 512, max_parts=4).tolist() == [[0, p] for p in range(4)]
 
 
 def test_workspace_size_formula():

@@ -62,14 +62,19 @@ def free_gpu():
     torch.cuda.empty_cache()
 
 
-def run_partitioned(g, w, P, max_context_len=None):
+def run_partitioned(g, w, P, max_context_len=None, listed=False, lens=None):
+    """Split-context decode: the dense grid, or with a host work list."""
     mcl = int(w.lengths.max()) if max_context_len is None else max_context_len
     ws = torch.empty(max(pa.pa_decode_partitioned_workspace_size(w.S, w.Hq, w.D, mcl, P), 16),
                      dtype=torch.uint8, device="cuda")
     out = torch.full((w.S, w.Hq, w.D), 0x7FFF, dtype=torch.int16, device="cuda")
     c, st = g.cache, g.step
+    items = None
+    if listed:
+        wl = pa.partition_work_items(w.lengths if lens is None else lens, P)
+        items = torch.from_numpy(wl[::-1].copy()).cuda()        # any order is allowed
     pa.pa_decode_partitioned(out, g.q, c.key_cache, c.value_cache, st.block_tables, st.context_lens,
-                             mcl, w.scale, w.dtype, P, ws)
+                             mcl, w.scale, w.dtype, P, ws, items)
     torch.cuda.synchronize()
     return gpu_side.to_host16(out)
 
@@ -117,6 +122,8 @@ def test_small_workloads(cfg, bs):
     check_outputs(run_single(g, w), ref32, refT, w.dtype, label + " single")
     for P in sorted({w.bs, 3 * w.bs, 512}):
         check_outputs(run_partitioned(g, w, P), ref32, refT, w.dtype, label + f" P={P}")
+        check_outputs(run_partitioned(g, w, P, listed=True), ref32, refT, w.dtype,
+                      label + f" P={P} listed")
     del g
     free_gpu()
 
@@ -157,6 +164,8 @@ def test_edge_lengths(Hq, Hkv, D, bs, dtype):
     check_outputs(run_single(g, w), ref32, refT, dtype, label + " single")
     for PP in (bs, P, 1024):
         check_outputs(run_partitioned(g, w, PP), ref32, refT, dtype, label + f" P={PP}")
+        check_outputs(run_partitioned(g, w, PP, listed=True), ref32, refT, dtype,
+                      label + f" P={PP} listed")
     del g
     free_gpu()
 
@@ -170,7 +179,10 @@ def test_zero_length_and_empty_batch():
     # sequence 2 reports no tokens: its rows become zeros, the others are unchanged
     g.step.context_lens[2] = 0
     torch.cuda.synchronize()
-    for out in (run_single(g, w), run_partitioned(g, w, 512)):
+    lens0 = w.lengths.copy()
+    lens0[2] = 0
+    for out in (run_single(g, w), run_partitioned(g, w, 512),
+                run_partitioned(g, w, 512, listed=True, lens=lens0)):
         assert np.all(out[2] == 0)
         keep = [i for i in range(w.S) if i != 2]
         check_outputs(out[keep], ref32[keep], refT[keep], w.dtype, "L=0 neighbours")
