@@ -190,16 +190,21 @@ def pa_decode_partitioned(out, query, key_cache, value_cache, block_tables, cont
 
 def partition_work_items(context_lens, partition_size, max_parts=None):
     """Host-side work list for pa_decode_partitioned: (sequence, partition)
-    for every live partition, sequence-major.  context_lens: int array [S]."""
+    for every live partition.  Full partitions come first (sequence-major),
+    then the ragged last partitions by decreasing length, so the shortest
+    work fills the tail of the launch.  context_lens: int array [S]."""
     L = np.asarray(context_lens, dtype=np.int64)
     nP = (L + partition_size - 1) // partition_size
     if max_parts is not None:
         nP = np.minimum(nP, max_parts)
     total = int(nP.sum())
+    seq = np.repeat(np.arange(L.shape[0], dtype=np.int64), nP)
+    part = np.arange(total, dtype=np.int64) - np.repeat(np.cumsum(nP) - nP, nP)
+    ntok = np.minimum(partition_size, L[seq] - part * partition_size)
+    order = np.argsort(-ntok, kind="stable")
     out = np.empty((total, 2), np.int32)
-    out[:, 0] = np.repeat(np.arange(L.shape[0], dtype=np.int32), nP)
-    start = np.repeat(np.cumsum(nP) - nP, nP)
-    out[:, 1] = np.arange(total, dtype=np.int64) - start
+    out[:, 0] = seq[order]
+    out[:, 1] = part[order]
     return out
 
 

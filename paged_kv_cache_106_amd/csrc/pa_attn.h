@@ -183,6 +183,40 @@ __device__ inline uint4 load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
+// Wave-wide reductions that leave the result in every lane: a DPP butterfly
+// inside each 16-lane row, then the four row results read back as scalars.
+__device__ inline float wave_max_all(float x) {
+  x = fmaxf(x, dpp<0xB1>(x));
+  x = fmaxf(x, dpp<0x4E>(x));
+  x = fmaxf(x, dpp<0x141>(x));
+  x = fmaxf(x, dpp<0x140>(x));
+  const float a = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 0));
+  const float b = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 16));
+  const float c = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 32));
+  const float d = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 48));
+  return fmaxf(fmaxf(a, b), fmaxf(c, d));
+}
+
+__device__ inline float wave_sum_all(float x) {
+  x = group_sum<16>(x);
+  const float a = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 0));
+  const float b = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 16));
+  const float c = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 32));
+  const float d = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 48));
+  return (a + b) + (c + d);
+}
+
+// Makes a wave's own LDS writes visible to its other lanes before they read.
+__device__ inline void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Each wave runs its own softmax over its own units: logits, its running max
+// m, sum l and accumulator acc (in the base-2 domain), with no workgroup
+// barrier until the four waves' (m, l, acc) are combined at the end:
+//   M = max_w m_w,  acc = sum_w 2^(m_w - M) acc_w,  l = sum_w 2^(m_w - M) l_w.
 template <int DT, int D, int GT, bool SPLIT>
 __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
   using F = Fmt<DT>;
@@ -270,7 +304,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
   float* wsum = wmax + kWaves * GTP;                        // [kWaves][GTP]
 
   float acc[GT][8];
-  float m_run[GT], l_run[GT];
+  float m_run[GT], l_run[GT];                       // wave-uniform
 #pragma unroll
   for (int hh = 0; hh < GT; ++hh) {
     m_run[hh] = -__builtin_inff();
@@ -281,24 +315,22 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
     }
   }
 
-  // One chunk of n tokens from c0: logits, softmax statistics, P.V.  The
-  // split kernel runs it once (q is dead after the logits and acc is born at
-  // P.V, so the two never share registers); the single-pass kernel loops.
+  // One chunk of n tokens from c0 for this wave's units (u = wave, wave + 4,
+  // ...): logits, its own softmax statistics, P.V.  The split kernel runs it
+  // once (q is dead after the logits and acc is born at the softmax, so the
+  // two never share registers); the single-pass kernel loops.
   auto run_chunk = [&](const int c0, const int n) {
-    // q slices for the QK layout: chunk c of head hh = dims c*64 + kcol*8 .. +8
-    uint4 qv[GT][KC];
-    {
-      const uint16_t* q = static_cast<const uint16_t*>(p.q);
-#pragma unroll
-      for (int hh = 0; hh < GT; ++hh)
-#pragma unroll
-        for (int c = 0; c < KC; ++c)
-          qv[hh][c] = hh < nact
-                          ? *reinterpret_cast<const uint4*>(q + (out_row0 + hh) * D + c * 64 + kcol * 8)
-                          : make_uint4(0, 0, 0, 0);
-    }
     const int nunits = (n + UNIT - 1) / UNIT;
-    const int cnt = nunits > wave ? (nunits - wave + kWaves - 1) / kWaves : 0;  // units of this wave
+    const int cnt = nunits > wave ? (nunits - wave + kWaves - 1) / kWaves : 0;
+    if (cnt == 0) {                                 // uniform: this wave has no tokens
+      if constexpr (SPLIT) {
+#pragma unroll
+        for (int hh = 0; hh < GT; ++hh)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[hh][e] = 0.f;
+      }
+      return;
+    }
 
     // base of the i-th unit of this wave (clamped to its last unit: extra
     // prefetches at the end of a loop re-read a unit already in cache)
@@ -322,8 +354,21 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
 #pragma unroll
       for (int j = 0; j < VLOADS; ++j) dst[j] = load16(r, voff, j * VTOK * tok_bytes);
     };
-    // logits of one unit: raw q.k (scaled later), written by the lane holding
-    // column 0 of each token
+
+    // q slices for the QK layout: chunk c of head hh = dims c*64 + kcol*8 .. +8
+    uint4 qv[GT][KC];
+    {
+      const uint16_t* q = static_cast<const uint16_t*>(p.q);
+#pragma unroll
+      for (int hh = 0; hh < GT; ++hh)
+#pragma unroll
+        for (int c = 0; c < KC; ++c)
+          qv[hh][c] = hh < nact
+                          ? *reinterpret_cast<const uint4*>(q + (out_row0 + hh) * D + c * 64 + kcol * 8)
+                          : make_uint4(0, 0, 0, 0);
+    }
+    // logits of one unit (raw q.k; scaled in the softmax step), written by
+    // the lane holding column 0 of each token
     auto qk_unit = [&](const uint4 (&kx)[KLOADS], int i) {
       const int u = wave + kWaves * i;
 #pragma unroll
@@ -368,12 +413,14 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
         for (int hh = 0; hh < GT; ++hh)
 #pragma unroll
           for (int e = 0; e < 8; ++e) acc[hh][e] = fmaf(pr[hh], vf[e], acc[hh][e]);
+        // keep each group's probabilities and widened V short-lived
+        __builtin_amdgcn_sched_barrier(0);
       }
     };
 
-    // ---------------- phase 1: logits, double-buffered units ----------------
+    // ---- logits of the wave's units, double-buffered ----
     uint4 va[VLOADS];
-    if (cnt > 0) {
+    {
       uint4 ka[KLOADS], kb[KLOADS];
       load_k(ka, 0);
       for (int i = 0; i < cnt; i += 2) {
@@ -382,45 +429,39 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
         load_k(ka, i + 2);
         if (i + 1 < cnt) qk_unit(kb, i + 1);
       }
-      load_v(va, 0);                       // first V unit streams in during phase 2
     }
+    load_v(va, 0);                         // the first V unit streams in during the softmax
+    wave_lds_sync();
 
-    // ---------------- phase 2: scale, chunk max, probabilities, sums ----------------
-    __syncthreads();
+    // ---- the wave's softmax over its tokens (lane l: wave tokens l, l+64, ...) ----
+    const int wtok = cnt * UNIT;
+    auto tok_of = [&](int r) { return (wave + kWaves * (r / UNIT)) * UNIT + (r % UNIT); };
     float mloc[GT];
 #pragma unroll
     for (int hh = 0; hh < GT; ++hh) mloc[hh] = -__builtin_inff();
-    for (int t = tid; t < n; t += kThreads) {
+    for (int r = lane; r < wtok; r += 64) {
+      const int t = tok_of(r);
       float v[GTP];
       lds_load(v, s_lds + t * GTP);
 #pragma unroll
       for (int hh = 0; hh < GT; ++hh) {
         v[hh] *= p.scale_log2;
-        mloc[hh] = v[hh] > mloc[hh] ? v[hh] : mloc[hh];
+        if (t < n) mloc[hh] = v[hh] > mloc[hh] ? v[hh] : mloc[hh];
       }
       lds_store(s_lds + t * GTP, v);
     }
-#pragma unroll
-    for (int hh = 0; hh < GT; ++hh) mloc[hh] = wave_max_from(mloc[hh], 1);
-    if (lane == 0) {
-#pragma unroll
-      for (int hh = 0; hh < GT; ++hh) wmax[wave * GTP + hh] = mloc[hh];
-    }
-    __syncthreads();
     float m_new[GT], alpha[GT];
 #pragma unroll
     for (int hh = 0; hh < GT; ++hh) {
-      float mc = wmax[hh];
-#pragma unroll
-      for (int w = 1; w < kWaves; ++w) mc = fmaxf(mc, wmax[w * GTP + hh]);
-      m_new[hh] = fmaxf(m_run[hh], mc);
+      m_new[hh] = fmaxf(m_run[hh], wave_max_all(mloc[hh]));
       alpha[hh] = fast_exp2(m_run[hh] - m_new[hh]);   // 0 on the first chunk
       m_run[hh] = m_new[hh];
     }
     float lsum[GT];
 #pragma unroll
     for (int hh = 0; hh < GT; ++hh) lsum[hh] = 0.f;
-    for (int t = tid; t < nunits * UNIT; t += kThreads) {
+    for (int r = lane; r < wtok; r += 64) {
+      const int t = tok_of(r);
       float v[GTP];
       lds_load(v, s_lds + t * GTP);
 #pragma unroll
@@ -432,26 +473,15 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
       lds_store(s_lds + t * GTP, v);
     }
 #pragma unroll
-    for (int hh = 0; hh < GT; ++hh) lsum[hh] = wave_sum_from(lsum[hh], 1);
-    if (lane == 0) {
-#pragma unroll
-      for (int hh = 0; hh < GT; ++hh) wsum[wave * GTP + hh] = lsum[hh];
-    }
-    __syncthreads();
-#pragma unroll
     for (int hh = 0; hh < GT; ++hh) {
-      float lc = 0.f;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) lc += wsum[w * GTP + hh];
-      l_run[hh] = l_run[hh] * alpha[hh] + lc;
-    }
-#pragma unroll
-    for (int hh = 0; hh < GT; ++hh)
+      l_run[hh] = l_run[hh] * alpha[hh] + wave_sum_all(lsum[hh]);
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[hh][e] = SPLIT ? 0.f : acc[hh][e] * alpha[hh];
+    }
+    wave_lds_sync();
 
-    // ---------------- phase 3: P . V, double-buffered units ----------------
-    if (cnt > 0) {
+    // ---- P . V of the wave's units, double-buffered ----
+    {
       uint4 vb[VLOADS];
       for (int i = 0; i < cnt; i += 2) {
         load_v(vb, i + 1);
@@ -460,7 +490,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
         if (i + 1 < cnt) pv_unit(vb, i + 1);
       }
     }
-    __syncthreads();   // the next chunk reuses s_lds
+    wave_lds_sync();                       // the next chunk rewrites this wave's rows
   };
 
   if constexpr (SPLIT) {
@@ -469,7 +499,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
     for (int c0 = t_begin; c0 < t_end; c0 += p.chunk) run_chunk(c0, min(p.chunk, t_end - c0));
   }
 
-  // ---------------- reduce over the token rows of the waves ----------------
+  // ---------------- combine the waves ----------------
 #pragma unroll
   for (int hh = 0; hh < GT; ++hh)
 #pragma unroll
@@ -482,24 +512,43 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
       *reinterpret_cast<float4*>(dst + 4) = make_float4(acc[hh][4], acc[hh][5], acc[hh][6], acc[hh][7]);
     }
   }
+  if (lane == 0) {
+#pragma unroll
+    for (int hh = 0; hh < GT; ++hh) {
+      wmax[wave * GTP + hh] = m_run[hh];
+      wsum[wave * GTP + hh] = l_run[hh];
+    }
+  }
   __syncthreads();
 
 #pragma unroll
   for (int hh = 0; hh < GT; ++hh) {
     if (hh >= nact) break;
+    float mw[kWaves], M = -__builtin_inff();
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      mw[w] = wmax[w * GTP + hh];
+      M = fmaxf(M, mw[w]);
+    }
+    float wt[kWaves], lt = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      wt[w] = fast_exp2(mw[w] - M);                 // 0 for a wave without tokens
+      lt += wt[w] * wsum[w * GTP + hh];
+    }
     for (int d = tid; d < D; d += kThreads) {
       float v = 0.f;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) v += red[(w * GT + hh) * D + d];
+      for (int w = 0; w < kWaves; ++w) v += wt[w] * red[(w * GT + hh) * D + d];
       if constexpr (SPLIT) {
         const int64_t slot = (out_row0 + hh) * p.num_parts + part;
         p.part_acc[slot * D + d] = v;
         if (d == 0) {
-          p.part_max[slot] = m_run[hh];
-          p.part_sum[slot] = l_run[hh];
+          p.part_max[slot] = M;
+          p.part_sum[slot] = lt;
         }
       } else {
-        static_cast<uint16_t*>(p.out)[(out_row0 + hh) * D + d] = F::narrow(v / l_run[hh]);
+        static_cast<uint16_t*>(p.out)[(out_row0 + hh) * D + d] = F::narrow(v / lt);
       }
     }
   }

@@ -115,8 +115,9 @@ def test_partitioned_rejects_on_host(kw, status):
 
 
 def test_partition_work_items():
-    wl = pa.partition_work_items([1, 1024, 1025, 0, 512], 512)
-    assert wl.tolist() == [[0, 0], [1, 0], [1, 1], [2, 0], [2, 1], [2, 2], [4, 0]]
+    wl = pa.partition_work_items([1, 1024, 1025, 0, 512, 700], 512)
+    # full partitions first (sequence-major), then ragged ones by decreasing length
+    assert wl.tolist() == [[1, 0], [1, 1], [2, 0], [2, 1], [4, 0], [5, 0], [5, 1], [0, 0], [2, 2]]
     assert pa.partition_work_items([5000], 512, max_parts=4).tolist() == [[0, p] for p in range(4)]
 
 
