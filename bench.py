@@ -35,36 +35,70 @@ def log(*a):
 
 def cpu_baseline(w, budget_s):
     """The oracle as it stands, timed on the host cores over whole sequences of
-    the same workload until about budget_s seconds of work."""
+    the same workload (in a seeded order, cycling) until about budget_s
+    seconds of work."""
     import oracle
     from tests import oracle_side
 
     o = oracle_side.build(w)
     threads = len(os.sched_getaffinity(0))
     per_tok = 2 * w.Hkv * w.D * w.elem_bytes
-    spent, done_bytes, seqs = 0.0, 0, []
+    spent, done_bytes, nseq, ntok = 0.0, 0, 0, 0
     order = np.random.default_rng(1234).permutation(w.S)
     k = 0
-    while spent < budget_s and k < w.S:
-        batch = [int(i) for i in order[k:k + 4]]
-        k += len(batch)
+    while spent < budget_s:
+        batch = [int(order[(k + j) % w.S]) for j in range(4)]
+        k += 4
         pairs = np.array([[i, h] for i in batch for h in range(w.Hq)], np.int32)
         t0 = time.perf_counter()
         oracle.decode_pairs(o.q, o.key_cache, o.value_cache, o.block_tables, o.context_lens,
                             w.scale, w.dtype, pairs, nthreads=threads)
         spent += time.perf_counter() - t0
-        done_bytes += int(sum(int(w.lengths[i]) for i in batch)) * per_tok
-        seqs += batch
+        toks = int(sum(int(w.lengths[i]) for i in batch))
+        done_bytes += toks * per_tok
+        ntok += toks
+        nseq += len(batch)
     return {
         "value": done_bytes / spent / 1e9,
         "unit": "GB/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": (f"{len(seqs)} of {w.S} sequences (all {w.Hq} q heads each, "
-                   f"{sum(int(w.lengths[i]) for i in seqs)} tokens), {spent:.1f} s; "
+        "sample": (f"{nseq} sequence decodes drawn cyclically from the workload's {w.S} "
+                   f"(all {w.Hq} q heads each, {ntok} tokens), {spent:.1f} s of oracle time; "
                    "logical K/V bytes of the sample / oracle decode time"),
-        "seqs_per_s": len(seqs) / spent,
+        "seqs_per_s": nseq / spent,
     }
+
+
+def kernel_source_sha256():
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "paged_kv_cache_106_amd", "csrc", "*"))):
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(config_id, block_size):
+    """HBM bytes per decode call from the committed PMC summary of this
+    workload, or None if there is none or the kernel sources changed since."""
+    import glob
+    import re
+    names = {3: "decode_qwen25_7b_gqa_64seq_pmc.md"}
+    name = names.get(config_id) if block_size in (None, 16) else None
+    if not name:
+        return None
+    path = os.path.join(ROOT, "profiles", name)
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    sha = re.search(r"^kernel_source_sha256: (\w+)", text, re.M)
+    tr = re.search(r"^traffic_bytes_per_call: (\d+)", text, re.M)
+    if not sha or not tr or sha.group(1) != kernel_source_sha256():
+        return None
+    return int(tr.group(1))
 
 
 def main():
@@ -198,7 +232,8 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": recorded_traffic(args.config, args.block_size),
+            "traffic_unit": "bytes per decode call (FETCH_SIZE x2 + WRITE_SIZE, copy-calibrated)",
         },
     }
     del g
