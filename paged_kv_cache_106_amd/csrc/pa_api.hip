@@ -217,7 +217,7 @@ pa_status pa_decode_partitioned(void* out, const void* query, const void* key_ca
   if (num_work_items < 0 || (num_work_items > 0 && !work_items) ||
       (work_items && !pa::aligned(work_items, 4)))
     return fail(PA_ERR_INVALID_ARG, "work_items must be NULL or a 4-byte aligned device array");
-  if (static_cast<int64_t>(num_work_items) * p.num_kv_heads * p.head_chunks > INT32_MAX)
+  if ((static_cast<int64_t>(num_work_items) + 7) * p.num_kv_heads * p.head_chunks > INT32_MAX)
     return fail(PA_ERR_UNSUPPORTED, "num_work_items * num_kv_heads * head chunks overflows int32");
   if (num_seqs == 0) return PA_OK;
   const int64_t parts = (static_cast<int64_t>(max_context_len) + partition_size - 1) / partition_size;

@@ -173,9 +173,13 @@ __device__ inline void lds_load(float (&v)[N], const float* src) {
   }
 }
 
-// Buffer resource over one physical block (the base is wave-uniform).
-__device__ inline __amdgpu_buffer_rsrc_t block_rsrc(const char* base) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, 0x7fffffff, 0x00020000);
+// Buffer resource over one physical block (the base is wave-uniform).  With
+// num_records = 0 every load through it is out of range: the hardware returns
+// zeros without touching memory, which makes prefetches past a wave's last
+// unit free.
+__device__ inline __amdgpu_buffer_rsrc_t block_rsrc(const char* base, bool live) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, live ? 0x7fffffff : 0,
+                                           0x00020000);
 }
 
 __device__ inline uint4 load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
@@ -233,10 +237,10 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
 
   // Which (sequence, KV head x head chunk, partition) this workgroup serves.
   //  single pass:  grid (KV heads x chunks, sequences)
-  //  split, list:  1-D grid over work items x (KV heads x chunks), the KV head
-  //                innermost, so the workgroups reading one token row run
-  //                together; items come from the caller, one per live
-  //                (sequence, partition), so no workgroup is empty
+  //  split, list:  1-D grid over work items x (KV heads x chunks); the KV
+  //                heads of an item (one token row) land on one XCD, and
+  //                items come from the caller, one per live (sequence,
+  //                partition), so no workgroup is empty
   //  split, dense: grid (partitions, KV heads x chunks, sequences), partitions
   //                fastest and their count odd: workgroups go to the 8 XCDs
   //                round-robin by linear id, and an odd stride rotates each
@@ -249,9 +253,14 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
     seq = blockIdx.y;
   } else {
     if (p.work_items) {
+      // linear id = (item / 8) * 8 * nkv + kvhc * 8 + item % 8: ids equal mod 8
+      // share an XCD, so the KV heads of one item (one token row) do
       const int nkv = p.num_kv_heads * p.head_chunks;
-      const int item = blockIdx.x / nkv;
-      kvhc = blockIdx.x - item * nkv;
+      const int grp = blockIdx.x / (8 * nkv);
+      const int r = blockIdx.x - grp * 8 * nkv;
+      kvhc = r >> 3;
+      const int item = grp * 8 + (r & 7);
+      if (item >= p.num_work_items) return;         // uniform: whole workgroup
       seq = p.work_items[2 * item];
       part = p.work_items[2 * item + 1];
       if (static_cast<unsigned>(seq) >= static_cast<unsigned>(p.num_seqs) ||
@@ -332,8 +341,8 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
       return;
     }
 
-    // base of the i-th unit of this wave (clamped to its last unit: extra
-    // prefetches at the end of a loop re-read a unit already in cache)
+    // base of the i-th unit of this wave (clamped to its last unit; loads for
+    // i >= cnt go through an empty descriptor and fetch nothing)
     auto unit_base = [&](const char* pool, int i) -> const char* {
       const int u = wave + kWaves * min(i, cnt - 1);
       const int t0 = c0 + u * UNIT;
@@ -342,7 +351,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
       return pool + blk * block_bytes + static_cast<int64_t>(t0 & bs_mask) * tok_bytes;
     };
     auto load_k = [&](uint4 (&dst)[KLOADS], int i) {
-      const auto r = block_rsrc(unit_base(kbase, i));
+      const auto r = block_rsrc(unit_base(kbase, i), i < cnt);
 #pragma unroll
       for (int j = 0; j < KGROUPS; ++j)
 #pragma unroll
@@ -350,7 +359,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
           dst[j * KC + c] = load16(r, koff + c * 128, j * 8 * tok_bytes);
     };
     auto load_v = [&](uint4 (&dst)[VLOADS], int i) {
-      const auto r = block_rsrc(unit_base(vbase, i));
+      const auto r = block_rsrc(unit_base(vbase, i), i < cnt);
 #pragma unroll
       for (int j = 0; j < VLOADS; ++j) dst[j] = load16(r, voff, j * VTOK * tok_bytes);
     };
@@ -638,7 +647,7 @@ int launch_attn_gt(int kind, const AttnParams& p, hipStream_t stream) {
     const dim3 grid(nkv, p.num_seqs, 1);
     hipLaunchKernelGGL((attn_kernel<DT, D, GT, false>), grid, block, lds, stream, p);
   } else {
-    const dim3 grid = p.work_items ? dim3(p.num_work_items * nkv, 1, 1)
+    const dim3 grid = p.work_items ? dim3(((p.num_work_items + 7) / 8) * 8 * nkv, 1, 1)
                                    : dim3(p.grid_parts, nkv, p.num_seqs);
     hipLaunchKernelGGL((attn_kernel<DT, D, GT, true>), grid, block, lds, stream, p);
   }
