@@ -71,10 +71,14 @@ def cpu_baseline(w, budget_s):
 
 
 def kernel_source_sha256():
+    """sha256 over the sources the decode kernels are built and launched from."""
     import glob
     import hashlib
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(ROOT, "paged_kv_cache_106_amd", "csrc", "*"))):
+    csrc = os.path.join(ROOT, "paged_kv_cache_106_amd", "csrc")
+    files = glob.glob(os.path.join(csrc, "pa_attn*")) + [
+        os.path.join(csrc, "pa_internal.h"), os.path.join(csrc, "pa_api.hip")]
+    for f in sorted(files):
         h.update(os.path.basename(f).encode())
         with open(f, "rb") as fh:
             h.update(fh.read())

@@ -103,6 +103,8 @@ pa_status check_decode(void* out, const void* query, const void* key_cache,
   p->group = group;
   p->heads_per_wg = gt;
   p->head_chunks = chunks;
+  p->work_items = nullptr;
+  p->num_work_items = 0;
   p->block_size = block_size;
   p->log2_block_size = log2_exact(block_size);
   p->num_blocks = num_blocks;

@@ -8,30 +8,34 @@
 // same workgroup, so every K/V byte is read from HBM once for all of them.
 //
 // Workgroup = 4 waves = 256 lanes, one (sequence, KV head, head chunk[,
-// partition]).  Its token range is processed in chunks of `chunk` tokens
-// (the partition size for the split kernel), each in three phases:
+// partition]).  Its tokens are cut into units of 16 and wave w takes units
+// w, w+4, ...; each wave runs its own softmax over its units, chunk by chunk
+// (the partition for the split kernel), in three phases:
 //
-//  1. logits.  A token's K row for one KV head is D*2 bytes; LPT = D/8 lanes
-//     each load 16 bytes of it (one global_load_dwordx4), so a wave load
-//     covers TPI = 64/LPT tokens that always sit in one physical block.
-//     Each lane takes partial dot products of its 8 elements with the
-//     matching 8 elements of every q head (v_dot2 on 16-bit pairs, fp32
-//     accumulate), and DPP row operations sum the LPT partials.  Logits,
-//     in the base-2 domain (scale * log2 e folded in), go to LDS.
-//  2. softmax statistics.  Per-head chunk max across the workgroup, then
-//     p = 2^(logit - max) written back over the logits, and their sum.
-//  3. P.V.  Same load pattern over V; each lane accumulates p * V for its
-//     8 dims and every head of the group in fp32 registers.
+//  1. logits.  8 lanes per token, each holding 16-byte pieces of the K row
+//     (buffer_load_dwordx4), take partial dot products with the matching q
+//     elements of every head of the group (v_dot2 on 16-bit pairs, fp32
+//     accumulate); a 3-step DPP sum finishes each dot product and the raw
+//     logits go to the wave's rows of LDS.
+//  2. softmax.  The wave scales them into the base-2 domain (scale * log2 e),
+//     takes its max per head, overwrites them with p = 2^(logit - max) and
+//     sums them.
+//  3. P.V.  D/8 lanes per token, each holding 8 consecutive dims of the V
+//     row, accumulate p * V for every head in fp32 registers.
 //
-// The single-pass kernel ("v1") loops over all chunks of the context with a
-// running max / sum / accumulator (rescaled by 2^(old max - new max)) and
-// writes the normalised output.  The split kernel ("v2") handles one
-// partition per workgroup and stores (max, sum, acc); the merge kernel
-// combines partitions with the log-sum-exp identity.
+// K and V stream through a ring of unit buffers per wave, every refill
+// issued on every path so that the wait counts track the ring.  At the end
+// the four waves' (max, sum, acc) meet in LDS and combine with the
+// log-sum-exp identity.  The single-pass kernel ("v1") keeps each wave's
+// running max / sum / accumulator across chunks (rescaled by
+// 2^(old max - new max)) and writes the normalised output; the split kernel
+// ("v2") stores (max, sum, acc) of its partition and the merge kernel
+// combines the partitions.
 //
-// Loads use a wave-uniform (SGPR) block base and a per-lane 32-bit offset;
-// block ids come from the table through scalar loads.  Tail tokens of the
-// last block are masked by select (the pools' unused slots may hold NaN).
+// Loads use a wave-uniform block base and per-lane 32-bit offsets.  A wave's
+// block ids arrive in one vector load (lane i: its unit i) and are read back
+// with readlane; tail tokens of the last block are masked by select (the
+// pools' unused slots may hold NaN).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -43,6 +47,16 @@ namespace pa {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
+// unit loads each wave keeps in flight (K, then V): the single-pass kernel
+// walks whole contexts with few workgroups per CU and wants a deeper ring
+#ifndef PA_DEPTH_SPLIT
+#define PA_DEPTH_SPLIT 3
+#endif
+#ifndef PA_DEPTH_SINGLE
+#define PA_DEPTH_SINGLE 4
+#endif
+constexpr int kDepthSplit = PA_DEPTH_SPLIT;
+constexpr int kDepthSingle = PA_DEPTH_SINGLE;
 
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef __bf16 bf162v __attribute__((ext_vector_type(2)));
@@ -111,6 +125,24 @@ __device__ inline float wave_max_from(float x, int first_stride) {
 __device__ inline float wave_sum_from(float x, int first_stride) {
   for (int off = first_stride; off < 64; off <<= 1) x += __shfl_xor(x, off);
   return x;
+}
+
+// Sum over the lanes l, l ^ S, l ^ 2S, ... up to 64 for S = 8 or 16: lane
+// xor 8 by a DPP rotate inside the 16-lane row, xor 16 and xor 32 by the
+// CDNA4 row swaps.  v_permlane16_swap(a, b) exchanges the odd rows of a with
+// the even rows of b, so with a = b = x the two results add up to
+// x[l] + x[l ^ 16] in every lane; v_permlane32_swap does the same with the
+// two 32-lane halves.
+template <int S>
+__device__ inline float rows_sum(float x) {
+  static_assert(S == 8 || S == 16, "row stride");
+  if constexpr (S == 8) x += dpp<0x128>(x);   // row_ror:8
+  const uint32_t b = __float_as_uint(x);
+  const auto r16 = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+  x = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+  const uint32_t c = __float_as_uint(x);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(c, c, false, false);
+  return __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
 }
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -217,233 +249,186 @@ __device__ inline void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Each wave runs its own softmax over its own units: logits, its running max
-// m, sum l and accumulator acc (in the base-2 domain), with no workgroup
-// barrier until the four waves' (m, l, acc) are combined at the end:
-//   M = max_w m_w,  acc = sum_w 2^(m_w - M) acc_w,  l = sum_w 2^(m_w - M) l_w.
-template <int DT, int D, int GT, bool SPLIT>
-__global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
+// Per-wave pieces shared by the single-pass and split kernels.  Everything
+// here is wave-uniform except what a lane holds of q, K, V, the block ids
+// and the accumulators.
+template <int DT, int D, int GT>
+struct WaveAttn {
   using F = Fmt<DT>;
   using TL = Tile<D, GT>;
-  constexpr int UNIT = TL::UNIT, KC = TL::KC, KGROUPS = TL::KGROUPS, KLOADS = TL::KLOADS;
-  constexpr int VL = TL::VL, VTOK = TL::VTOK, VLOADS = TL::VLOADS, GTP = TL::GTP;
-  extern __shared__ float lds[];
+  static constexpr int UNIT = TL::UNIT, KC = TL::KC, KGROUPS = TL::KGROUPS, KLOADS = TL::KLOADS;
+  static constexpr int VL = TL::VL, VTOK = TL::VTOK, VLOADS = TL::VLOADS, GTP = TL::GTP;
 
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63;
-  const int krow = lane >> 3, kcol = lane & 7;      // QK: token row, 16-byte column
-  const int vrow = lane / VL, vcol = lane % VL;     // PV: token row, 16-byte column
+  // Tokens [c0, c0 + n) of one sequence as one wave sees them: its units are
+  // u = wave, wave + 4, ... below ceil(n / UNIT), cnt of them.  Lane i of blk
+  // holds the physical block of the wave's unit i, fetched by one vector load
+  // and read back with readlane when the unit's loads are issued.
+  struct Span {
+    int c0, n, cnt;
+    int blk;
+  };
 
-  // Which (sequence, KV head x head chunk, partition) this workgroup serves.
-  //  single pass:  grid (KV heads x chunks, sequences)
-  //  split, list:  1-D grid over work items x (KV heads x chunks); the KV
-  //                heads of an item (one token row) land on one XCD, and
-  //                items come from the caller, one per live (sequence,
-  //                partition), so no workgroup is empty
-  //  split, dense: grid (partitions, KV heads x chunks, sequences), partitions
-  //                fastest and their count odd: workgroups go to the 8 XCDs
-  //                round-robin by linear id, and an odd stride rotates each
-  //                sequence's partition p across them (partition p exists only
-  //                for sequences longer than p * P, so a fixed mapping would
-  //                load the XCDs unevenly)
-  int seq, kvhc, part = 0;
-  if constexpr (!SPLIT) {
-    kvhc = blockIdx.x;
-    seq = blockIdx.y;
-  } else {
-    if (p.work_items) {
-      // linear id = (item / 8) * 8 * nkv + kvhc * 8 + item % 8: ids equal mod 8
-      // share an XCD, so the KV heads of one item (one token row) do
-      const int nkv = p.num_kv_heads * p.head_chunks;
-      const int grp = blockIdx.x / (8 * nkv);
-      const int r = blockIdx.x - grp * 8 * nkv;
-      kvhc = r >> 3;
-      const int item = grp * 8 + (r & 7);
-      if (item >= p.num_work_items) return;         // uniform: whole workgroup
-      seq = p.work_items[2 * item];
-      part = p.work_items[2 * item + 1];
-      if (static_cast<unsigned>(seq) >= static_cast<unsigned>(p.num_seqs) ||
-          static_cast<unsigned>(part) >= static_cast<unsigned>(p.num_parts))
-        return;                                     // uniform: whole workgroup
-    } else {
-      part = blockIdx.x;
-      kvhc = blockIdx.y;
-      seq = blockIdx.z;
-      if (part >= p.num_parts) return;
-    }
-  }
-  const int kvh = kvhc / p.head_chunks;
-  const int hc = kvhc - kvh * p.head_chunks;
-  const int head0 = kvh * p.group + hc * GT;
-  const int nact = min(GT, p.group - hc * GT);    // active heads of this chunk
+  int wave, lane, krow, kcol, vrow, vcol;
+  const char* kbase;
+  const char* vbase;
+  const uint16_t* q;
+  int64_t block_bytes;
+  uint32_t tok_bytes, koff, voff;
+  int bs_mask, log2_bs, num_blocks;
+  float scale_log2;
+  float* s_lds;   // [chunk][GTP]: logits, then probabilities; a unit's rows belong to its wave
 
-  int L = p.context_lens[seq];
-  L = max(0, min(L, p.mb * p.block_size));         // never past the table row
-  int t_begin = 0, t_end = L;
-  if constexpr (SPLIT) {
-    t_begin = part * p.chunk;
-    if (t_begin >= L) return;                       // uniform: whole workgroup
-    t_end = min(L, t_begin + p.chunk);
+  __device__ __forceinline__ WaveAttn(const AttnParams& p, int kvh, float* lds) {
+    const int tid = threadIdx.x;
+    wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    lane = tid & 63;
+    krow = lane >> 3;
+    kcol = lane & 7;
+    vrow = lane / VL;
+    vcol = lane % VL;
+    kbase = static_cast<const char*>(p.k_cache);
+    vbase = static_cast<const char*>(p.v_cache);
+    q = static_cast<const uint16_t*>(p.q);
+    block_bytes = p.block_stride * 2;
+    tok_bytes = static_cast<uint32_t>(p.num_kv_heads) * D * 2;
+    const uint32_t head_off = static_cast<uint32_t>(kvh) * D * 2;
+    koff = static_cast<uint32_t>(krow) * tok_bytes + head_off + kcol * 16;
+    voff = static_cast<uint32_t>(vrow) * tok_bytes + head_off + vcol * 16;
+    bs_mask = p.block_size - 1;
+    log2_bs = p.log2_block_size;
+    num_blocks = p.num_blocks;
+    scale_log2 = p.scale_log2;
+    s_lds = lds;
   }
 
-  const int64_t out_row0 = static_cast<int64_t>(seq) * p.num_q_heads + head0;
-  if constexpr (!SPLIT) {
-    if (L == 0) {
-      uint16_t* out = static_cast<uint16_t*>(p.out);
-      for (int hh = 0; hh < nact; ++hh)
-        for (int d = tid; d < D; d += kThreads) out[(out_row0 + hh) * D + d] = 0;
-      return;
-    }
+  // bt is the sequence's table row and c0 + n must not pass the tokens it
+  // maps; n <= 0 gives an empty span that reads nothing.
+  __device__ __forceinline__ Span span(const int32_t* bt, int c0, int n) const {
+    Span s;
+    s.c0 = c0;
+    s.n = n;
+    const int nunits = n > 0 ? (n + UNIT - 1) / UNIT : 0;
+    s.cnt = nunits > wave ? (nunits - wave + kWaves - 1) / kWaves : 0;
+    s.blk = 0;
+    if (lane < s.cnt) s.blk = bt[(c0 + (wave + kWaves * lane) * UNIT) >> log2_bs];
+    return s;
   }
 
-  const int32_t* bt = p.block_tables + static_cast<int64_t>(seq) * p.mb;
-  const char* kbase = static_cast<const char*>(p.k_cache);
-  const char* vbase = static_cast<const char*>(p.v_cache);
-  const int64_t block_bytes = p.block_stride * 2;
-  const uint32_t tok_bytes = static_cast<uint32_t>(p.num_kv_heads) * D * 2;
-  const uint32_t head_off = static_cast<uint32_t>(kvh) * D * 2;
-  const uint32_t koff = static_cast<uint32_t>(krow) * tok_bytes + head_off + kcol * 16;
-  const uint32_t voff = static_cast<uint32_t>(vrow) * tok_bytes + head_off + vcol * 16;
-  const int bs_mask = p.block_size - 1;
-
-  float* s_lds = lds;                                       // [chunk][GTP]
-  float* red = lds + static_cast<size_t>(p.chunk) * GTP;    // [kWaves][GT][D]
-  float* wmax = red + kWaves * GT * D;                      // [kWaves][GTP]
-  float* wsum = wmax + kWaves * GTP;                        // [kWaves][GTP]
-
-  float acc[GT][8];
-  float m_run[GT], l_run[GT];                       // wave-uniform
-#pragma unroll
-  for (int hh = 0; hh < GT; ++hh) {
-    m_run[hh] = -__builtin_inff();
-    l_run[hh] = 0.f;
-    if constexpr (!SPLIT) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[hh][e] = 0.f;
-    }
+  // Byte offset from a pool's start of the wave's unit i, clamped to its last
+  // unit; block 0 when the wave has no unit or the entry is out of range.
+  __device__ __forceinline__ int64_t unit_off(const Span& s, int i) const {
+    const int j = max(0, min(i, s.cnt - 1));
+    int blk = __builtin_amdgcn_readlane(s.blk, j);
+    blk = static_cast<unsigned>(blk) < static_cast<unsigned>(num_blocks) ? blk : 0;
+    const int t0 = s.c0 + (wave + kWaves * j) * UNIT;
+    return blk * block_bytes + static_cast<int64_t>(t0 & bs_mask) * tok_bytes;
   }
 
-  // One chunk of n tokens from c0 for this wave's units (u = wave, wave + 4,
-  // ...): logits, its own softmax statistics, P.V.  The split kernel runs it
-  // once (q is dead after the logits and acc is born at the softmax, so the
-  // two never share registers); the single-pass kernel loops.
-  auto run_chunk = [&](const int c0, const int n) {
-    const int nunits = (n + UNIT - 1) / UNIT;
-    const int cnt = nunits > wave ? (nunits - wave + kWaves - 1) / kWaves : 0;
-    if (cnt == 0) {                                 // uniform: this wave has no tokens
-      if constexpr (SPLIT) {
+  // Loads of unit i >= cnt go through an empty descriptor and fetch nothing.
+  __device__ __forceinline__ void load_k(uint4 (&dst)[KLOADS], const Span& s, int i) const {
+    const auto r = block_rsrc(kbase + unit_off(s, i), i < s.cnt);
 #pragma unroll
-        for (int hh = 0; hh < GT; ++hh)
+    for (int j = 0; j < KGROUPS; ++j)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) acc[hh][e] = 0.f;
+      for (int c = 0; c < KC; ++c) dst[j * KC + c] = load16(r, koff + c * 128, j * 8 * tok_bytes);
+  }
+  __device__ __forceinline__ void load_v(uint4 (&dst)[VLOADS], const Span& s, int i) const {
+    const auto r = block_rsrc(vbase + unit_off(s, i), i < s.cnt);
+#pragma unroll
+    for (int j = 0; j < VLOADS; ++j) dst[j] = load16(r, voff, j * VTOK * tok_bytes);
+  }
+
+  // q slices for the QK layout: chunk c of head hh = dims c*64 + kcol*8 .. +8
+  __device__ __forceinline__ void load_q(uint4 (&qv)[GT][KC], int64_t row0, int nact) const {
+#pragma unroll
+    for (int hh = 0; hh < GT; ++hh)
+#pragma unroll
+      for (int c = 0; c < KC; ++c)
+        qv[hh][c] = hh < nact
+                        ? *reinterpret_cast<const uint4*>(q + (row0 + hh) * D + c * 64 + kcol * 8)
+                        : make_uint4(0, 0, 0, 0);
+  }
+
+  // Logits of the wave's unit i (raw q.k; scaled in the softmax), written by
+  // the lane holding column 0 of each token.
+  __device__ __forceinline__ void qk_unit(const uint4 (&qv)[GT][KC], const uint4 (&kx)[KLOADS],
+                                          int i) const {
+    const int u = wave + kWaves * i;
+#pragma unroll
+    for (int j = 0; j < KGROUPS; ++j) {
+      float sv[GTP];
+#pragma unroll
+      for (int hh = 0; hh < GT; ++hh) {
+        float a = 0.f;
+#pragma unroll
+        for (int c = 0; c < KC; ++c) {
+          const uint4 k = kx[j * KC + c];
+          a = F::dot2(qv[hh][c].x, k.x, a);
+          a = F::dot2(qv[hh][c].y, k.y, a);
+          a = F::dot2(qv[hh][c].z, k.z, a);
+          a = F::dot2(qv[hh][c].w, k.w, a);
+        }
+        sv[hh] = group_sum<8>(a);
       }
-      return;
+#pragma unroll
+      for (int hh = GT; hh < GTP; ++hh) sv[hh] = 0.f;
+      if (kcol == 0) lds_store(s_lds + (u * UNIT + j * 8 + krow) * GTP, sv);
     }
+  }
 
-    // base of the i-th unit of this wave (clamped to its last unit; loads for
-    // i >= cnt go through an empty descriptor and fetch nothing)
-    auto unit_base = [&](const char* pool, int i) -> const char* {
-      const int u = wave + kWaves * min(i, cnt - 1);
-      const int t0 = c0 + u * UNIT;
-      int blk = __builtin_amdgcn_readfirstlane(bt[t0 >> p.log2_block_size]);
-      blk = (static_cast<unsigned>(blk) < static_cast<unsigned>(p.num_blocks)) ? blk : 0;
-      return pool + blk * block_bytes + static_cast<int64_t>(t0 & bs_mask) * tok_bytes;
-    };
-    auto load_k = [&](uint4 (&dst)[KLOADS], int i) {
-      const auto r = block_rsrc(unit_base(kbase, i), i < cnt);
+  // P.V of the wave's unit i; tokens past n get V = 0 (their p is 0 and their
+  // slots may hold NaN).
+  __device__ __forceinline__ void pv_unit(float (&acc)[GT][8], const uint4 (&vx)[VLOADS],
+                                          const Span& s, int i) const {
+    const int u = wave + kWaves * i;
+    const bool tail = (u + 1) * UNIT > s.n;
 #pragma unroll
-      for (int j = 0; j < KGROUPS; ++j)
-#pragma unroll
-        for (int c = 0; c < KC; ++c)
-          dst[j * KC + c] = load16(r, koff + c * 128, j * 8 * tok_bytes);
-    };
-    auto load_v = [&](uint4 (&dst)[VLOADS], int i) {
-      const auto r = block_rsrc(unit_base(vbase, i), i < cnt);
-#pragma unroll
-      for (int j = 0; j < VLOADS; ++j) dst[j] = load16(r, voff, j * VTOK * tok_bytes);
-    };
-
-    // q slices for the QK layout: chunk c of head hh = dims c*64 + kcol*8 .. +8
-    uint4 qv[GT][KC];
-    {
-      const uint16_t* q = static_cast<const uint16_t*>(p.q);
+    for (int j = 0; j < VLOADS; ++j) {
+      const int t = u * UNIT + j * VTOK + vrow;
+      uint4 x = vx[j];
+      if (tail && t >= s.n) x = make_uint4(0, 0, 0, 0);
+      float pr[GTP];
+      lds_load(pr, s_lds + t * GTP);
+      float vf[8];
+      vf[0] = F::lo(x.x); vf[1] = F::hi(x.x);
+      vf[2] = F::lo(x.y); vf[3] = F::hi(x.y);
+      vf[4] = F::lo(x.z); vf[5] = F::hi(x.z);
+      vf[6] = F::lo(x.w); vf[7] = F::hi(x.w);
 #pragma unroll
       for (int hh = 0; hh < GT; ++hh)
 #pragma unroll
-        for (int c = 0; c < KC; ++c)
-          qv[hh][c] = hh < nact
-                          ? *reinterpret_cast<const uint4*>(q + (out_row0 + hh) * D + c * 64 + kcol * 8)
-                          : make_uint4(0, 0, 0, 0);
+        for (int e = 0; e < 8; ++e) acc[hh][e] = fmaf(pr[hh], vf[e], acc[hh][e]);
+      // keep each group's probabilities and widened V short-lived
+      __builtin_amdgcn_sched_barrier(0);
     }
-    // logits of one unit (raw q.k; scaled in the softmax step), written by
-    // the lane holding column 0 of each token
-    auto qk_unit = [&](const uint4 (&kx)[KLOADS], int i) {
-      const int u = wave + kWaves * i;
-#pragma unroll
-      for (int j = 0; j < KGROUPS; ++j) {
-        float sv[GTP];
-#pragma unroll
-        for (int hh = 0; hh < GT; ++hh) {
-          float a = 0.f;
-#pragma unroll
-          for (int c = 0; c < KC; ++c) {
-            const uint4 k = kx[j * KC + c];
-            a = F::dot2(qv[hh][c].x, k.x, a);
-            a = F::dot2(qv[hh][c].y, k.y, a);
-            a = F::dot2(qv[hh][c].z, k.z, a);
-            a = F::dot2(qv[hh][c].w, k.w, a);
-          }
-          sv[hh] = group_sum<8>(a);
-        }
-#pragma unroll
-        for (int hh = GT; hh < GTP; ++hh) sv[hh] = 0.f;
-        if (kcol == 0) lds_store(s_lds + (u * UNIT + j * 8 + krow) * GTP, sv);
-      }
-    };
-    // P.V of one unit; tokens past the chunk end get V = 0 (their p is 0 and
-    // their slots may hold NaN)
-    auto pv_unit = [&](const uint4 (&vx)[VLOADS], int i) {
-      const int u = wave + kWaves * i;
-      const bool tail = (u + 1) * UNIT > n;
-#pragma unroll
-      for (int j = 0; j < VLOADS; ++j) {
-        const int t = u * UNIT + j * VTOK + vrow;
-        uint4 x = vx[j];
-        if (tail && t >= n) x = make_uint4(0, 0, 0, 0);
-        float pr[GTP];
-        lds_load(pr, s_lds + t * GTP);
-        float vf[8];
-        vf[0] = F::lo(x.x); vf[1] = F::hi(x.x);
-        vf[2] = F::lo(x.y); vf[3] = F::hi(x.y);
-        vf[4] = F::lo(x.z); vf[5] = F::hi(x.z);
-        vf[6] = F::lo(x.w); vf[7] = F::hi(x.w);
-#pragma unroll
-        for (int hh = 0; hh < GT; ++hh)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) acc[hh][e] = fmaf(pr[hh], vf[e], acc[hh][e]);
-        // keep each group's probabilities and widened V short-lived
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    };
+  }
 
-    // ---- logits of the wave's units, double-buffered ----
-    uint4 va[VLOADS];
-    {
-      uint4 ka[KLOADS], kb[KLOADS];
-      load_k(ka, 0);
-      for (int i = 0; i < cnt; i += 2) {
-        load_k(kb, i + 1);
-        qk_unit(ka, i);
-        load_k(ka, i + 2);
-        if (i + 1 < cnt) qk_unit(kb, i + 1);
+  // Logits of all the wave's units through a ring of DEPTH unit buffers:
+  // units 0 .. DEPTH-1 are already on their way, and the buffer unit i was
+  // consumed from refills with unit i + DEPTH.  Every refill is issued, past
+  // the wave's last unit through the empty descriptor: with the loads on
+  // every path the compiler's wait counts see the ring in issue order and
+  // wait for one unit at a time (a skipped refill would make it wait for all).
+  template <int DEPTH>
+  __device__ __forceinline__ void logits(const uint4 (&qv)[GT][KC], uint4 (&kb)[DEPTH][KLOADS],
+                                         const Span& s) const {
+    for (int i = 0; i < s.cnt; i += DEPTH) {
+#pragma unroll
+      for (int b = 0; b < DEPTH; ++b) {
+        if (b == 0 || i + b < s.cnt) qk_unit(qv, kb[b], i + b);   // uniform
+        load_k(kb[b], s, i + b + DEPTH);
       }
     }
-    load_v(va, 0);                         // the first V unit streams in during the softmax
-    wave_lds_sync();
+  }
 
-    // ---- the wave's softmax over its tokens (lane l: wave tokens l, l+64, ...) ----
-    const int wtok = cnt * UNIT;
+  // The wave's softmax over its tokens of the span (lane l takes the wave's
+  // tokens l, l + 64, ...): scales the logits into the base-2 domain, folds
+  // their max into m_run, overwrites them with p = 2^(logit - m_run), and
+  // sets l_run = alpha * l_run + sum p with alpha = 2^(old m_run - new m_run),
+  // which it returns for the caller's accumulator.
+  __device__ __forceinline__ void softmax(const Span& s, float (&m_run)[GT], float (&l_run)[GT],
+                                          float (&alpha)[GT]) const {
+    const int wtok = s.cnt * UNIT;
     auto tok_of = [&](int r) { return (wave + kWaves * (r / UNIT)) * UNIT + (r % UNIT); };
     float mloc[GT];
 #pragma unroll
@@ -454,16 +439,16 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
       lds_load(v, s_lds + t * GTP);
 #pragma unroll
       for (int hh = 0; hh < GT; ++hh) {
-        v[hh] *= p.scale_log2;
-        if (t < n) mloc[hh] = v[hh] > mloc[hh] ? v[hh] : mloc[hh];
+        v[hh] *= scale_log2;
+        if (t < s.n) mloc[hh] = v[hh] > mloc[hh] ? v[hh] : mloc[hh];
       }
       lds_store(s_lds + t * GTP, v);
     }
-    float m_new[GT], alpha[GT];
+    float m_new[GT];
 #pragma unroll
     for (int hh = 0; hh < GT; ++hh) {
       m_new[hh] = fmaxf(m_run[hh], wave_max_all(mloc[hh]));
-      alpha[hh] = fast_exp2(m_run[hh] - m_new[hh]);   // 0 on the first chunk
+      alpha[hh] = fast_exp2(m_run[hh] - m_new[hh]);   // 0 while m_run is -inf
       m_run[hh] = m_new[hh];
     }
     float lsum[GT];
@@ -475,63 +460,75 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
       lds_load(v, s_lds + t * GTP);
 #pragma unroll
       for (int hh = 0; hh < GT; ++hh) {
-        const float pr = t < n ? fast_exp2(v[hh] - m_new[hh]) : 0.f;
+        const float pr = t < s.n ? fast_exp2(v[hh] - m_new[hh]) : 0.f;
         v[hh] = pr;
         lsum[hh] += pr;
       }
       lds_store(s_lds + t * GTP, v);
     }
 #pragma unroll
-    for (int hh = 0; hh < GT; ++hh) {
-      l_run[hh] = l_run[hh] * alpha[hh] + wave_sum_all(lsum[hh]);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[hh][e] = SPLIT ? 0.f : acc[hh][e] * alpha[hh];
-    }
-    wave_lds_sync();
-
-    // ---- P . V of the wave's units, double-buffered ----
-    {
-      uint4 vb[VLOADS];
-      for (int i = 0; i < cnt; i += 2) {
-        load_v(vb, i + 1);
-        pv_unit(va, i);
-        load_v(va, i + 2);
-        if (i + 1 < cnt) pv_unit(vb, i + 1);
-      }
-    }
-    wave_lds_sync();                       // the next chunk rewrites this wave's rows
-  };
-
-  if constexpr (SPLIT) {
-    run_chunk(t_begin, t_end - t_begin);
-  } else {
-    for (int c0 = t_begin; c0 < t_end; c0 += p.chunk) run_chunk(c0, min(p.chunk, t_end - c0));
+    for (int hh = 0; hh < GT; ++hh) l_run[hh] = l_run[hh] * alpha[hh] + wave_sum_all(lsum[hh]);
   }
 
-  // ---------------- combine the waves ----------------
+  // P.V over all the wave's units through a ring of DEPTH unit buffers, as
+  // the logits.
+  template <int DEPTH>
+  __device__ __forceinline__ void values(float (&acc)[GT][8], uint4 (&vb)[DEPTH][VLOADS],
+                                         const Span& s) const {
+    for (int i = 0; i < s.cnt; i += DEPTH) {
 #pragma unroll
-  for (int hh = 0; hh < GT; ++hh)
+      for (int b = 0; b < DEPTH; ++b) {
+        if (b == 0 || i + b < s.cnt) pv_unit(acc, vb[b], s, i + b);   // uniform
+        load_v(vb[b], s, i + b + DEPTH);
+      }
+    }
+  }
+};
+
+// The workgroup's result for query heads row0 .. row0 + nact - 1 of one
+// sequence: the waves' (m_w, l_w, acc_w) meet in `red` and combine as
+//   M = max_w m_w,  acc = sum_w 2^(m_w - M) acc_w,  l = sum_w 2^(m_w - M) l_w
+// (a wave without tokens has m_w = -inf and weight 0).  Split: (acc, M, l)
+// go to the partition's workspace slot; single pass: out = acc / l.
+template <int DT, int D, int GT, bool SPLIT>
+__device__ __forceinline__ void combine_waves(const AttnParams& p, float (&acc)[GT][8],
+                                              const float (&m_w)[GT], const float (&l_w)[GT],
+                                              float* red, int64_t row0, int nact, int part) {
+  using TL = Tile<D, GT>;
+  constexpr int VL = TL::VL, GTP = TL::GTP;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int vrow = lane / VL, vcol = lane % VL;
+  float* wmax = red + kWaves * GT * D;   // [kWaves][GTP]
+  float* wsum = wmax + kWaves * GTP;     // [kWaves][GTP]
+  // one head at a time: the scheduler would otherwise copy all GT * 8 values
+  // before the first swap and hold twice the accumulators
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[hh][e] = wave_sum_from(acc[hh][e], VL);
-  if (vrow == 0) {
+  for (int hh = 0; hh < GT; ++hh) {
 #pragma unroll
-    for (int hh = 0; hh < GT; ++hh) {
+    for (int e = 0; e < 8; ++e) acc[hh][e] = rows_sum<VL>(acc[hh][e]);
+    if (vrow == 0) {
       float* dst = red + (wave * GT + hh) * D + vcol * 8;
       *reinterpret_cast<float4*>(dst) = make_float4(acc[hh][0], acc[hh][1], acc[hh][2], acc[hh][3]);
       *reinterpret_cast<float4*>(dst + 4) = make_float4(acc[hh][4], acc[hh][5], acc[hh][6], acc[hh][7]);
     }
+    __builtin_amdgcn_sched_barrier(0);
   }
   if (lane == 0) {
 #pragma unroll
     for (int hh = 0; hh < GT; ++hh) {
-      wmax[wave * GTP + hh] = m_run[hh];
-      wsum[wave * GTP + hh] = l_run[hh];
+      wmax[wave * GTP + hh] = m_w[hh];
+      wsum[wave * GTP + hh] = l_w[hh];
     }
   }
   __syncthreads();
 
-#pragma unroll
-  for (int hh = 0; hh < GT; ++hh) {
+  // one float4 of one head per thread: GT * D / 4 <= 256 items, one pass
+  constexpr int C4 = D / 4;
+  for (int idx = tid; idx < GT * C4; idx += kThreads) {
+    const int hh = idx / C4;
+    const int c = idx - hh * C4;
     if (hh >= nact) break;
     float mw[kWaves], M = -__builtin_inff();
 #pragma unroll
@@ -539,43 +536,203 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
       mw[w] = wmax[w * GTP + hh];
       M = fmaxf(M, mw[w]);
     }
-    float wt[kWaves], lt = 0.f;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    float lt = 0.f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      wt[w] = fast_exp2(mw[w] - M);                 // 0 for a wave without tokens
-      lt += wt[w] * wsum[w * GTP + hh];
+      const float wt = fast_exp2(mw[w] - M);
+      lt += wt * wsum[w * GTP + hh];
+      const float4 r = *reinterpret_cast<const float4*>(red + (w * GT + hh) * D + c * 4);
+      v.x = fmaf(wt, r.x, v.x);
+      v.y = fmaf(wt, r.y, v.y);
+      v.z = fmaf(wt, r.z, v.z);
+      v.w = fmaf(wt, r.w, v.w);
     }
-    for (int d = tid; d < D; d += kThreads) {
-      float v = 0.f;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) v += wt[w] * red[(w * GT + hh) * D + d];
-      if constexpr (SPLIT) {
-        const int64_t slot = (out_row0 + hh) * p.num_parts + part;
-        p.part_acc[slot * D + d] = v;
-        if (d == 0) {
-          p.part_max[slot] = M;
-          p.part_sum[slot] = lt;
-        }
-      } else {
-        static_cast<uint16_t*>(p.out)[(out_row0 + hh) * D + d] = F::narrow(v / lt);
+    if constexpr (SPLIT) {
+      const int64_t slot = (row0 + hh) * p.num_parts + part;
+      *reinterpret_cast<float4*>(p.part_acc + slot * D + c * 4) = v;
+      if (c == 0) {
+        p.part_max[slot] = M;
+        p.part_sum[slot] = lt;
       }
+    } else {
+      using F = Fmt<DT>;
+      const uint32_t lo = F::narrow(v.x / lt) | (static_cast<uint32_t>(F::narrow(v.y / lt)) << 16);
+      const uint32_t hi = F::narrow(v.z / lt) | (static_cast<uint32_t>(F::narrow(v.w / lt)) << 16);
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + (row0 + hh) * D + c * 4) =
+          make_uint2(lo, hi);
     }
   }
 }
 
+// Single-pass decode ("v1"): workgroup = (KV head x head chunk, sequence); it
+// walks the whole context in chunks of p.chunk tokens, each wave keeping its
+// own running max / sum / accumulator across chunks (rescaled by alpha),
+// and writes the normalised output.
+template <int DT, int D, int GT>
+__global__ __launch_bounds__(kThreads) void single_kernel(AttnParams p) {
+  using W = WaveAttn<DT, D, GT>;
+  extern __shared__ float lds[];
+  const int kvhc = blockIdx.x;
+  const int seq = blockIdx.y;
+  const int kvh = kvhc / p.head_chunks;
+  const int hc = kvhc - kvh * p.head_chunks;
+  const int head0 = kvh * p.group + hc * GT;
+  const int nact = min(GT, p.group - hc * GT);   // active heads of this chunk
+  const int64_t row0 = static_cast<int64_t>(seq) * p.num_q_heads + head0;
+
+  int L = p.context_lens[seq];
+  L = max(0, min(L, p.mb * p.block_size));         // never past the table row
+  if (L == 0) {                                    // uniform: whole workgroup
+    uint16_t* out = static_cast<uint16_t*>(p.out);
+    for (int hh = 0; hh < nact; ++hh)
+      for (int d = threadIdx.x; d < D; d += kThreads) out[(row0 + hh) * D + d] = 0;
+    return;
+  }
+
+  const W w(p, kvh, lds);
+  const int32_t* bt = p.block_tables + static_cast<int64_t>(seq) * p.mb;
+  float acc[GT][8], m_run[GT], l_run[GT];
+#pragma unroll
+  for (int hh = 0; hh < GT; ++hh) {
+    m_run[hh] = -__builtin_inff();
+    l_run[hh] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[hh][e] = 0.f;
+  }
+  for (int c0 = 0; c0 < L; c0 += p.chunk) {
+    const typename W::Span s = w.span(bt, c0, min(p.chunk, L - c0));
+    if (s.cnt == 0) continue;                      // uniform: this wave has no tokens
+    {
+      uint4 kb[kDepthSingle][W::KLOADS];
+#pragma unroll
+      for (int b = 0; b < kDepthSingle; ++b) w.load_k(kb[b], s, b);
+      uint4 qv[GT][W::KC];
+      w.load_q(qv, row0, nact);
+      w.template logits<kDepthSingle>(qv, kb, s);
+    }
+    uint4 vb[kDepthSingle][W::VLOADS];             // streams in during the softmax
+#pragma unroll
+    for (int b = 0; b < kDepthSingle; ++b) w.load_v(vb[b], s, b);
+    wave_lds_sync();
+    float alpha[GT];
+    w.softmax(s, m_run, l_run, alpha);
+#pragma unroll
+    for (int hh = 0; hh < GT; ++hh)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[hh][e] *= alpha[hh];
+    wave_lds_sync();
+    w.template values<kDepthSingle>(acc, vb, s);
+    wave_lds_sync();                               // the next chunk rewrites this wave's rows
+  }
+  combine_waves<DT, D, GT, false>(p, acc, m_run, l_run, lds + static_cast<size_t>(p.chunk) * W::GTP,
+                                  row0, nact, 0);
+}
+
+// Split-context partitions ("v2"): one (sequence, partition) work item for
+// one KV head x head chunk per workgroup; each wave runs its own softmax over
+// its units of the partition and the waves combine into the partition's
+// (max, sum, acc) workspace slot.
+//  list:  1-D grid over work items x (KV heads x chunks).  Linear id =
+//         (item / 8) * 8 * nkv + kvhc * 8 + item % 8: ids equal mod 8 share
+//         an XCD, so the KV heads of one item (the same token rows) do.
+//  dense: grid (partitions, KV heads x chunks, sequences), partitions fastest
+//         and their count odd: workgroups go to the 8 XCDs round-robin by
+//         linear id, and an odd stride rotates each sequence's partition p
+//         across them (partition p exists only for sequences longer than
+//         p * P, so a fixed mapping would load the XCDs unevenly).
+template <int DT, int D, int GT>
+__global__ __launch_bounds__(kThreads) void split_kernel(AttnParams p) {
+  using W = WaveAttn<DT, D, GT>;
+  extern __shared__ float lds[];
+  int seq, kvhc, part;
+  if (p.work_items) {
+    const int nkv = p.num_kv_heads * p.head_chunks;
+    const int grp = blockIdx.x / (8 * nkv);
+    const int r = blockIdx.x - grp * 8 * nkv;
+    kvhc = r >> 3;
+    const int item = grp * 8 + (r & 7);
+    if (item >= p.num_work_items) return;          // uniform: whole workgroup
+    seq = __builtin_amdgcn_readfirstlane(p.work_items[2 * item]);
+    part = __builtin_amdgcn_readfirstlane(p.work_items[2 * item + 1]);
+  } else {
+    part = blockIdx.x;
+    kvhc = blockIdx.y;
+    seq = blockIdx.z;
+  }
+  if (static_cast<unsigned>(seq) >= static_cast<unsigned>(p.num_seqs) ||
+      static_cast<unsigned>(part) >= static_cast<unsigned>(p.num_parts))
+    return;                                        // uniform: whole workgroup
+  int L = __builtin_amdgcn_readfirstlane(p.context_lens[seq]);
+  L = max(0, min(L, p.mb * p.block_size));         // never past the table row
+  const int c0 = part * p.chunk;
+  if (c0 >= L) return;                             // uniform: whole workgroup
+
+  const int kvh = kvhc / p.head_chunks;
+  const int hc = kvhc - kvh * p.head_chunks;
+  const int head0 = kvh * p.group + hc * GT;
+  const int nact = min(GT, p.group - hc * GT);     // active heads of this chunk
+  const int64_t row0 = static_cast<int64_t>(seq) * p.num_q_heads + head0;
+  const W w(p, kvh, lds);
+  const typename W::Span s =
+      w.span(p.block_tables + static_cast<int64_t>(seq) * p.mb, c0, min(p.chunk, L - c0));
+
+  float acc[GT][8], m_w[GT], l_w[GT];
+#pragma unroll
+  for (int hh = 0; hh < GT; ++hh) {
+    m_w[hh] = -__builtin_inff();
+    l_w[hh] = 0.f;
+  }
+  if (s.cnt > 0) {                                 // uniform: this wave has tokens
+    {
+      uint4 kb[kDepthSplit][W::KLOADS];
+#pragma unroll
+      for (int b = 0; b < kDepthSplit; ++b) w.load_k(kb[b], s, b);
+      uint4 qv[GT][W::KC];
+      w.load_q(qv, row0, nact);
+      w.template logits<kDepthSplit>(qv, kb, s);
+    }
+    uint4 vb[kDepthSplit][W::VLOADS];              // streams in during the softmax
+#pragma unroll
+    for (int b = 0; b < kDepthSplit; ++b) w.load_v(vb[b], s, b);
+    wave_lds_sync();
+    float alpha[GT];
+    w.softmax(s, m_w, l_w, alpha);
+    // acc is born here, after q is dead: the two never share registers
+#pragma unroll
+    for (int hh = 0; hh < GT; ++hh)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[hh][e] = 0.f;
+    wave_lds_sync();
+    w.template values<kDepthSplit>(acc, vb, s);
+  } else {
+#pragma unroll
+    for (int hh = 0; hh < GT; ++hh)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[hh][e] = 0.f;
+  }
+  combine_waves<DT, D, GT, true>(p, acc, m_w, l_w, lds + static_cast<size_t>(p.chunk) * W::GTP,
+                                 row0, nact, part);
+}
+
 // Merge of the partitions of one (sequence, q head) per workgroup:
 //   M = max_p m_p,  w_p = 2^(m_p - M),  out = sum_p w_p acc_p / sum_p w_p l_p
-// Wave w takes partitions w, w+4, ...: the partition index is wave-uniform, so
-// m_p and l_p arrive through scalar loads and each lane streams its E dims of
-// acc_p, several partitions in flight at once.  The waves' sums meet in LDS.
+// Partials arrive in batches of 64: thread t reads float4 column t % C4 of
+// partials t / C4, t / C4 + ROWS, ...  The first batch is requested together
+// with the maxima, before M is known, so a context of up to 64 partitions
+// costs one round trip to memory after its length; the batch's weights go
+// through LDS.
 template <int DT, int D>
 __global__ __launch_bounds__(kThreads) void merge_kernel(AttnParams p) {
   using F = Fmt<DT>;
-  constexpr int E = D / 64;   // dims per lane
-  constexpr int UNROLL = 4;
-  __shared__ float red_acc[kWaves][D];
-  __shared__ float red_l[kWaves];
-  __shared__ float red_m[kWaves];
+  constexpr int C4 = D / 4;                 // float4 columns of one partial
+  constexpr int ROWS = kThreads / C4;       // partials per load round
+  constexpr int BATCH = 64;
+  constexpr int R = BATCH / ROWS;           // load rounds per batch
+  __shared__ float s_w[BATCH];
+  __shared__ float s_m[kWaves];
+  __shared__ float s_l;
+  __shared__ float4 s_acc[kWaves][C4];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -592,64 +749,100 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(AttnParams p) {
   const int64_t base = static_cast<int64_t>(pair) * p.num_parts;
   const float* pm = p.part_max + base;
   const float* ps = p.part_sum + base;
-  const float* pa = p.part_acc + base * D + lane * E;
+  const float4* pa = reinterpret_cast<const float4*>(p.part_acc + base * D);
+  const int col = tid % C4, row = tid / C4;
 
-  float m = -__builtin_inff();
-  for (int k = tid; k < np; k += kThreads) m = fmaxf(m, pm[k]);
-  m = wave_max_from(m, 1);
-  if (lane == 0) red_m[wave] = m;
-  __syncthreads();
-  m = fmaxf(fmaxf(red_m[0], red_m[1]), fmaxf(red_m[2], red_m[3]));
-
-  float l = 0.f;
-  float acc[E];
+  float4 x[R];
+  auto load_batch = [&](int k0) {
 #pragma unroll
-  for (int e = 0; e < E; ++e) acc[e] = 0.f;
-  for (int k0 = wave; k0 < np; k0 += kWaves * UNROLL) {
-    float x[UNROLL][E];
-    float wk[UNROLL];
-#pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-      const int k = min(k0 + u * kWaves, np - 1);  // clamped: loads stay in range
-      wk[u] = (k0 + u * kWaves < np) ? fast_exp2(pm[k] - m) : 0.f;
-      const float* src = pa + static_cast<int64_t>(k) * D;
-      if constexpr (E == 2) {
-        const float2 v = *reinterpret_cast<const float2*>(src);
-        x[u][0] = v.x; x[u][1] = v.y;
-      } else {
-        x[u][0] = src[0];
-      }
-      l += wk[u] * ps[k];
+    for (int r = 0; r < R; ++r) {
+      const int k = k0 + row + r * ROWS;
+      x[r] = k < np ? pa[static_cast<int64_t>(k) * C4 + col] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-#pragma unroll
-    for (int u = 0; u < UNROLL; ++u)
-#pragma unroll
-      for (int e = 0; e < E; ++e) acc[e] = fmaf(wk[u], x[u][e], acc[e]);
-  }
-#pragma unroll
-  for (int e = 0; e < E; ++e) red_acc[wave][lane * E + e] = acc[e];
-  if (lane == 0) red_l[wave] = l;
+  };
+  load_batch(0);
+  // maxima: thread t < 64 keeps m_t and l_t of the first batch
+  const float m0 = tid < np ? pm[tid] : -__builtin_inff();
+  const float l0 = tid < np ? ps[tid] : 0.f;
+  float m = m0;
+  for (int k = tid + kThreads; k < np; k += kThreads) m = fmaxf(m, pm[k]);
+  m = wave_max_all(m);
+  if (lane == 0) s_m[wave] = m;
   __syncthreads();
-  const float lt = red_l[0] + red_l[1] + red_l[2] + red_l[3];
-  for (int d = tid; d < D; d += kThreads) {
-    const float v = red_acc[0][d] + red_acc[1][d] + red_acc[2][d] + red_acc[3][d];
-    out[d] = F::narrow(v / lt);
+  const float M = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
+
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float l = 0.f;                                   // wave 0 only
+  for (int k0 = 0; k0 < np; k0 += BATCH) {
+    if (tid < BATCH) {
+      const int k = k0 + tid;
+      float wk = 0.f;
+      if (k < np) {
+        const float mk = k0 == 0 ? m0 : pm[k];
+        const float lk = k0 == 0 ? l0 : ps[k];
+        wk = fast_exp2(mk - M);
+        l += wk * lk;
+      }
+      s_w[tid] = wk;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const float wk = s_w[row + r * ROWS];
+      acc.x = fmaf(wk, x[r].x, acc.x);
+      acc.y = fmaf(wk, x[r].y, acc.y);
+      acc.z = fmaf(wk, x[r].z, acc.z);
+      acc.w = fmaf(wk, x[r].w, acc.w);
+    }
+    if (k0 + BATCH < np) {                         // uniform
+      __syncthreads();                             // s_w is rewritten for the next batch
+      load_batch(k0 + BATCH);
+    }
+  }
+  // rows of one column inside a wave, then across the waves
+#pragma unroll
+  for (int off = C4; off < 64; off <<= 1) {
+    acc.x += __shfl_xor(acc.x, off);
+    acc.y += __shfl_xor(acc.y, off);
+    acc.z += __shfl_xor(acc.z, off);
+    acc.w += __shfl_xor(acc.w, off);
+  }
+  if (lane < C4) s_acc[wave][lane] = acc;
+  if (wave == 0) {
+    l = wave_sum_all(l);
+    if (lane == 0) s_l = l;
+  }
+  __syncthreads();
+  if (tid < C4) {
+    float4 v = s_acc[0][tid];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) {
+      v.x += s_acc[w][tid].x;
+      v.y += s_acc[w][tid].y;
+      v.z += s_acc[w][tid].z;
+      v.w += s_acc[w][tid].w;
+    }
+    const float lt = s_l;
+    const uint32_t lo = F::narrow(v.x / lt) | (static_cast<uint32_t>(F::narrow(v.y / lt)) << 16);
+    const uint32_t hi = F::narrow(v.z / lt) | (static_cast<uint32_t>(F::narrow(v.w / lt)) << 16);
+    *reinterpret_cast<uint2*>(out + tid * 4) = make_uint2(lo, hi);
   }
 }
 
 template <int DT, int D, int GT>
 int launch_attn_gt(int kind, const AttnParams& p, hipStream_t stream) {
   using TL = Tile<D, GT>;
-  const size_t lds = lds_floats(D, GT, TL::GTP, p.chunk) * sizeof(float);
   const dim3 block(kThreads);
   const int nkv = p.num_kv_heads * p.head_chunks;
   if (kind == 0) {
+    const size_t lds = lds_floats(D, GT, TL::GTP, p.chunk) * sizeof(float);
     const dim3 grid(nkv, p.num_seqs, 1);
-    hipLaunchKernelGGL((attn_kernel<DT, D, GT, false>), grid, block, lds, stream, p);
+    hipLaunchKernelGGL((single_kernel<DT, D, GT>), grid, block, lds, stream, p);
   } else {
+    const size_t lds = lds_floats(D, GT, TL::GTP, p.chunk) * sizeof(float);
     const dim3 grid = p.work_items ? dim3(((p.num_work_items + 7) / 8) * 8 * nkv, 1, 1)
                                    : dim3(p.grid_parts, nkv, p.num_seqs);
-    hipLaunchKernelGGL((attn_kernel<DT, D, GT, true>), grid, block, lds, stream, p);
+    hipLaunchKernelGGL((split_kernel<DT, D, GT>), grid, block, lds, stream, p);
   }
   return static_cast<int>(hipGetLastError());
 }
