@@ -117,6 +117,12 @@ pa_status pa_reshape_and_cache(const void* key, const void* value,
  * A sequence with context_lens[i] == 0 gets an all-zero output row.
  * Supported: head_dim in {64, 128}; block_size in {16, 32};
  * num_q_heads % num_kv_heads == 0.
+ *   start_event,
+ *   stop_event        NULL, or events (created with timing) that the launch
+ *                     records itself when the decode starts and ends
+ *                     (hipExtLaunchKernel): times the decode without a
+ *                     marker in the stream.  With nothing to launch they are
+ *                     recorded at the call.
  * ---------------------------------------------------------------------- */
 pa_status pa_decode(void* out, const void* query, const void* key_cache,
                     const void* value_cache, const int32_t* block_tables,
@@ -125,7 +131,8 @@ pa_status pa_decode(void* out, const void* query, const void* key_cache,
                     int32_t num_kv_heads, int32_t head_dim,
                     int32_t block_size, int32_t num_blocks,
                     int32_t max_context_len, float scale, pa_dtype dtype,
-                    hipStream_t stream);
+                    hipStream_t stream,
+                    hipEvent_t start_event, hipEvent_t stop_event);
 
 /* Bytes of device workspace pa_decode_partitioned needs: per (sequence,
  * q head, partition) an fp32 accumulator [head_dim], a max and a sum, for
@@ -162,6 +169,8 @@ size_t pa_decode_partitioned_workspace_size(int32_t num_seqs,
  * l = sum exp(logit - m) and acc = sum exp(logit - m) V; a second kernel
  * merges: out = sum_p e^(m_p - M) acc_p / sum_p e^(m_p - M) l_p with
  * M = max_p m_p.  Result as pa_decode up to fp32 rounding order.
+ * start_event / stop_event as for pa_decode: recorded when the first kernel
+ * starts and the merge ends.
  * ---------------------------------------------------------------------- */
 pa_status pa_decode_partitioned(void* out, const void* query,
                                 const void* key_cache, const void* value_cache,
@@ -175,7 +184,8 @@ pa_status pa_decode_partitioned(void* out, const void* query,
                                 int32_t partition_size,
                                 const int32_t* work_items,
                                 int32_t num_work_items, void* workspace,
-                                size_t workspace_bytes, hipStream_t stream);
+                                size_t workspace_bytes, hipStream_t stream,
+                                hipEvent_t start_event, hipEvent_t stop_event);
 
 /* ------------------------------------------------------------------------
  * Decode-step update of device-resident block tables.
@@ -200,6 +210,46 @@ pa_status pa_update_block_tables(int32_t* block_tables, int32_t max_blocks_per_s
                                  const int64_t* slot_mapping, int32_t num_seqs,
                                  int32_t block_size, int32_t num_blocks,
                                  hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * One decode step's writes in one launch: the same results as copying the
+ * step's staged metadata to the device, then pa_update_block_tables, then
+ * pa_reshape_and_cache (the new token goes into its slot and its block into
+ * the table: "vLLM 深度拆解：当大模型推理学会「分页注意力」", §3.1 and §3.3
+ * append_slot; "LLM推理优化：vLLM PagedAttention深度解析与工程实践", §3.1
+ * block table), without the copy launch: the kernel reads the staged arrays
+ * from pinned host memory over the bus.
+ *   staged_slots   [num_seqs] int64, pinned host memory (hipHostMalloc or a
+ *                  pinned torch tensor; 8-byte aligned): each new token's slot
+ *   staged_lens    [num_seqs] int32, pinned host memory: context lengths, the
+ *                  new token included
+ *   staged_items   [num_items][2] int32, pinned host memory (8-byte aligned),
+ *                  or NULL with num_items = 0: a work list for
+ *                  pa_decode_partitioned
+ *   slot_mapping   [num_seqs] int64, device: receives staged_slots
+ *   context_lens   [num_seqs] int32, device: receives staged_lens
+ *   work_items     [num_items][2] int32, device: receives staged_items
+ *   block_tables   [num_seqs][max_blocks_per_seq] int32, device, updated as
+ *                  pa_update_block_tables does
+ *   key, value     [num_seqs][num_kv_heads][head_dim] 16-bit, device
+ *   key_cache, value_cache  the pools, written as pa_reshape_and_cache does
+ * The staged buffers must stay unchanged until the launch has run:
+ * done_event (NULL, or an event created with timing) is recorded by the
+ * launch itself when its kernel ends, and a host that waits on it before
+ * rewriting them needs no marker in the stream.  Copy-on-write block copies
+ * (pa_copy_blocks) must be issued before this call.  Returns
+ * PA_ERR_INVALID_ARG, launching nothing, when a staged pointer is not host
+ * memory the device can read.
+ * ---------------------------------------------------------------------- */
+pa_status pa_write_step(const int64_t* staged_slots, const int32_t* staged_lens,
+                        const int32_t* staged_items, int32_t num_items,
+                        int64_t* slot_mapping, int32_t* context_lens,
+                        int32_t* work_items, int32_t* block_tables,
+                        int32_t max_blocks_per_seq, const void* key,
+                        const void* value, void* key_cache, void* value_cache,
+                        int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim,
+                        int32_t block_size, int32_t num_blocks,
+                        hipStream_t stream, hipEvent_t done_event);
 
 /* ------------------------------------------------------------------------
  * Block copy for copy-on-write: for each pair k, block dst[k] of both pools

@@ -20,11 +20,12 @@ from ._native import (  # noqa: F401
     pa_decode_partitioned_workspace_size,
     pa_reshape_and_cache,
     pa_update_block_tables,
+    pa_write_step,
     partition_work_items,
 )
 
 __all__ = [
     "Allocator", "PaError", "PaOOM", "PA_F16", "PA_BF16", "lib", "pa_copy_blocks", "pa_decode",
     "pa_decode_partitioned", "pa_decode_partitioned_workspace_size", "pa_reshape_and_cache",
-    "pa_update_block_tables", "partition_work_items",
+    "pa_update_block_tables", "pa_write_step", "partition_work_items",
 ]

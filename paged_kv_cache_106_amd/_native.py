@@ -58,9 +58,9 @@ _sig("pa_last_error", ctypes.c_char_p, [])
 _sig("pa_version", ctypes.c_char_p, [])
 _sig("pa_reshape_and_cache", _i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp])
 _DEC = [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32]
-_sig("pa_decode", _i32, _DEC + [_vp])
+_sig("pa_decode", _i32, _DEC + [_vp, _vp, _vp])
 _sig("pa_decode_partitioned_workspace_size", _sz, [_i32, _i32, _i32, _i32, _i32])
-_sig("pa_decode_partitioned", _i32, _DEC + [_i32, _vp, _i32, _vp, _sz, _vp])
+_sig("pa_decode_partitioned", _i32, _DEC + [_i32, _vp, _i32, _vp, _sz, _vp, _vp, _vp])
 _sig("pa_copy_blocks", _i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp])
 _sig("pa_alloc_create", _i32, [_i32, _i32, _i32p, ctypes.POINTER(_vp)])
 _sig("pa_alloc_destroy", None, [_vp])
@@ -68,6 +68,8 @@ _sig("pa_alloc_allocate", _i32, [_vp, _i64, _i32])
 _sig("pa_alloc_append_slot", _i32, [_vp, _i64, _i64p, _i32p, _i32p])
 _sig("pa_alloc_append_slots", _i32, [_vp, _i64p, _i32, _i64p, _i32p, _i32p, _i32p])
 _sig("pa_update_block_tables", _i32, [_vp, _i32, _vp, _vp, _i32, _i32, _i32, _vp])
+_sig("pa_write_step", _i32, [_vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp,
+                             _i32, _i32, _i32, _i32, _i32, _vp, _vp])
 _sig("pa_alloc_share_prefix", _i32, [_vp, _i64, _i64, _i32])
 _sig("pa_alloc_fork", _i32, [_vp, _i64, _i64])
 _sig("pa_alloc_free", _i32, [_vp, _i64])
@@ -110,12 +112,27 @@ def _stream(stream):
     return getattr(stream, "cuda_stream", stream)
 
 
+def _event(e):
+    """hipEvent_t of an event object from ._hip (or None)."""
+    return None if e is None else e.handle
+
+
 def _dptr(t, name, elem_size=None):
     if not getattr(t, "is_cuda", False):
         raise ValueError(f"{name} must be a GPU tensor")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if elem_size is not None and t.element_size() != elem_size:
+        raise ValueError(f"{name} must have {elem_size}-byte elements")
+    return t.data_ptr()
+
+
+def _pinned_ptr(t, name, elem_size):
+    if getattr(t, "is_cuda", True) or not t.is_pinned():
+        raise ValueError(f"{name} must be a pinned host tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.element_size() != elem_size:
         raise ValueError(f"{name} must have {elem_size}-byte elements")
     return t.data_ptr()
 
@@ -138,6 +155,38 @@ def pa_reshape_and_cache(key, value, key_cache, value_cache, slot_mapping, dtype
         bs, nb, _dtype_code(dtype), _stream(stream)))
 
 
+def pa_write_step(staged_slots, staged_lens, staged_items, slot_mapping, context_lens, work_items,
+                  block_tables, key, value, key_cache, value_cache, stream=None, done_event=None):
+    """One decode step's metadata copy, table update and cache write in one
+    launch.  staged_slots int64 [S], staged_lens int32 [S] and staged_items
+    int32 [n][2] (or None) are pinned host tensors; the rest are GPU tensors:
+    slot_mapping int64 [S], context_lens int32 [S], work_items int32 [>= n][2],
+    block_tables int32 [S][MB], key/value [S][Hkv][D], caches [NB][bs][Hkv][D]."""
+    nb, bs, hkv, d = key_cache.shape
+    s = staged_slots.shape[0]
+    if tuple(staged_lens.shape) != (s,) or tuple(slot_mapping.shape) != (s,) or \
+            tuple(context_lens.shape) != (s,):
+        raise ValueError("staged and device slots / lengths must be [S]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != s:
+        raise ValueError("block_tables must be [S][MB]")
+    if tuple(key.shape) != (s, hkv, d) or tuple(value.shape) != (s, hkv, d):
+        raise ValueError("key/value must be [S][Hkv][D] matching the caches")
+    if tuple(value_cache.shape) != tuple(key_cache.shape):
+        raise ValueError("key_cache and value_cache shapes differ")
+    n = 0 if staged_items is None else int(staged_items.shape[0])
+    if n and (staged_items.dim() != 2 or staged_items.shape[1] != 2 or
+              work_items.shape[0] < n or work_items.shape[1] != 2):
+        raise ValueError("work lists must be [n][2], the device one at least as long")
+    _check(_lib.pa_write_step(
+        _pinned_ptr(staged_slots, "staged_slots", 8), _pinned_ptr(staged_lens, "staged_lens", 4),
+        _pinned_ptr(staged_items, "staged_items", 4) if n else None, n,
+        _dptr(slot_mapping, "slot_mapping", 8), _dptr(context_lens, "context_lens", 4),
+        _dptr(work_items, "work_items", 4) if n else None, _dptr(block_tables, "block_tables", 4),
+        block_tables.shape[1], _dptr(key, "key", 2), _dptr(value, "value", 2),
+        _dptr(key_cache, "key_cache", 2), _dptr(value_cache, "value_cache", 2), s, hkv, d, bs, nb,
+        _stream(stream), _event(done_event)))
+
+
 def _decode_args(out, query, key_cache, value_cache, block_tables, context_lens, max_context_len,
                  scale, dtype):
     s, hq, d = query.shape
@@ -156,11 +205,12 @@ def _decode_args(out, query, key_cache, value_cache, block_tables, context_lens,
 
 
 def pa_decode(out, query, key_cache, value_cache, block_tables, context_lens, max_context_len,
-              scale, dtype, stream=None):
-    """Single-pass paged decode; writes out [S][Hq][D]."""
+              scale, dtype, stream=None, start_event=None, stop_event=None):
+    """Single-pass paged decode; writes out [S][Hq][D].  start/stop events
+    (._hip.Event with timing, or None) are recorded by the launch itself."""
     args = _decode_args(out, query, key_cache, value_cache, block_tables, context_lens,
                         max_context_len, scale, dtype)
-    _check(_lib.pa_decode(*args, _stream(stream)))
+    _check(_lib.pa_decode(*args, _stream(stream), _event(start_event), _event(stop_event)))
 
 
 def pa_decode_partitioned_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len,
@@ -171,9 +221,10 @@ def pa_decode_partitioned_workspace_size(num_seqs, num_q_heads, head_dim, max_co
 
 def pa_decode_partitioned(out, query, key_cache, value_cache, block_tables, context_lens,
                           max_context_len, scale, dtype, partition_size, workspace,
-                          work_items=None, stream=None):
+                          work_items=None, stream=None, start_event=None, stop_event=None):
     """Split-context paged decode + merge; workspace is a uint8 GPU tensor;
-    work_items an optional int32 GPU tensor [n][2] of (sequence, partition)."""
+    work_items an optional int32 GPU tensor [n][2] of (sequence, partition);
+    start/stop events as for pa_decode."""
     args = _decode_args(out, query, key_cache, value_cache, block_tables, context_lens,
                         max_context_len, scale, dtype)
     if work_items is None:
@@ -185,7 +236,7 @@ def pa_decode_partitioned(out, query, key_cache, value_cache, block_tables, cont
     _check(_lib.pa_decode_partitioned(*args, int(partition_size), wi, int(nwi),
                                       _dptr(workspace, "workspace"),
                                       workspace.numel() * workspace.element_size(),
-                                      _stream(stream)))
+                                      _stream(stream), _event(start_event), _event(stop_event)))
 
 
 def partition_work_items(context_lens, partition_size, max_parts=None):

@@ -44,7 +44,8 @@ Workspace workspace_layout(int64_t num_seqs, int64_t num_q_heads, int64_t head_d
   return w;
 }
 
-int (*attn_launcher(pa_dtype dtype, int32_t head_dim))(int, const AttnParams&, hipStream_t) {
+int (*attn_launcher(pa_dtype dtype, int32_t head_dim))(int, const AttnParams&, hipStream_t,
+                                                       hipEvent_t, hipEvent_t) {
   if (dtype == PA_F16) return head_dim == 64 ? launch_attn_f16_d64 : launch_attn_f16_d128;
   return head_dim == 64 ? launch_attn_bf16_d64 : launch_attn_bf16_d128;
 }
@@ -112,6 +113,18 @@ pa_status check_decode(void* out, const void* query, const void* key_cache,
   return PA_OK;
 }
 
+// With nothing to launch, the caller's events still mark this point of the
+// stream, so waiting on them behaves as after a launch.
+pa_status mark_events(hipEvent_t start, hipEvent_t stop, hipStream_t stream, const char* what) {
+  for (hipEvent_t e : {start, stop}) {
+    if (e && hipEventRecord(e, stream) != hipSuccess) {
+      g_last_error = std::string(what) + ": hipEventRecord failed";
+      return PA_ERR_HIP;
+    }
+  }
+  return PA_OK;
+}
+
 pa_status launched(int err, const char* what) {
   if (err != 0) {
     std::string msg = std::string(what) + ": " + hipGetErrorString(static_cast<hipError_t>(err));
@@ -168,12 +181,80 @@ pa_status pa_reshape_and_cache(const void* key, const void* value, void* key_cac
                       "pa_reshape_and_cache");
 }
 
+namespace {
+// Device address of pinned host memory (NULL stays NULL); fails for memory
+// the device cannot read.
+bool device_view(const void* host, const void** dev) {
+  if (!host) {
+    *dev = nullptr;
+    return true;
+  }
+  void* d = nullptr;
+  if (hipHostGetDevicePointer(&d, const_cast<void*>(host), 0) != hipSuccess || !d) {
+    (void)hipGetLastError();   // leave no sticky error for the next call
+    return false;
+  }
+  *dev = d;
+  return true;
+}
+}  // namespace
+
+pa_status pa_write_step(const int64_t* staged_slots, const int32_t* staged_lens,
+                        const int32_t* staged_items, int32_t num_items, int64_t* slot_mapping,
+                        int32_t* context_lens, int32_t* work_items, int32_t* block_tables,
+                        int32_t max_blocks_per_seq, const void* key, const void* value,
+                        void* key_cache, void* value_cache, int32_t num_seqs,
+                        int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                        int32_t num_blocks, hipStream_t stream, hipEvent_t done_event) {
+  pa::clear_error();
+  if (num_seqs < 0 || num_items < 0) return fail(PA_ERR_INVALID_ARG, "negative count");
+  if (num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0 ||
+      max_blocks_per_seq <= 0)
+    return fail(PA_ERR_INVALID_ARG,
+                "num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq must be positive");
+  if (head_dim % 8 != 0) return fail(PA_ERR_UNSUPPORTED, "head_dim must be a multiple of 8");
+  if (num_seqs == 0 && num_items == 0)
+    return pa::mark_events(nullptr, done_event, stream, "pa_write_step");
+  if (num_seqs > 0 && (!staged_slots || !staged_lens || !slot_mapping || !context_lens ||
+                       !block_tables || !key || !value || !key_cache || !value_cache))
+    return fail(PA_ERR_INVALID_ARG, "NULL pointer");
+  if (num_items > 0 && (!staged_items || !work_items))
+    return fail(PA_ERR_INVALID_ARG, "NULL work list");
+  if (!pa::aligned(staged_slots, 8) || !pa::aligned(staged_lens, 4) ||
+      !pa::aligned(staged_items, 8) || !pa::aligned(slot_mapping, 8) ||
+      !pa::aligned(context_lens, 4) || !pa::aligned(work_items, 8) ||
+      !pa::aligned(block_tables, 4) || !pa::aligned(key, 16) || !pa::aligned(value, 16) ||
+      !pa::aligned(key_cache, 16) || !pa::aligned(value_cache, 16))
+    return fail(PA_ERR_INVALID_ARG,
+                "misaligned buffer (K/V 16 bytes, slots and work list 8, lengths and tables 4)");
+  const int64_t row = static_cast<int64_t>(num_kv_heads) * head_dim;
+  const int64_t chunks_per_tok = row / 8;
+  if (chunks_per_tok > INT32_MAX) return fail(PA_ERR_UNSUPPORTED, "token row too large");
+  const int64_t num_chunks = static_cast<int64_t>(num_seqs) * chunks_per_tok;
+  if ((num_chunks + 255) / 256 + (static_cast<int64_t>(num_items) + 255) / 256 > INT32_MAX)
+    return fail(PA_ERR_UNSUPPORTED, "too many tokens");
+  const void *ds, *dl, *di;
+  if (!device_view(staged_slots, &ds) || !device_view(staged_lens, &dl) ||
+      !device_view(staged_items, &di))
+    return fail(PA_ERR_INVALID_ARG,
+                "staged arrays must be pinned host memory the device can read (hipHostMalloc)");
+  const int64_t num_slots = static_cast<int64_t>(num_blocks) * block_size;
+  return pa::launched(
+      pa::launch_write_step(static_cast<const int64_t*>(ds), static_cast<const int32_t*>(dl),
+                            static_cast<const int32_t*>(di), num_items, slot_mapping,
+                            context_lens, work_items, block_tables, max_blocks_per_seq,
+                            block_size, key, value, key_cache, value_cache, num_seqs,
+                            static_cast<int32_t>(chunks_per_tok), num_slots, stream,
+                            done_event),
+      "pa_write_step");
+}
+
 pa_status pa_decode(void* out, const void* query, const void* key_cache, const void* value_cache,
                     const int32_t* block_tables, int32_t max_blocks_per_seq,
                     const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                     int32_t num_blocks, int32_t max_context_len, float scale, pa_dtype dtype,
-                    hipStream_t stream) {
+                    hipStream_t stream, hipEvent_t start_event, hipEvent_t stop_event) {
   pa::clear_error();
   pa::AttnParams p;
   const pa_status st = pa::check_decode(out, query, key_cache, value_cache, block_tables,
@@ -181,9 +262,10 @@ pa_status pa_decode(void* out, const void* query, const void* key_cache, const v
                                         num_kv_heads, head_dim, block_size, num_blocks,
                                         max_context_len, scale, dtype, &p);
   if (st != PA_OK) return st;
-  if (num_seqs == 0) return PA_OK;
+  if (num_seqs == 0) return pa::mark_events(start_event, stop_event, stream, "pa_decode");
   p.chunk = pa::kSingleChunk;
-  return pa::launched(pa::attn_launcher(dtype, head_dim)(0, p, stream), "pa_decode");
+  return pa::launched(pa::attn_launcher(dtype, head_dim)(0, p, stream, start_event, stop_event),
+                      "pa_decode");
 }
 
 size_t pa_decode_partitioned_workspace_size(int32_t num_seqs, int32_t num_q_heads,
@@ -204,7 +286,8 @@ pa_status pa_decode_partitioned(void* out, const void* query, const void* key_ca
                                 int32_t max_context_len, float scale, pa_dtype dtype,
                                 int32_t partition_size, const int32_t* work_items,
                                 int32_t num_work_items, void* workspace, size_t workspace_bytes,
-                                hipStream_t stream) {
+                                hipStream_t stream, hipEvent_t start_event,
+                                hipEvent_t stop_event) {
   pa::clear_error();
   pa::AttnParams p;
   const pa_status st = pa::check_decode(out, query, key_cache, value_cache, block_tables,
@@ -221,7 +304,8 @@ pa_status pa_decode_partitioned(void* out, const void* query, const void* key_ca
     return fail(PA_ERR_INVALID_ARG, "work_items must be NULL or a 4-byte aligned device array");
   if ((static_cast<int64_t>(num_work_items) + 7) * p.num_kv_heads * p.head_chunks > INT32_MAX)
     return fail(PA_ERR_UNSUPPORTED, "num_work_items * num_kv_heads * head chunks overflows int32");
-  if (num_seqs == 0) return PA_OK;
+  if (num_seqs == 0)
+    return pa::mark_events(start_event, stop_event, stream, "pa_decode_partitioned");
   const int64_t parts = (static_cast<int64_t>(max_context_len) + partition_size - 1) / partition_size;
   if (parts >= pa::kMaxGrid) return fail(PA_ERR_UNSUPPORTED, "more than 65534 partitions");
   const pa::Workspace w = pa::workspace_layout(num_seqs, num_q_heads, head_dim, parts);
@@ -240,10 +324,12 @@ pa_status pa_decode_partitioned(void* out, const void* query, const void* key_ca
   auto launch = pa::attn_launcher(dtype, head_dim);
   const bool any = work_items ? num_work_items > 0 : parts > 0;
   if (any) {
-    const pa_status s1 = pa::launched(launch(1, p, stream), "pa_decode_partitioned (partitions)");
+    const pa_status s1 =
+        pa::launched(launch(1, p, stream, start_event, nullptr), "pa_decode_partitioned (partitions)");
     if (s1 != PA_OK) return s1;
   }
-  return pa::launched(launch(2, p, stream), "pa_decode_partitioned (merge)");
+  return pa::launched(launch(2, p, stream, any ? nullptr : start_event, stop_event),
+                      "pa_decode_partitioned (merge)");
 }
 
 pa_status pa_update_block_tables(int32_t* block_tables, int32_t max_blocks_per_seq,

@@ -38,6 +38,7 @@
 // pools' unused slots may hold NaN).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -50,12 +51,16 @@ constexpr int kThreads = 64 * kWaves;
 // unit loads each wave keeps in flight (K, then V): the single-pass kernel
 // walks whole contexts with few workgroups per CU and wants a deeper ring
 #ifndef PA_DEPTH_SPLIT
-#define PA_DEPTH_SPLIT 3
+#define PA_DEPTH_SPLIT 2
 #endif
 #ifndef PA_DEPTH_SINGLE
 #define PA_DEPTH_SINGLE 4
 #endif
+#ifndef PA_EARLY_V
+#define PA_EARLY_V 1
+#endif
 constexpr int kDepthSplit = PA_DEPTH_SPLIT;
+constexpr bool kEarlyV = PA_EARLY_V;
 constexpr int kDepthSingle = PA_DEPTH_SINGLE;
 
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
@@ -338,15 +343,16 @@ struct WaveAttn {
     for (int j = 0; j < VLOADS; ++j) dst[j] = load16(r, voff, j * VTOK * tok_bytes);
   }
 
-  // q slices for the QK layout: chunk c of head hh = dims c*64 + kcol*8 .. +8
+  // q slices for the QK layout: chunk c of head hh = dims c*64 + kcol*8 .. +8.
+  // Heads past nact reread the last active head (their results are never
+  // stored): loads on every path keep the wait counts exact.
   __device__ __forceinline__ void load_q(uint4 (&qv)[GT][KC], int64_t row0, int nact) const {
 #pragma unroll
     for (int hh = 0; hh < GT; ++hh)
 #pragma unroll
       for (int c = 0; c < KC; ++c)
-        qv[hh][c] = hh < nact
-                        ? *reinterpret_cast<const uint4*>(q + (row0 + hh) * D + c * 64 + kcol * 8)
-                        : make_uint4(0, 0, 0, 0);
+        qv[hh][c] = *reinterpret_cast<const uint4*>(q + (row0 + min(hh, nact - 1)) * D + c * 64 +
+                                                     kcol * 8);
   }
 
   // Logits of the wave's unit i (raw q.k; scaled in the softmax), written by
@@ -604,11 +610,11 @@ __global__ __launch_bounds__(kThreads) void single_kernel(AttnParams p) {
     const typename W::Span s = w.span(bt, c0, min(p.chunk, L - c0));
     if (s.cnt == 0) continue;                      // uniform: this wave has no tokens
     {
+      uint4 qv[GT][W::KC];
+      w.load_q(qv, row0, nact);                    // first: waiting for q must not wait for K
       uint4 kb[kDepthSingle][W::KLOADS];
 #pragma unroll
       for (int b = 0; b < kDepthSingle; ++b) w.load_k(kb[b], s, b);
-      uint4 qv[GT][W::KC];
-      w.load_q(qv, row0, nact);
       w.template logits<kDepthSingle>(qv, kb, s);
     }
     uint4 vb[kDepthSingle][W::VLOADS];             // streams in during the softmax
@@ -684,17 +690,28 @@ __global__ __launch_bounds__(kThreads) void split_kernel(AttnParams p) {
     l_w[hh] = 0.f;
   }
   if (s.cnt > 0) {                                 // uniform: this wave has tokens
+    // Issue order matters: loads complete in order for the wait counts, so q
+    // goes first (waiting for it must not wait for the rings).
+    uint4 vb[kDepthSplit][W::VLOADS];
     {
+      uint4 qv[GT][W::KC];
+      w.load_q(qv, row0, nact);
       uint4 kb[kDepthSplit][W::KLOADS];
 #pragma unroll
       for (int b = 0; b < kDepthSplit; ++b) w.load_k(kb[b], s, b);
-      uint4 qv[GT][W::KC];
-      w.load_q(qv, row0, nact);
+      if constexpr (kEarlyV) {
+        // the V ring fills behind the K ring: its first units are resident by
+        // the time the logits are done, so the stream does not drain between
+        // the two phases
+#pragma unroll
+        for (int b = 0; b < kDepthSplit; ++b) w.load_v(vb[b], s, b);
+      }
       w.template logits<kDepthSplit>(qv, kb, s);
     }
-    uint4 vb[kDepthSplit][W::VLOADS];              // streams in during the softmax
+    if constexpr (!kEarlyV) {
 #pragma unroll
-    for (int b = 0; b < kDepthSplit; ++b) w.load_v(vb[b], s, b);
+      for (int b = 0; b < kDepthSplit; ++b) w.load_v(vb[b], s, b);   // streams in during the softmax
+    }
     wave_lds_sync();
     float alpha[GT];
     w.softmax(s, m_w, l_w, alpha);
@@ -830,39 +847,41 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(AttnParams p) {
 }
 
 template <int DT, int D, int GT>
-int launch_attn_gt(int kind, const AttnParams& p, hipStream_t stream) {
+int launch_attn_gt(int kind, const AttnParams& p, hipStream_t stream, hipEvent_t start,
+                   hipEvent_t stop) {
   using TL = Tile<D, GT>;
   const dim3 block(kThreads);
   const int nkv = p.num_kv_heads * p.head_chunks;
   if (kind == 0) {
     const size_t lds = lds_floats(D, GT, TL::GTP, p.chunk) * sizeof(float);
     const dim3 grid(nkv, p.num_seqs, 1);
-    hipLaunchKernelGGL((single_kernel<DT, D, GT>), grid, block, lds, stream, p);
+    hipExtLaunchKernelGGL((single_kernel<DT, D, GT>), grid, block, lds, stream, start, stop, 0, p);
   } else {
     const size_t lds = lds_floats(D, GT, TL::GTP, p.chunk) * sizeof(float);
     const dim3 grid = p.work_items ? dim3(((p.num_work_items + 7) / 8) * 8 * nkv, 1, 1)
                                    : dim3(p.grid_parts, nkv, p.num_seqs);
-    hipLaunchKernelGGL((split_kernel<DT, D, GT>), grid, block, lds, stream, p);
+    hipExtLaunchKernelGGL((split_kernel<DT, D, GT>), grid, block, lds, stream, start, stop, 0, p);
   }
   return static_cast<int>(hipGetLastError());
 }
 
 template <int DT, int D>
-int launch_attn(int kind, const AttnParams& p, hipStream_t stream) {
+int launch_attn(int kind, const AttnParams& p, hipStream_t stream, hipEvent_t start,
+                hipEvent_t stop) {
   if (kind == 2) {
     const dim3 grid(p.num_seqs * p.num_q_heads);
-    hipLaunchKernelGGL((merge_kernel<DT, D>), grid, dim3(kThreads), 0, stream, p);
+    hipExtLaunchKernelGGL((merge_kernel<DT, D>), grid, dim3(kThreads), 0, stream, start, stop, 0, p);
     return static_cast<int>(hipGetLastError());
   }
   switch (p.heads_per_wg) {
-    case 1: return launch_attn_gt<DT, D, 1>(kind, p, stream);
-    case 2: return launch_attn_gt<DT, D, 2>(kind, p, stream);
-    case 3: return launch_attn_gt<DT, D, 3>(kind, p, stream);
-    case 4: return launch_attn_gt<DT, D, 4>(kind, p, stream);
-    case 5: return launch_attn_gt<DT, D, 5>(kind, p, stream);
-    case 6: return launch_attn_gt<DT, D, 6>(kind, p, stream);
-    case 7: return launch_attn_gt<DT, D, 7>(kind, p, stream);
-    case 8: return launch_attn_gt<DT, D, 8>(kind, p, stream);
+    case 1: return launch_attn_gt<DT, D, 1>(kind, p, stream, start, stop);
+    case 2: return launch_attn_gt<DT, D, 2>(kind, p, stream, start, stop);
+    case 3: return launch_attn_gt<DT, D, 3>(kind, p, stream, start, stop);
+    case 4: return launch_attn_gt<DT, D, 4>(kind, p, stream, start, stop);
+    case 5: return launch_attn_gt<DT, D, 5>(kind, p, stream, start, stop);
+    case 6: return launch_attn_gt<DT, D, 6>(kind, p, stream, start, stop);
+    case 7: return launch_attn_gt<DT, D, 7>(kind, p, stream, start, stop);
+    case 8: return launch_attn_gt<DT, D, 8>(kind, p, stream, start, stop);
     default: return static_cast<int>(hipErrorInvalidValue);
   }
 }

@@ -2,7 +2,8 @@
 #include "pa_attn.h"
 
 namespace pa {
-int launch_attn_bf16_d128(int kind, const AttnParams& p, hipStream_t stream) {
-  return launch_attn<PA_BF16, 128>(kind, p, stream);
+int launch_attn_bf16_d128(int kind, const AttnParams& p, hipStream_t stream, hipEvent_t start,
+                          hipEvent_t stop) {
+  return launch_attn<PA_BF16, 128>(kind, p, stream, start, stop);
 }
 }  // namespace pa

@@ -45,15 +45,27 @@ struct AttnParams {
 
 // Launchers; each returns the hipError_t of its launch.
 // kind: 0 = single-pass decode, 1 = split-context partitions, 2 = merge.
-int launch_attn_f16_d64(int kind, const AttnParams& p, hipStream_t stream);
-int launch_attn_f16_d128(int kind, const AttnParams& p, hipStream_t stream);
-int launch_attn_bf16_d64(int kind, const AttnParams& p, hipStream_t stream);
-int launch_attn_bf16_d128(int kind, const AttnParams& p, hipStream_t stream);
+// start / stop (may be NULL): events the launch itself records when the
+// kernel starts / ends (hipExtLaunchKernel), with no marker in the stream.
+int launch_attn_f16_d64(int kind, const AttnParams& p, hipStream_t stream, hipEvent_t start,
+                        hipEvent_t stop);
+int launch_attn_f16_d128(int kind, const AttnParams& p, hipStream_t stream, hipEvent_t start,
+                         hipEvent_t stop);
+int launch_attn_bf16_d64(int kind, const AttnParams& p, hipStream_t stream, hipEvent_t start,
+                         hipEvent_t stop);
+int launch_attn_bf16_d128(int kind, const AttnParams& p, hipStream_t stream, hipEvent_t start,
+                          hipEvent_t stop);
 int launch_cache_write(const void* key, const void* value, void* k_cache, void* v_cache,
                        const int64_t* slots, int32_t n, int32_t chunks_per_tok,
                        int64_t num_slots, hipStream_t stream);
 int launch_update_tables(int32_t* tables, int32_t mb, const int32_t* lens, const int64_t* slots,
                          int32_t n, int32_t bs, int64_t num_slots, hipStream_t stream);
+int launch_write_step(const int64_t* staged_slots, const int32_t* staged_lens,
+                      const int32_t* staged_items, int32_t num_items, int64_t* slot_mapping,
+                      int32_t* context_lens, int32_t* work_items, int32_t* tables, int32_t mb,
+                      int32_t bs, const void* key, const void* value, void* k_cache,
+                      void* v_cache, int32_t n, int32_t chunks_per_tok, int64_t num_slots,
+                      hipStream_t stream, hipEvent_t done);
 int launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int32_t num_pairs,
                        int64_t chunks_per_block, int32_t num_blocks, hipStream_t stream);
 

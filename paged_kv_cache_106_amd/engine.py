@@ -20,10 +20,13 @@ Pinned metadata buffers are double-buffered: the host prepares step k+1
 while the GPU still runs step k, and waits on an event only before reusing
 a buffer whose copy may not have run yet.
 """
+import collections
+
 import numpy as np
 import torch
 
 from . import _native as pa
+from ._hip import Event
 
 POISON = {"f16": 0x7E00, "bf16": 0x7FC0}   # quiet-NaN patterns for unused slots
 
@@ -72,10 +75,14 @@ class DecodeStep:
 
     The block tables live on the GPU: they are uploaded whole once (and again
     by ``sync_tables`` after any allocator change other than this step's own
-    appends); each step then sends only the new tokens' slots, the context
-    lengths and any copy-on-write pairs, and pa_update_block_tables records
-    each new token's block in place.
+    appends); each step stages only the new tokens' slots, the context
+    lengths, any copy-on-write pairs and the work list in pinned memory, and
+    one pa_write_step launch brings them to the device, records each new
+    token's block in the tables and writes the new K/V.
     """
+
+    RING = 8            # pinned staging buffers
+    EVENT_EVERY = 4     # write launches per recorded event (<= RING)
 
     def __init__(self, cache, seq_ids, num_q_heads, kernel="partitioned", partition_size=512,
                  max_context_len=None, scale=None, stream=None):
@@ -93,23 +100,29 @@ class DecodeStep:
         self.max_context_len = int(max_context_len)
         self.mb = -(-self.max_context_len // bs)
         self.max_parts = -(-self.max_context_len // self.partition_size)
-        self._num_items = [0, 0]
         self.scale = float(np.float32(1.0 / np.sqrt(cache.head_dim))) if scale is None else float(scale)
         self.stream = stream if stream is not None else torch.cuda.current_stream(cache.device)
         dev = cache.device
 
         # per-step metadata: built in ordinary (cached) host memory, copied in one
-        # memcpy into pinned staging (double-buffered; CPU stores straight into
-        # pinned pages can be very slow), then to the device twin
+        # memcpy into a ring of pinned staging buffers (CPU stores straight into
+        # pinned pages can be very slow), which the step's write launch reads.
+        # Step k uses buffer k % RING; every EVENT_EVERY-th write launch records
+        # an event when it has run, and before reusing a buffer the host waits
+        # for the first such event at or after the buffer's previous step.
+        # (Every event costs the stream a few microseconds, so not one per step.)
         self._stage = np.zeros(self._meta_bytes(), np.uint8)
         self._host = [torch.empty(self._meta_bytes(), dtype=torch.uint8, pin_memory=True)
-                      for _ in range(2)]
-        self._events = [None, None]
-        self._turn = 0
+                      for _ in range(self.RING)]
+        self._num_items = [0] * self.RING
+        self._num_cow = [0] * self.RING
+        self._step = 0                               # steps prepared so far
+        self._cur = 0
+        self._recorded = collections.deque()         # (step, event) of recorded write launches
+        self._spare = [Event(timing=True) for _ in range(self.RING // self.EVENT_EVERY + 2)]
         self._dev_meta = torch.empty(self._meta_bytes(), dtype=torch.uint8, device=dev)
         self.slot_mapping, self.context_lens, self.cow_pairs, self.work_items = \
             self._views(self._dev_meta)
-        self._num_cow = [0, 0]
         self.block_tables = torch.zeros((self.S, self.mb), dtype=torch.int32, device=dev)
         self.out = torch.empty((self.S, self.num_q_heads, cache.head_dim), dtype=torch.int16,
                                device=dev)
@@ -154,10 +167,13 @@ class DecodeStep:
     def prepare(self):
         """a1: one slot per sequence from the host allocator, staged in pinned
         memory.  Returns the index of the staging buffer."""
-        b = self._turn
-        self._turn ^= 1
-        if self._events[b] is not None:
-            self._events[b].synchronize()          # its previous copy has run
+        k = self._step
+        b = k % self.RING
+        if k >= self.RING:                          # step k - RING's write must have run
+            while self._recorded and self._recorded[0][0] < k - self.RING:
+                self._spare.append(self._recorded.popleft()[1])
+            if self._recorded:
+                self._recorded[0][1].synchronize()
         sm, cl, cow, items = (t.numpy() for t in self._views(torch.from_numpy(self._stage)))
         if int(self.host_context_lens.max(initial=0)) >= self.max_context_len:
             raise ValueError("a sequence would outgrow max_context_len")
@@ -180,39 +196,56 @@ class DecodeStep:
         return b
 
     def upload(self, b):
-        """a2: async copy of the staged metadata to the device, on the step's stream."""
-        n = self._nbytes
+        """a2: the staged metadata reaches the device inside write_new's launch
+        (pa_write_step reads the pinned staging buffer over the bus); only
+        copy-on-write pairs, which pa_copy_blocks reads before that launch,
+        are copied here."""
+        self._cur = b
+        self._step += 1
         self._ncow_dev = self._num_cow[b]
         self._nitems_dev = self._num_items[b]
-        with torch.cuda.stream(self.stream):
-            self._dev_meta[:n].copy_(self._host[b][:n], non_blocking=True)
-            ev = torch.cuda.Event()
-            ev.record(self.stream)
-        self._events[b] = ev
+        if self._ncow_dev:
+            o2 = self._offsets()[1]
+            n = 8 * self._ncow_dev
+            with torch.cuda.stream(self.stream):
+                self._dev_meta[o2:o2 + n].copy_(self._host[b][o2:o2 + n], non_blocking=True)
 
     def write_new(self, k_new, v_new):
-        """a3: copy-on-write copies (if any), the table entries of the new
-        tokens' blocks, then the new tokens' K/V ([S][Hkv][D]) into their slots."""
+        """a3: copy-on-write copies (if any), then one launch that copies the
+        staged slots, lengths and work list to the device, records the new
+        tokens' blocks in the tables and writes their K/V ([S][Hkv][D]) into
+        their slots."""
         c = self.cache
+        b = self._cur
         if self._ncow_dev:
             pa.pa_copy_blocks(c.key_cache, c.value_cache, self.cow_pairs[: self._ncow_dev],
                               c.dtype, self.stream)
-        pa.pa_update_block_tables(self.block_tables, self.context_lens, self.slot_mapping,
-                                  c.block_size, c.num_blocks, self.stream)
-        pa.pa_reshape_and_cache(k_new, v_new, c.key_cache, c.value_cache, self.slot_mapping,
-                                c.dtype, self.stream)
+        sm, cl, _, items = self._views(self._host[b])
+        n = self._nitems_dev
+        k = self._step - 1
+        ev = None
+        if k % self.EVENT_EVERY == self.EVENT_EVERY - 1:
+            ev = self._spare.pop()                 # the launch records it when it has run
+            self._recorded.append((k, ev))
+        pa.pa_write_step(sm, cl, items[:n] if n else None, self.slot_mapping, self.context_lens,
+                         self.work_items, self.block_tables, k_new, v_new, c.key_cache,
+                         c.value_cache, self.stream, done_event=ev)
 
-    def attend(self, q):
-        """a4 or a5+a6: decode for q [S][Hq][D] into self.out."""
+    def attend(self, q, start_event=None, stop_event=None):
+        """a4 or a5+a6: decode for q [S][Hq][D] into self.out.  Optional
+        ._hip.Event objects are recorded by the decode's launches themselves
+        when it starts and ends."""
         c = self.cache
         if self.kernel == "single":
             pa.pa_decode(self.out, q, c.key_cache, c.value_cache, self.block_tables,
-                         self.context_lens, self.max_context_len, self.scale, c.dtype, self.stream)
+                         self.context_lens, self.max_context_len, self.scale, c.dtype, self.stream,
+                         start_event, stop_event)
         else:
             pa.pa_decode_partitioned(self.out, q, c.key_cache, c.value_cache, self.block_tables,
                                      self.context_lens, self.max_context_len, self.scale, c.dtype,
                                      self.partition_size, self.workspace,
-                                     self.work_items[: self._nitems_dev], self.stream)
+                                     self.work_items[: self._nitems_dev], self.stream,
+                                     start_event, stop_event)
         return self.out
 
     def __call__(self, q, k_new, v_new):

@@ -61,7 +61,7 @@ def decode(**kw):
     a.update(kw)
     return L.pa_decode(a["out"], a["query"], a["key_cache"], a["value_cache"], a["block_tables"],
                        a["mb"], a["context_lens"], a["S"], a["Hq"], a["Hkv"], a["D"], a["bs"],
-                       a["NB"], a["maxlen"], a["scale"], a["dtype"], None)
+                       a["NB"], a["maxlen"], a["scale"], a["dtype"], None, None, None)
 
 
 def decode_part(P=512, ws=BAD, ws_bytes=1 << 30, items=None, nitems=0, **kw):
@@ -72,7 +72,7 @@ def decode_part(P=512, ws=BAD, ws_bytes=1 << 30, items=None, nitems=0, **kw):
     return L.pa_decode_partitioned(a["out"], a["query"], a["key_cache"], a["value_cache"],
                                    a["block_tables"], a["mb"], a["context_lens"], a["S"], a["Hq"],
                                    a["Hkv"], a["D"], a["bs"], a["NB"], a["maxlen"], a["scale"],
-                                   a["dtype"], P, items, nitems, ws, ws_bytes, None)
+                                   a["dtype"], P, items, nitems, ws, ws_bytes, None, None, None)
 
 
 @pytest.mark.parametrize("kw,status", [

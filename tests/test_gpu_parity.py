@@ -209,6 +209,91 @@ def test_negative_slots_write_nothing():
     free_gpu()
 
 
+def test_write_step_matches_separate_calls():
+    """pa_write_step (staged metadata read from pinned memory, one launch)
+    leaves the pools, the tables and the device metadata bit-identical to a
+    device copy followed by pa_update_block_tables and pa_reshape_and_cache,
+    padding slots included."""
+    w = workload(3, "small")
+    g = gpu_side.build(w, extra_tokens=4)
+    c, st = g.cache, g.step
+    a = c.allocator
+    slots, lens, _, _ = a.append_slots(st.seq_ids)
+    slots[1] = -1                                   # a padding token: no write, no table entry
+    items = pa.partition_work_items(lens, 64)
+    pin = lambda x: torch.from_numpy(np.ascontiguousarray(x)).pin_memory()
+    s_h, l_h, i_h = pin(slots), pin(lens), pin(items)
+    kc, vc = c.key_cache.clone(), c.value_cache.clone()
+    bt = st.block_tables.clone()
+    # separate calls
+    sm_a = s_h.cuda(); cl_a = l_h.cuda()
+    pa.pa_update_block_tables(st.block_tables, cl_a, sm_a, w.bs, w.num_blocks)
+    pa.pa_reshape_and_cache(g.k_new, g.v_new, c.key_cache, c.value_cache, sm_a, w.dtype)
+    # one launch
+    sm_b = torch.full_like(sm_a, 7)
+    cl_b = torch.full_like(cl_a, 7)
+    wi_b = torch.full((items.shape[0] + 3, 2), -9, dtype=torch.int32, device="cuda")
+    pa.pa_write_step(s_h, l_h, i_h, sm_b, cl_b, wi_b, bt, g.k_new, g.v_new, kc, vc)
+    torch.cuda.synchronize()
+    assert np.array_equal(gpu_side.to_host16(kc), gpu_side.to_host16(c.key_cache))
+    assert np.array_equal(gpu_side.to_host16(vc), gpu_side.to_host16(c.value_cache))
+    assert torch.equal(bt, st.block_tables)
+    assert torch.equal(sm_b, sm_a) and torch.equal(cl_b, cl_a)
+    got = wi_b.cpu().numpy()
+    assert np.array_equal(got[: items.shape[0]], items) and (got[items.shape[0]:] == -9).all()
+    del g
+    free_gpu()
+
+
+def test_launch_recorded_events():
+    """Events handed to the decode and to the step write are recorded by the
+    launches themselves: they complete, time a positive interval, and change
+    no result."""
+    from paged_kv_cache_106_amd._hip import Event
+    for cfg in (3, 2):                               # split-context, single pass
+        w = workload(cfg, "small")
+        g = gpu_side.build(w)
+        ref = g.step.attend(g.q).clone()
+        e0, e1 = Event(timing=True), Event(timing=True)
+        out = g.step.attend(g.q, e0, e1)
+        e1.synchronize()
+        ms = e0.elapsed_time(e1)
+        print(f"[cfg{cfg} small] decode {ms * 1e3:.1f} us", flush=True)
+        assert 0.0 < ms < 1000.0
+        assert torch.equal(out, ref)
+        del g
+        free_gpu()
+
+
+def test_write_step_rejects_pageable_staging():
+    """Staged arrays the device cannot read are refused before any launch:
+    by the binding (not pinned) and by the C ABI (pageable pointer)."""
+    import ctypes
+    w = workload(1, "full")
+    g = gpu_side.build(w)
+    c, st = g.cache, g.step
+    slots = torch.zeros(w.S, dtype=torch.int64)
+    lens = torch.ones(w.S, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        pa.pa_write_step(slots, lens, None, st.slot_mapping, st.context_lens, st.work_items,
+                         st.block_tables, g.k_new, g.v_new, c.key_cache, c.value_cache)
+    before = gpu_side.to_host16(c.key_cache).copy()
+    hs = np.zeros(w.S, np.int64)
+    hl = np.ones(w.S, np.int32)
+    lib = pa.lib()
+    st_code = lib.pa_write_step(
+        hs.ctypes.data, hl.ctypes.data, None, 0, st.slot_mapping.data_ptr(),
+        st.context_lens.data_ptr(), None, st.block_tables.data_ptr(), st.block_tables.shape[1],
+        g.k_new.data_ptr(), g.v_new.data_ptr(), c.key_cache.data_ptr(), c.value_cache.data_ptr(),
+        w.S, w.Hkv, w.D, w.bs, w.num_blocks, torch.cuda.current_stream().cuda_stream, None)
+    torch.cuda.synchronize()
+    assert st_code == 1, lib.pa_last_error()        # PA_ERR_INVALID_ARG
+    assert b"pinned" in lib.pa_last_error()
+    assert np.array_equal(gpu_side.to_host16(c.key_cache), before)
+    del g
+    free_gpu()
+
+
 def test_copy_on_write_blocks():
     """fork, then append: the allocator reports (src, dst) and pa_copy_blocks
     copies the shared block bit for bit before the new token lands."""
@@ -234,13 +319,16 @@ def test_copy_on_write_blocks():
 
 
 def test_decode_steps_across_block_boundaries():
-    """Three whole decode steps (a1..a6) of the engine against the oracle
-    replaying the same appends: positions cross block boundaries."""
+    """Twenty whole decode steps (a1..a6) of the engine against the oracle
+    replaying the same appends: positions cross block boundaries, and the
+    staging ring wraps twice (its buffers are reused only after the write
+    launch that read them has run)."""
     w = workload(3, "small")
-    g = gpu_side.build(w, extra_tokens=4)
+    g = gpu_side.build(w, extra_tokens=21)
     o = oracle_side.build(w)
     step = g.step
-    for k in range(3):
+    assert 20 > 2 * step.RING
+    for k in range(20):
         out = step(g.q, g.k_new, g.v_new)
         slots = np.array([o.model.append_slot(i)[0] for i in range(w.S)], np.int64)
         oracle.cache_write(o.k_new, o.v_new, o.key_cache, o.value_cache, slots)
@@ -254,6 +342,34 @@ def test_decode_steps_across_block_boundaries():
                                     nthreads=0)
         check_outputs(gpu_side.to_host16(out), ref32, refT, w.dtype, f"engine step {k}")
     assert np.array_equal(gpu_side.to_host16(g.cache.key_cache), o.key_cache)
+    del g
+    free_gpu()
+
+
+def test_engine_steps_back_to_back():
+    """Twenty steps enqueued with no host synchronisation (the host runs ahead
+    of the GPU and the staging ring wraps twice): the pools, tables and
+    lengths end as the oracle's after the same twenty appends, and the last
+    step's output matches."""
+    w = workload(3, "small")
+    g = gpu_side.build(w, extra_tokens=21)
+    o = oracle_side.build(w)
+    step = g.step
+    for k in range(20):
+        out = step(g.q, g.k_new, g.v_new)
+    for k in range(20):
+        slots = np.array([o.model.append_slot(i)[0] for i in range(w.S)], np.int64)
+        oracle.cache_write(o.k_new, o.v_new, o.key_cache, o.value_cache, slots)
+    torch.cuda.synchronize()
+    bt = oracle_side.tables_of(o.model, w.S, step.mb)
+    cl = np.array([o.model.num_tokens[i] for i in range(w.S)], np.int32)
+    assert np.array_equal(step.block_tables.cpu().numpy(), bt)
+    assert np.array_equal(step.context_lens.cpu().numpy(), cl)
+    assert np.array_equal(gpu_side.to_host16(g.cache.key_cache), o.key_cache)
+    assert np.array_equal(gpu_side.to_host16(g.cache.value_cache), o.value_cache)
+    ref32, refT = oracle.decode(o.q, o.key_cache, o.value_cache, bt, cl, w.scale, w.dtype,
+                                nthreads=0)
+    check_outputs(gpu_side.to_host16(out), ref32, refT, w.dtype, "engine, 20 steps back to back")
     del g
     free_gpu()
 
