@@ -351,6 +351,22 @@ int32_t pa_alloc_num_free(const pa_allocator* a);
 /* Reference count of a physical block, or -1 for an invalid id. */
 int32_t pa_alloc_refcount(const pa_allocator* a, int32_t block_id);
 
+/* Work list for pa_decode_partitioned from the host's context lengths:
+ * every live (sequence, partition) pair of partition_size tokens (at most
+ * max_parts per sequence; max_parts < 0: no limit), full partitions first in
+ * sequence order, then each sequence's ragged last partition, longest first
+ * (ties in sequence order), so the shortest work fills the end of the
+ * launch.  Splitting the context into partitions follows the split-context
+ * ("v2") kernel of "LLM推理优化：vLLM PagedAttention深度解析与工程实践", §4.1;
+ * the order is this library's scheduling choice.
+ *   context_lens  [num_seqs] int32, host memory
+ *   items_out     [capacity][2] int32, host memory: (sequence, partition)
+ * *n_out = the number of items; PA_ERR_INVALID_ARG if it exceeds capacity
+ * (the first capacity items are written). */
+pa_status pa_partition_work_items(const int32_t* context_lens, int32_t num_seqs,
+                                  int32_t partition_size, int32_t max_parts,
+                                  int32_t* items_out, int32_t capacity, int32_t* n_out);
+
 /* The free pool in order (head first) into out[0..cap); *n_out = its size. */
 pa_status pa_alloc_free_list(const pa_allocator* a, int32_t* out, int32_t cap,
                              int32_t* n_out);

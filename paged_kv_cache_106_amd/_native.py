@@ -80,6 +80,7 @@ _sig("pa_alloc_num_tokens", _i32, [_vp, _i64])
 _sig("pa_alloc_num_free", _i32, [_vp])
 _sig("pa_alloc_refcount", _i32, [_vp, _i32])
 _sig("pa_alloc_free_list", _i32, [_vp, _i32p, _i32, _i32p])
+_sig("pa_partition_work_items", _i32, [_vp, _i32, _i32, _i32, _vp, _i32, _i32p])
 
 
 def lib():
@@ -239,24 +240,22 @@ def pa_decode_partitioned(out, query, key_cache, value_cache, block_tables, cont
                                       _stream(stream), _event(start_event), _event(stop_event)))
 
 
-def partition_work_items(context_lens, partition_size, max_parts=None):
-    """Host-side work list for pa_decode_partitioned: (sequence, partition)
-    for every live partition.  Full partitions come first (sequence-major),
-    then the ragged last partitions by decreasing length, so the shortest
-    work fills the tail of the launch.  context_lens: int array [S]."""
-    L = np.asarray(context_lens, dtype=np.int64)
-    nP = (L + partition_size - 1) // partition_size
-    if max_parts is not None:
-        nP = np.minimum(nP, max_parts)
-    total = int(nP.sum())
-    seq = np.repeat(np.arange(L.shape[0], dtype=np.int64), nP)
-    part = np.arange(total, dtype=np.int64) - np.repeat(np.cumsum(nP) - nP, nP)
-    ntok = np.minimum(partition_size, L[seq] - part * partition_size)
-    order = np.argsort(-ntok, kind="stable")
-    out = np.empty((total, 2), np.int32)
-    out[:, 0] = seq[order]
-    out[:, 1] = part[order]
-    return out
+def partition_work_items(context_lens, partition_size, max_parts=None, out=None):
+    """Host-side work list for pa_decode_partitioned (pa_partition_work_items):
+    (sequence, partition) for every live partition, full partitions first
+    (sequence-major), then the ragged last partitions by decreasing length,
+    so the shortest work fills the tail of the launch.  context_lens: int
+    array [S].  Returns int32 [n][2] (a view of `out` if given)."""
+    L = np.ascontiguousarray(context_lens, dtype=np.int32)
+    if out is None:
+        P = int(partition_size)
+        cap = int(((L.astype(np.int64) + P - 1) // P).sum()) if P > 0 else 0
+        out = np.empty((max(cap, 1), 2), np.int32)
+    n = ctypes.c_int32()
+    _check(_lib.pa_partition_work_items(L.ctypes.data, L.shape[0], int(partition_size),
+                                        -1 if max_parts is None else int(max_parts),
+                                        out.ctypes.data, out.shape[0], ctypes.byref(n)))
+    return out[: n.value]
 
 
 def pa_update_block_tables(block_tables, context_lens, slot_mapping, block_size, num_blocks,

@@ -13,6 +13,7 @@
 //   sequences   hash map seq_id -> {block ids in logical order, token count}
 // Every failing call returns before changing anything.
 
+#include <algorithm>
 #include <cstdint>
 #include <cstring>
 #include <new>
@@ -309,6 +310,54 @@ pa_status pa_alloc_free_list(const pa_allocator* a, int32_t* out, int32_t cap, i
     return invalid("pa_alloc_free_list: output too small");
   for (int64_t k = 0; k < a->count; ++k)
     out[k] = a->ring[static_cast<size_t>((a->head + k) % a->num_blocks)];
+  return PA_OK;
+}
+
+pa_status pa_partition_work_items(const int32_t* context_lens, int32_t num_seqs,
+                                  int32_t partition_size, int32_t max_parts, int32_t* items_out,
+                                  int32_t capacity, int32_t* n_out) {
+  pa::clear_error();
+  if (!n_out || num_seqs < 0 || partition_size <= 0 || capacity < 0 ||
+      (num_seqs > 0 && !context_lens) || (capacity > 0 && !items_out))
+    return invalid("pa_partition_work_items: bad argument");
+  struct Ragged {
+    int32_t ntok, seq, part;
+  };
+  std::vector<Ragged> ragged;
+  ragged.reserve(static_cast<size_t>(num_seqs));
+  int64_t n = 0;
+  // full partitions, sequence-major; the ragged last ones are set aside
+  for (int32_t i = 0; i < num_seqs; ++i) {
+    const int64_t L = context_lens[i];
+    if (L <= 0) continue;
+    int64_t np = (L + partition_size - 1) / partition_size;
+    if (max_parts >= 0 && np > max_parts) np = max_parts;
+    for (int64_t p = 0; p < np; ++p) {
+      const int64_t ntok = std::min<int64_t>(partition_size, L - p * partition_size);
+      if (ntok < partition_size) {
+        ragged.push_back({static_cast<int32_t>(ntok), i, static_cast<int32_t>(p)});
+        continue;
+      }
+      if (n < capacity) {
+        items_out[2 * n] = i;
+        items_out[2 * n + 1] = static_cast<int32_t>(p);
+      }
+      ++n;
+    }
+  }
+  // then the ragged ones, longest first (ties in sequence order)
+  std::stable_sort(ragged.begin(), ragged.end(),
+                   [](const Ragged& x, const Ragged& y) { return x.ntok > y.ntok; });
+  for (const Ragged& r : ragged) {
+    if (n < capacity) {
+      items_out[2 * n] = r.seq;
+      items_out[2 * n + 1] = r.part;
+    }
+    ++n;
+  }
+  if (n > INT32_MAX) return invalid("pa_partition_work_items: too many items");
+  *n_out = static_cast<int32_t>(n);
+  if (n > capacity) return invalid("pa_partition_work_items: output too small");
   return PA_OK;
 }
 

@@ -21,6 +21,7 @@ while the GPU still runs step k, and waits on an event only before reusing
 a buffer whose copy may not have run yet.
 """
 import collections
+import ctypes
 
 import numpy as np
 import torch
@@ -131,6 +132,59 @@ class DecodeStep:
         self.workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=dev)
         self.host_context_lens = np.zeros(self.S, np.int32)
         self.sync_tables()
+        self._bind_calls()
+
+    def _bind_calls(self):
+        """Argument lists of the per-step library calls, built once: every
+        buffer they name belongs to this object and is never reallocated, so
+        a step fills in only what changes (counts, the new K/V and q, events).
+        The per-step inputs are checked against the shapes fixed here."""
+        c = self.cache
+        S = self.S
+        L = pa.lib()
+        self._sm, self._cl, self._cow, self._items = \
+            (t.numpy() for t in self._views(torch.from_numpy(self._stage)))
+        self._src = np.empty(S, np.int32)
+        self._dst = np.empty(S, np.int32)
+        self._nitems = ctypes.c_int32()
+        i64p, i32p = ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int32)
+        self._append_call = (L.pa_alloc_append_slots, (
+            c.allocator._h, self.seq_ids.ctypes.data_as(i64p), S, self._sm.ctypes.data_as(i64p),
+            self._cl.ctypes.data_as(i32p), self._src.ctypes.data_as(i32p),
+            self._dst.ctypes.data_as(i32p)))
+        self._items_call = (L.pa_partition_work_items, (
+            self._cl.ctypes.data, S, self.partition_size, self.max_parts, self._items.ctypes.data,
+            self._items.shape[0], ctypes.byref(self._nitems)))
+        o1, _, o3 = self._offsets()
+        stream = self.stream.cuda_stream
+        self._write_args = []
+        for h in self._host:
+            base = h.data_ptr()
+            self._write_args.append([
+                base, base + o1, base + o3, 0, self.slot_mapping.data_ptr(),
+                self.context_lens.data_ptr(), self.work_items.data_ptr(),
+                self.block_tables.data_ptr(), self.mb, None, None, c.key_cache.data_ptr(),
+                c.value_cache.data_ptr(), S, c.num_kv_heads, c.head_dim, c.block_size,
+                c.num_blocks, stream, None])
+        self._kv_shape = (S, c.num_kv_heads, c.head_dim)
+        self._q_shape = (S, self.num_q_heads, c.head_dim)
+        dec = [self.out.data_ptr(), None, c.key_cache.data_ptr(), c.value_cache.data_ptr(),
+               self.block_tables.data_ptr(), self.mb, self.context_lens.data_ptr(), S,
+               self.num_q_heads, c.num_kv_heads, c.head_dim, c.block_size, c.num_blocks,
+               self.max_context_len, self.scale, pa._dtype_code(c.dtype)]
+        if self.kernel == "single":
+            self._decode_fn, self._decode_args = L.pa_decode, dec + [stream, None, None]
+        else:
+            self._decode_fn = L.pa_decode_partitioned
+            self._decode_args = dec + [self.partition_size, self.work_items.data_ptr(), 0,
+                                       self.workspace.data_ptr(),
+                                       self.workspace.numel(), stream, None, None]
+
+    def _check_input(self, t, shape, name):
+        if tuple(t.shape) != shape or not t.is_cuda or t.element_size() != 2 or \
+                not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous 16-bit GPU tensor of shape {shape}")
+        return t.data_ptr()
 
     # layout: slots int64 [S] | context_lens int32 [S] (+pad to 8 bytes) |
     #         cow pairs int32 [S][2] | work items int32 [S * max_parts][2]
@@ -166,7 +220,8 @@ class DecodeStep:
 
     def prepare(self):
         """a1: one slot per sequence from the host allocator, staged in pinned
-        memory.  Returns the index of the staging buffer."""
+        memory with the lengths, copy-on-write pairs and work list.  Returns
+        the index of the staging buffer."""
         k = self._step
         b = k % self.RING
         if k >= self.RING:                          # step k - RING's write must have run
@@ -174,25 +229,23 @@ class DecodeStep:
                 self._spare.append(self._recorded.popleft()[1])
             if self._recorded:
                 self._recorded[0][1].synchronize()
-        sm, cl, cow, items = (t.numpy() for t in self._views(torch.from_numpy(self._stage)))
         if int(self.host_context_lens.max(initial=0)) >= self.max_context_len:
             raise ValueError("a sequence would outgrow max_context_len")
-        _, _, src, dst = self.cache.allocator.append_slots(
-            self.seq_ids, slots_out=sm, context_lens_out=self.host_context_lens)
-        cl[:] = self.host_context_lens
-        k = np.flatnonzero(src >= 0)
-        self._num_cow[b] = int(k.size)
-        if k.size:
-            cow[: k.size, 0] = src[k]
-            cow[: k.size, 1] = dst[k]
-        n = self._offsets()[1] + 8 * int(k.size)
+        fn, args = self._append_call
+        pa._check(fn(*args))                        # slots and lengths into the staging area
+        self.host_context_lens[:] = self._cl
+        cow = np.flatnonzero(self._src >= 0)
+        self._num_cow[b] = int(cow.size)
+        if cow.size:
+            self._cow[: cow.size, 0] = self._src[cow]
+            self._cow[: cow.size, 1] = self._dst[cow]
+        n = self._offsets()[1] + 8 * int(cow.size)
         if self.kernel == "partitioned":
-            wl = pa.partition_work_items(self.host_context_lens, self.partition_size, self.max_parts)
-            items[: wl.shape[0]] = wl
-            self._num_items[b] = int(wl.shape[0])
-            n = self._offsets()[2] + 8 * int(wl.shape[0])
+            fn, args = self._items_call
+            pa._check(fn(*args))
+            self._num_items[b] = self._nitems.value
+            n = self._offsets()[2] + 8 * self._nitems.value
         self._host[b].numpy()[:n] = self._stage[:n]
-        self._nbytes = n
         return b
 
     def upload(self, b):
@@ -220,32 +273,29 @@ class DecodeStep:
         if self._ncow_dev:
             pa.pa_copy_blocks(c.key_cache, c.value_cache, self.cow_pairs[: self._ncow_dev],
                               c.dtype, self.stream)
-        sm, cl, _, items = self._views(self._host[b])
-        n = self._nitems_dev
+        args = self._write_args[b]
+        args[3] = self._nitems_dev
+        args[9] = self._check_input(k_new, self._kv_shape, "k_new")
+        args[10] = self._check_input(v_new, self._kv_shape, "v_new")
         k = self._step - 1
         ev = None
         if k % self.EVENT_EVERY == self.EVENT_EVERY - 1:
             ev = self._spare.pop()                 # the launch records it when it has run
             self._recorded.append((k, ev))
-        pa.pa_write_step(sm, cl, items[:n] if n else None, self.slot_mapping, self.context_lens,
-                         self.work_items, self.block_tables, k_new, v_new, c.key_cache,
-                         c.value_cache, self.stream, done_event=ev)
+        args[19] = None if ev is None else ev.handle
+        pa._check(pa.lib().pa_write_step(*args))
 
     def attend(self, q, start_event=None, stop_event=None):
         """a4 or a5+a6: decode for q [S][Hq][D] into self.out.  Optional
         ._hip.Event objects are recorded by the decode's launches themselves
         when it starts and ends."""
-        c = self.cache
-        if self.kernel == "single":
-            pa.pa_decode(self.out, q, c.key_cache, c.value_cache, self.block_tables,
-                         self.context_lens, self.max_context_len, self.scale, c.dtype, self.stream,
-                         start_event, stop_event)
-        else:
-            pa.pa_decode_partitioned(self.out, q, c.key_cache, c.value_cache, self.block_tables,
-                                     self.context_lens, self.max_context_len, self.scale, c.dtype,
-                                     self.partition_size, self.workspace,
-                                     self.work_items[: self._nitems_dev], self.stream,
-                                     start_event, stop_event)
+        args = self._decode_args
+        args[1] = self._check_input(q, self._q_shape, "q")
+        if self.kernel == "partitioned":
+            args[18] = self._nitems_dev
+        args[-2] = None if start_event is None else start_event.handle
+        args[-1] = None if stop_event is None else stop_event.handle
+        pa._check(self._decode_fn(*args))
         return self.out
 
     def __call__(self, q, k_new, v_new):
