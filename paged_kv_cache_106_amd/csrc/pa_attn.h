@@ -42,6 +42,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "pa_internal.h"
 
 namespace pa {
@@ -132,7 +134,7 @@ __device__ inline float wave_sum_from(float x, int first_stride) {
   return x;
 }
 
-// Sum over the lanes l, l ^ S, l ^ 2S, ... up to 64 for S = 8 or 16: lane
+// Sum over the lanes l, l ^ S, l ^ 2S, ... up to 64 for S = 8, 16 or 32: lane
 // xor 8 by a DPP rotate inside the 16-lane row, xor 16 and xor 32 by the
 // CDNA4 row swaps.  v_permlane16_swap(a, b) exchanges the odd rows of a with
 // the even rows of b, so with a = b = x the two results add up to
@@ -140,11 +142,13 @@ __device__ inline float wave_sum_from(float x, int first_stride) {
 // two 32-lane halves.
 template <int S>
 __device__ inline float rows_sum(float x) {
-  static_assert(S == 8 || S == 16, "row stride");
+  static_assert(S == 8 || S == 16 || S == 32, "row stride");
   if constexpr (S == 8) x += dpp<0x128>(x);   // row_ror:8
-  const uint32_t b = __float_as_uint(x);
-  const auto r16 = __builtin_amdgcn_permlane16_swap(b, b, false, false);
-  x = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+  if constexpr (S <= 16) {
+    const uint32_t b = __float_as_uint(x);
+    const auto r16 = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+    x = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+  }
   const uint32_t c = __float_as_uint(x);
   const auto r32 = __builtin_amdgcn_permlane32_swap(c, c, false, false);
   return __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
@@ -155,24 +159,37 @@ __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 // Token layout inside a workgroup.  Work is cut into units of 16 tokens (one
 // block of 16, or one half of a block of 32), and wave w takes units w, w+4,
 // ... of the chunk.
-//  QK: 8 lanes per token, each holding KC = D/64 16-byte chunks of the K row
-//      (dims c*64 + kcol*8 .. +8): a wave load covers 8 tokens x 128 bytes,
-//      and a 3-step DPP sum finishes each dot product.
-//  PV: VL = D/8 lanes per token, each holding 8 consecutive dims: a wave
-//      load covers VTOK = 64/VL tokens; each lane accumulates its 8 dims for
-//      every head of the group.
-template <int D, int GT>
+//  QK: QL lanes per token, each holding KC = D / (8 QL) 16-byte chunks of the
+//      K row (dims c*8*QL + kcol*8 .. +8): a wave load covers KTOK = 64 / QL
+//      tokens, and a log2(QL)-step DPP sum finishes each dot product.
+//  PV: VL = D / VW lanes per token, each holding VW consecutive dims (16 or
+//      8 bytes): a wave load covers VTOK = 64 / VL tokens; each lane
+//      accumulates its VW dims for every head of the group.
+// The narrow layout (QL 16, VW 4: half the q and accumulator registers per
+// lane, for the same bytes per load instruction in QK) lets more waves share
+// a SIMD when the group has many heads.
+template <int D, int GT, bool NARROW>
 struct Tile {
   static constexpr int UNIT = 16;
-  static constexpr int KC = D / 64;
-  static constexpr int KTOK = 8;
-  static constexpr int KGROUPS = UNIT / KTOK;       // 2
+  static constexpr int QL = (NARROW && D >= 128) ? 16 : 8;
+  static constexpr int KC = D / (8 * QL);
+  static constexpr int KTOK = 64 / QL;
+  static constexpr int KGROUPS = UNIT / KTOK;
   static constexpr int KLOADS = KGROUPS * KC;       // 16-byte loads per lane per unit
-  static constexpr int VL = D / 8;
+  static constexpr int VW = NARROW ? 4 : 8;
+  static constexpr int VL = D / VW;
   static constexpr int VTOK = 64 / VL;
   static constexpr int VLOADS = UNIT / VTOK;
   static constexpr int GTP = GT == 1 ? 1 : (GT == 2 ? 2 : (GT <= 4 ? 4 : 8));
+  static_assert(KC >= 1 && VL <= 32 && KGROUPS >= 1, "layout");
 };
+
+// Query heads per workgroup from which the narrow layout is used.
+#ifndef PA_NARROW_MIN_GT
+#define PA_NARROW_MIN_GT 5
+#endif
+template <int GT>
+constexpr bool kNarrow = GT >= PA_NARROW_MIN_GT;
 
 // LDS (floats): logits / probabilities [chunk][GTP], wave partial outputs
 // [kWaves][GT][D], wave maxima and sums [kWaves][GTP] each.
@@ -224,6 +241,11 @@ __device__ inline uint4 load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
+__device__ inline uint2 load8(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+  return make_uint2(v[0], v[1]);
+}
+
 // Wave-wide reductions that leave the result in every lane: a DPP butterfly
 // inside each 16-lane row, then the four row results read back as scalars.
 __device__ inline float wave_max_all(float x) {
@@ -260,9 +282,13 @@ __device__ inline void wave_lds_sync() {
 template <int DT, int D, int GT>
 struct WaveAttn {
   using F = Fmt<DT>;
-  using TL = Tile<D, GT>;
-  static constexpr int UNIT = TL::UNIT, KC = TL::KC, KGROUPS = TL::KGROUPS, KLOADS = TL::KLOADS;
-  static constexpr int VL = TL::VL, VTOK = TL::VTOK, VLOADS = TL::VLOADS, GTP = TL::GTP;
+  using TL = Tile<D, GT, kNarrow<GT>>;
+  static constexpr int UNIT = TL::UNIT, QL = TL::QL, KC = TL::KC, KTOK = TL::KTOK,
+                       KGROUPS = TL::KGROUPS, KLOADS = TL::KLOADS;
+  static constexpr int VW = TL::VW, VL = TL::VL, VTOK = TL::VTOK, VLOADS = TL::VLOADS,
+                       GTP = TL::GTP;
+  // a lane's piece of a V row: 16 bytes (8 dims) or 8 bytes (4 dims)
+  using VVec = typename std::conditional<VW == 8, uint4, uint2>::type;
 
   // Tokens [c0, c0 + n) of one sequence as one wave sees them: its units are
   // u = wave, wave + 4, ... below ceil(n / UNIT), cnt of them.  Lane i of blk
@@ -287,8 +313,8 @@ struct WaveAttn {
     const int tid = threadIdx.x;
     wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     lane = tid & 63;
-    krow = lane >> 3;
-    kcol = lane & 7;
+    krow = lane / QL;
+    kcol = lane % QL;
     vrow = lane / VL;
     vcol = lane % VL;
     kbase = static_cast<const char*>(p.k_cache);
@@ -298,7 +324,7 @@ struct WaveAttn {
     tok_bytes = static_cast<uint32_t>(p.num_kv_heads) * D * 2;
     const uint32_t head_off = static_cast<uint32_t>(kvh) * D * 2;
     koff = static_cast<uint32_t>(krow) * tok_bytes + head_off + kcol * 16;
-    voff = static_cast<uint32_t>(vrow) * tok_bytes + head_off + vcol * 16;
+    voff = static_cast<uint32_t>(vrow) * tok_bytes + head_off + vcol * VW * 2;
     bs_mask = p.block_size - 1;
     log2_bs = p.log2_block_size;
     num_blocks = p.num_blocks;
@@ -335,15 +361,21 @@ struct WaveAttn {
 #pragma unroll
     for (int j = 0; j < KGROUPS; ++j)
 #pragma unroll
-      for (int c = 0; c < KC; ++c) dst[j * KC + c] = load16(r, koff + c * 128, j * 8 * tok_bytes);
+      for (int c = 0; c < KC; ++c)
+        dst[j * KC + c] = load16(r, koff + c * QL * 16, j * KTOK * tok_bytes);
   }
-  __device__ __forceinline__ void load_v(uint4 (&dst)[VLOADS], const Span& s, int i) const {
+  __device__ __forceinline__ void load_v(VVec (&dst)[VLOADS], const Span& s, int i) const {
     const auto r = block_rsrc(vbase + unit_off(s, i), i < s.cnt);
 #pragma unroll
-    for (int j = 0; j < VLOADS; ++j) dst[j] = load16(r, voff, j * VTOK * tok_bytes);
+    for (int j = 0; j < VLOADS; ++j) {
+      if constexpr (VW == 8)
+        dst[j] = load16(r, voff, j * VTOK * tok_bytes);
+      else
+        dst[j] = load8(r, voff, j * VTOK * tok_bytes);
+    }
   }
 
-  // q slices for the QK layout: chunk c of head hh = dims c*64 + kcol*8 .. +8.
+  // q slices for the QK layout: chunk c of head hh = dims c*8*QL + kcol*8 .. +8.
   // Heads past nact reread the last active head (their results are never
   // stored): loads on every path keep the wait counts exact.
   __device__ __forceinline__ void load_q(uint4 (&qv)[GT][KC], int64_t row0, int nact) const {
@@ -351,8 +383,8 @@ struct WaveAttn {
     for (int hh = 0; hh < GT; ++hh)
 #pragma unroll
       for (int c = 0; c < KC; ++c)
-        qv[hh][c] = *reinterpret_cast<const uint4*>(q + (row0 + min(hh, nact - 1)) * D + c * 64 +
-                                                     kcol * 8);
+        qv[hh][c] = *reinterpret_cast<const uint4*>(q + (row0 + min(hh, nact - 1)) * D +
+                                                     c * 8 * QL + kcol * 8);
   }
 
   // Logits of the wave's unit i (raw q.k; scaled in the softmax), written by
@@ -374,36 +406,45 @@ struct WaveAttn {
           a = F::dot2(qv[hh][c].z, k.z, a);
           a = F::dot2(qv[hh][c].w, k.w, a);
         }
-        sv[hh] = group_sum<8>(a);
+        sv[hh] = group_sum<QL>(a);
       }
 #pragma unroll
       for (int hh = GT; hh < GTP; ++hh) sv[hh] = 0.f;
-      if (kcol == 0) lds_store(s_lds + (u * UNIT + j * 8 + krow) * GTP, sv);
+      if (kcol == 0) lds_store(s_lds + (u * UNIT + j * KTOK + krow) * GTP, sv);
     }
   }
 
   // P.V of the wave's unit i; tokens past n get V = 0 (their p is 0 and their
   // slots may hold NaN).
-  __device__ __forceinline__ void pv_unit(float (&acc)[GT][8], const uint4 (&vx)[VLOADS],
+  __device__ __forceinline__ void pv_unit(float (&acc)[GT][VW], const VVec (&vx)[VLOADS],
                                           const Span& s, int i) const {
     const int u = wave + kWaves * i;
     const bool tail = (u + 1) * UNIT > s.n;
 #pragma unroll
     for (int j = 0; j < VLOADS; ++j) {
       const int t = u * UNIT + j * VTOK + vrow;
-      uint4 x = vx[j];
-      if (tail && t >= s.n) x = make_uint4(0, 0, 0, 0);
+      uint32_t w[VW / 2];
+      if constexpr (VW == 8) {
+        w[0] = vx[j].x; w[1] = vx[j].y; w[2] = vx[j].z; w[3] = vx[j].w;
+      } else {
+        w[0] = vx[j].x; w[1] = vx[j].y;
+      }
+      if (tail && t >= s.n) {
+#pragma unroll
+        for (int e = 0; e < VW / 2; ++e) w[e] = 0;
+      }
       float pr[GTP];
       lds_load(pr, s_lds + t * GTP);
-      float vf[8];
-      vf[0] = F::lo(x.x); vf[1] = F::hi(x.x);
-      vf[2] = F::lo(x.y); vf[3] = F::hi(x.y);
-      vf[4] = F::lo(x.z); vf[5] = F::hi(x.z);
-      vf[6] = F::lo(x.w); vf[7] = F::hi(x.w);
+      float vf[VW];
+#pragma unroll
+      for (int e = 0; e < VW / 2; ++e) {
+        vf[2 * e] = F::lo(w[e]);
+        vf[2 * e + 1] = F::hi(w[e]);
+      }
 #pragma unroll
       for (int hh = 0; hh < GT; ++hh)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[hh][e] = fmaf(pr[hh], vf[e], acc[hh][e]);
+        for (int e = 0; e < VW; ++e) acc[hh][e] = fmaf(pr[hh], vf[e], acc[hh][e]);
       // keep each group's probabilities and widened V short-lived
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -479,7 +520,7 @@ struct WaveAttn {
   // P.V over all the wave's units through a ring of DEPTH unit buffers, as
   // the logits.
   template <int DEPTH>
-  __device__ __forceinline__ void values(float (&acc)[GT][8], uint4 (&vb)[DEPTH][VLOADS],
+  __device__ __forceinline__ void values(float (&acc)[GT][VW], VVec (&vb)[DEPTH][VLOADS],
                                          const Span& s) const {
     for (int i = 0; i < s.cnt; i += DEPTH) {
 #pragma unroll
@@ -497,11 +538,12 @@ struct WaveAttn {
 // (a wave without tokens has m_w = -inf and weight 0).  Split: (acc, M, l)
 // go to the partition's workspace slot; single pass: out = acc / l.
 template <int DT, int D, int GT, bool SPLIT>
-__device__ __forceinline__ void combine_waves(const AttnParams& p, float (&acc)[GT][8],
+__device__ __forceinline__ void combine_waves(const AttnParams& p,
+                                              float (&acc)[GT][Tile<D, GT, kNarrow<GT>>::VW],
                                               const float (&m_w)[GT], const float (&l_w)[GT],
                                               float* red, int64_t row0, int nact, int part) {
-  using TL = Tile<D, GT>;
-  constexpr int VL = TL::VL, GTP = TL::GTP;
+  using TL = Tile<D, GT, kNarrow<GT>>;
+  constexpr int VL = TL::VL, VW = TL::VW, GTP = TL::GTP;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -513,11 +555,13 @@ __device__ __forceinline__ void combine_waves(const AttnParams& p, float (&acc)[
 #pragma unroll
   for (int hh = 0; hh < GT; ++hh) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[hh][e] = rows_sum<VL>(acc[hh][e]);
+    for (int e = 0; e < VW; ++e) acc[hh][e] = rows_sum<VL>(acc[hh][e]);
     if (vrow == 0) {
-      float* dst = red + (wave * GT + hh) * D + vcol * 8;
-      *reinterpret_cast<float4*>(dst) = make_float4(acc[hh][0], acc[hh][1], acc[hh][2], acc[hh][3]);
-      *reinterpret_cast<float4*>(dst + 4) = make_float4(acc[hh][4], acc[hh][5], acc[hh][6], acc[hh][7]);
+      float* dst = red + (wave * GT + hh) * D + vcol * VW;
+#pragma unroll
+      for (int e = 0; e < VW; e += 4)
+        *reinterpret_cast<float4*>(dst + e) =
+            make_float4(acc[hh][e], acc[hh][e + 1], acc[hh][e + 2], acc[hh][e + 3]);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -555,7 +599,9 @@ __device__ __forceinline__ void combine_waves(const AttnParams& p, float (&acc)[
       v.w = fmaf(wt, r.w, v.w);
     }
     if constexpr (SPLIT) {
-      const int64_t slot = (row0 + hh) * p.num_parts + part;
+      // workspace rows [S][nP][Hq]: a workgroup's heads are one contiguous run
+      const int64_t seq = row0 / p.num_q_heads;
+      const int64_t slot = (seq * p.num_parts + part) * p.num_q_heads + (row0 - seq * p.num_q_heads) + hh;
       *reinterpret_cast<float4*>(p.part_acc + slot * D + c * 4) = v;
       if (c == 0) {
         p.part_max[slot] = M;
@@ -598,13 +644,13 @@ __global__ __launch_bounds__(kThreads) void single_kernel(AttnParams p) {
 
   const W w(p, kvh, lds);
   const int32_t* bt = p.block_tables + static_cast<int64_t>(seq) * p.mb;
-  float acc[GT][8], m_run[GT], l_run[GT];
+  float acc[GT][W::VW], m_run[GT], l_run[GT];
 #pragma unroll
   for (int hh = 0; hh < GT; ++hh) {
     m_run[hh] = -__builtin_inff();
     l_run[hh] = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[hh][e] = 0.f;
+    for (int e = 0; e < W::VW; ++e) acc[hh][e] = 0.f;
   }
   for (int c0 = 0; c0 < L; c0 += p.chunk) {
     const typename W::Span s = w.span(bt, c0, min(p.chunk, L - c0));
@@ -617,7 +663,7 @@ __global__ __launch_bounds__(kThreads) void single_kernel(AttnParams p) {
       for (int b = 0; b < kDepthSingle; ++b) w.load_k(kb[b], s, b);
       w.template logits<kDepthSingle>(qv, kb, s);
     }
-    uint4 vb[kDepthSingle][W::VLOADS];             // streams in during the softmax
+    typename W::VVec vb[kDepthSingle][W::VLOADS];             // streams in during the softmax
 #pragma unroll
     for (int b = 0; b < kDepthSingle; ++b) w.load_v(vb[b], s, b);
     wave_lds_sync();
@@ -626,7 +672,7 @@ __global__ __launch_bounds__(kThreads) void single_kernel(AttnParams p) {
 #pragma unroll
     for (int hh = 0; hh < GT; ++hh)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[hh][e] *= alpha[hh];
+      for (int e = 0; e < W::VW; ++e) acc[hh][e] *= alpha[hh];
     wave_lds_sync();
     w.template values<kDepthSingle>(acc, vb, s);
     wave_lds_sync();                               // the next chunk rewrites this wave's rows
@@ -683,7 +729,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(AttnParams p) {
   const typename W::Span s =
       w.span(p.block_tables + static_cast<int64_t>(seq) * p.mb, c0, min(p.chunk, L - c0));
 
-  float acc[GT][8], m_w[GT], l_w[GT];
+  float acc[GT][W::VW], m_w[GT], l_w[GT];
 #pragma unroll
   for (int hh = 0; hh < GT; ++hh) {
     m_w[hh] = -__builtin_inff();
@@ -692,23 +738,24 @@ __global__ __launch_bounds__(kThreads) void split_kernel(AttnParams p) {
   if (s.cnt > 0) {                                 // uniform: this wave has tokens
     // Issue order matters: loads complete in order for the wait counts, so q
     // goes first (waiting for it must not wait for the rings).
-    uint4 vb[kDepthSplit][W::VLOADS];
+    typename W::VVec vb[kDepthSplit][W::VLOADS];
     {
       uint4 qv[GT][W::KC];
       w.load_q(qv, row0, nact);
       uint4 kb[kDepthSplit][W::KLOADS];
 #pragma unroll
       for (int b = 0; b < kDepthSplit; ++b) w.load_k(kb[b], s, b);
-      if constexpr (kEarlyV) {
+      if constexpr (kEarlyV && !kNarrow<GT>) {
         // the V ring fills behind the K ring: its first units are resident by
         // the time the logits are done, so the stream does not drain between
-        // the two phases
+        // the two phases.  The narrow layout (many heads) skips this: the
+        // registers it would hold through the logits cost a wave per SIMD.
 #pragma unroll
         for (int b = 0; b < kDepthSplit; ++b) w.load_v(vb[b], s, b);
       }
       w.template logits<kDepthSplit>(qv, kb, s);
     }
-    if constexpr (!kEarlyV) {
+    if constexpr (!(kEarlyV && !kNarrow<GT>)) {
 #pragma unroll
       for (int b = 0; b < kDepthSplit; ++b) w.load_v(vb[b], s, b);   // streams in during the softmax
     }
@@ -719,14 +766,14 @@ __global__ __launch_bounds__(kThreads) void split_kernel(AttnParams p) {
 #pragma unroll
     for (int hh = 0; hh < GT; ++hh)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[hh][e] = 0.f;
+      for (int e = 0; e < W::VW; ++e) acc[hh][e] = 0.f;
     wave_lds_sync();
     w.template values<kDepthSplit>(acc, vb, s);
   } else {
 #pragma unroll
     for (int hh = 0; hh < GT; ++hh)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[hh][e] = 0.f;
+      for (int e = 0; e < W::VW; ++e) acc[hh][e] = 0.f;
   }
   combine_waves<DT, D, GT, true>(p, acc, m_w, l_w, lds + static_cast<size_t>(p.chunk) * W::GTP,
                                  row0, nact, part);
@@ -763,7 +810,10 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(AttnParams p) {
     for (int d = tid; d < D; d += kThreads) out[d] = 0;
     return;
   }
-  const int64_t base = static_cast<int64_t>(pair) * p.num_parts;
+  // partition k of (seq, head) sits in workspace row (seq * nP + k) * Hq + head
+  const int64_t base = static_cast<int64_t>(seq) * p.num_parts * p.num_q_heads +
+                       (pair - seq * p.num_q_heads);
+  const int64_t kstride = p.num_q_heads;
   const float* pm = p.part_max + base;
   const float* ps = p.part_sum + base;
   const float4* pa = reinterpret_cast<const float4*>(p.part_acc + base * D);
@@ -774,15 +824,16 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(AttnParams p) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int k = k0 + row + r * ROWS;
-      x[r] = k < np ? pa[static_cast<int64_t>(k) * C4 + col] : make_float4(0.f, 0.f, 0.f, 0.f);
+      x[r] = k < np ? pa[static_cast<int64_t>(k) * kstride * C4 + col]
+                    : make_float4(0.f, 0.f, 0.f, 0.f);
     }
   };
   load_batch(0);
   // maxima: thread t < 64 keeps m_t and l_t of the first batch
-  const float m0 = tid < np ? pm[tid] : -__builtin_inff();
-  const float l0 = tid < np ? ps[tid] : 0.f;
+  const float m0 = tid < np ? pm[tid * kstride] : -__builtin_inff();
+  const float l0 = tid < np ? ps[tid * kstride] : 0.f;
   float m = m0;
-  for (int k = tid + kThreads; k < np; k += kThreads) m = fmaxf(m, pm[k]);
+  for (int k = tid + kThreads; k < np; k += kThreads) m = fmaxf(m, pm[k * kstride]);
   m = wave_max_all(m);
   if (lane == 0) s_m[wave] = m;
   __syncthreads();
@@ -795,8 +846,8 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(AttnParams p) {
       const int k = k0 + tid;
       float wk = 0.f;
       if (k < np) {
-        const float mk = k0 == 0 ? m0 : pm[k];
-        const float lk = k0 == 0 ? l0 : ps[k];
+        const float mk = k0 == 0 ? m0 : pm[k * kstride];
+        const float lk = k0 == 0 ? l0 : ps[k * kstride];
         wk = fast_exp2(mk - M);
         l += wk * lk;
       }
@@ -849,7 +900,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(AttnParams p) {
 template <int DT, int D, int GT>
 int launch_attn_gt(int kind, const AttnParams& p, hipStream_t stream, hipEvent_t start,
                    hipEvent_t stop) {
-  using TL = Tile<D, GT>;
+  using TL = Tile<D, GT, kNarrow<GT>>;
   const dim3 block(kThreads);
   const int nkv = p.num_kv_heads * p.head_chunks;
   if (kind == 0) {

@@ -21,9 +21,9 @@ struct AttnParams {
   const void* v_cache;
   const int32_t* block_tables;  // [S][mb]
   const int32_t* context_lens;  // [S]
-  float* part_acc;            // [S][Hq][nP_max][D]   (split-context only)
-  float* part_max;            // [S][Hq][nP_max]
-  float* part_sum;            // [S][Hq][nP_max]
+  float* part_acc;            // [S][nP_max][Hq][D]   (split-context only)
+  float* part_max;            // [S][nP_max][Hq]
+  float* part_sum;            // [S][nP_max][Hq]
   int64_t block_stride;       // elements per physical block = bs * Hkv * D
   int32_t mb;                 // row stride of block_tables
   int32_t num_seqs;
