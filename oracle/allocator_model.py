@@ -45,6 +45,9 @@ class BlockManagerModel:
         self.num_tokens = {}    # seq_id -> tokens held
         self.refcount = [0] * num_blocks
 
+    def _take_free(self):
+        return self.free_blocks.pop(0)
+
     # -- growth ----------------------------------------------------------------
     def allocate(self, seq_id, num_tokens):
         table = self.tables.get(seq_id, [])
@@ -57,7 +60,7 @@ class BlockManagerModel:
         if len(self.free_blocks) < needed:
             raise OOM("not enough free blocks")
         for _ in range(needed):
-            block = self.free_blocks.pop(0)
+            block = self._take_free()
             self.refcount[block] = 1
             table.append(block)
         self.tables[seq_id] = table
@@ -78,7 +81,7 @@ class BlockManagerModel:
             table = self.tables[seq_id]
         elif need_cow:
             old = table[idx]
-            new = self.free_blocks.pop(0)
+            new = self._take_free()
             self.refcount[old] -= 1
             self.refcount[new] = 1
             table[idx] = new
@@ -136,3 +139,119 @@ class BlockManagerModel:
 
     def num_free(self):
         return len(self.free_blocks)
+
+
+class PrefixCachingBlockManagerModel(BlockManagerModel):
+    """The block manager with automatic prefix caching, as the pages describe
+    it: page "LLM推理优化：vLLM PagedAttention深度解析与工程实践", §4.2 (a block
+    whose KV equals the same prefix of an earlier request is reused), and the
+    Qwen2.5-7B vLLM 0.6.3 deployment page, §3.2 (prompts are cut into
+    fixed-size blocks, each block keyed by a hash of its token ids; a hit needs
+    a token-exact prefix that ends on a block boundary, so a change in the
+    first block loses every later one).
+
+    The cache is written here by its definition, not by hashing: the key of
+    the i-th full block of a prompt is the tuple of ALL prompt tokens up to
+    the end of that block, which is exactly what a chained block hash stands
+    for, with no possible collision.
+
+    Readings where the pages are silent (each stated, none of them theirs):
+
+    * only full blocks are cached; a prompt's full blocks are registered when
+      the prompt is allocated (its prefill writes them before anything later
+      in the stream can read them);
+    * the longest cached prefix is reused, but never the block that holds the
+      prompt's last token: that token's query is needed for the next token,
+      so at least one token is always computed, into a block the sequence
+      owns;
+    * a block whose count falls to zero stays cached while it waits in the
+      free pool, and loses its cache entry only when the pool hands it out
+      again; a hit on such a block takes it out of the pool;
+    * a cached block keeps its entry when a block of a shorter prefix loses
+      its own (its KV still belongs to the same tokens); the walk stops at
+      the first block that is not cached, so such a block is reused again
+      once the shorter prefix is cached anew;
+    * a key that is already cached keeps its block (a duplicate block of the
+      same prefix is simply not registered);
+    * with caching on, a freed sequence returns its blocks to the pool tail
+      deepest first (reverse table order), so that the ends of cached
+      prefixes are handed out before their beginnings.
+    """
+
+    def __init__(self, num_blocks, block_size, initial_free_order=None, prefix_caching=True):
+        super().__init__(num_blocks, block_size, initial_free_order)
+        self.prefix_caching = bool(prefix_caching)
+        self.cached = {}        # tuple(prompt tokens up to the end of a block) -> block id
+        self.block_key = {}     # block id -> its key, for cached blocks
+
+    def set_prefix_caching(self, enabled):
+        """Turning caching off (or on again) forgets every cached block."""
+        self.prefix_caching = bool(enabled)
+        self.cached = {}
+        self.block_key = {}
+
+    def _forget(self, block):
+        key = self.block_key.pop(block, None)
+        if key is not None:
+            del self.cached[key]
+
+    def _take_free(self):
+        block = self.free_blocks.pop(0)
+        self._forget(block)
+        return block
+
+    def cached_prefix_blocks(self, tokens):
+        """Cached blocks for the longest reusable block-aligned prefix."""
+        tokens = list(tokens)
+        bs = self.block_size
+        hits = []
+        if not self.prefix_caching:
+            return hits
+        for i in range((len(tokens) - 1) // bs if tokens else 0):
+            key = tuple(tokens[: (i + 1) * bs])
+            if key not in self.cached:
+                break
+            hits.append(self.cached[key])
+        return hits
+
+    def allocate_prompt(self, seq_id, tokens):
+        """New sequence holding the prompt; returns the number of leading
+        tokens whose KV is already cached (a multiple of block_size)."""
+        tokens = [int(t) for t in tokens]
+        if seq_id in self.tables:
+            raise ValueError("sequence already exists")
+        bs = self.block_size
+        n = len(tokens)
+        hits = self.cached_prefix_blocks(tokens)
+        fresh = -(-n // bs) - len(hits)
+        taken_from_pool = fresh + sum(1 for b in hits if self.refcount[b] == 0)
+        if taken_from_pool > len(self.free_blocks):
+            raise OOM("not enough free blocks")
+        for b in hits:
+            if self.refcount[b] == 0:
+                self.free_blocks.remove(b)
+            self.refcount[b] += 1
+        table = list(hits)
+        for _ in range(fresh):
+            b = self._take_free()
+            self.refcount[b] = 1
+            table.append(b)
+        if self.prefix_caching:
+            for i in range(len(hits), n // bs):
+                key = tuple(tokens[: (i + 1) * bs])
+                if key not in self.cached:
+                    self.cached[key] = table[i]
+                    self.block_key[table[i]] = key
+        self.tables[seq_id] = table
+        self.num_tokens[seq_id] = n
+        return len(hits) * bs
+
+    def free(self, seq_id):
+        if not self.prefix_caching:
+            return super().free(seq_id)
+        for block_id in reversed(self.tables.get(seq_id, [])):
+            self.refcount[block_id] -= 1
+            if self.refcount[block_id] == 0:
+                self.free_blocks.append(block_id)
+        self.tables.pop(seq_id, None)
+        self.num_tokens.pop(seq_id, None)

@@ -44,3 +44,34 @@ def test_planted_mistake_is_caught(tmp_path, name, old, new, selector):
                         os.path.join(ROOT, "tests", "test_oracle_pins.py"), "-k", selector],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode == 1, f"planted mistake '{name}' survived the pins:\n{r.stdout[-2000:]}"
+
+
+MODEL_SRC = os.path.join(ROOT, "oracle", "allocator_model.py")
+
+# (name, exact source text, planted replacement, occurrences of the anchor)
+MODEL_MUTATIONS = [
+    ("prefix key not chained", "key = tuple(tokens[: (i + 1) * bs])",
+     "key = tuple(tokens[i * bs: (i + 1) * bs])", 2),
+    ("last-token block reused", "range((len(tokens) - 1) // bs if tokens else 0)",
+     "range(len(tokens) // bs)", 1),
+    ("hit left in the pool", "self.free_blocks.remove(b)", "pass", 1),
+    ("handed-out block stays cached", "        self._forget(block)\n", "        pass\n", 1),
+    ("free in table order", "reversed(self.tables.get(seq_id, []))",
+     "self.tables.get(seq_id, [])", 1),
+    ("pool check ignores hits", "taken_from_pool = fresh + sum(", "taken_from_pool = fresh + 0 * sum(", 1),
+    ("duplicate key overwritten", "                if key not in self.cached:\n",
+     "                if True:\n", 1),
+]
+
+
+@pytest.mark.parametrize("name,old,new,count", MODEL_MUTATIONS, ids=[m[0] for m in MODEL_MUTATIONS])
+def test_planted_model_mistake_is_caught(tmp_path, name, old, new, count):
+    src = open(MODEL_SRC).read()
+    assert src.count(old) == count, f"mutation anchor for '{name}' not found {count} time(s)"
+    mutant = tmp_path / "allocator_model.py"
+    mutant.write_text(src.replace(old, new))
+    env = dict(os.environ, PA_ALLOC_MODEL_PATH=str(mutant))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_prefix_cache_pins.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode == 1, f"planted mistake '{name}' survived the pins:\n{r.stdout[-2000:]}"
