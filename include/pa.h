@@ -321,9 +321,47 @@ pa_status pa_alloc_share_prefix(pa_allocator* a, int64_t src_seq,
  * last block included) and holds as many tokens. */
 pa_status pa_alloc_fork(pa_allocator* a, int64_t src_seq, int64_t dst_seq);
 
-/* Drop seq_id: each of its blocks loses a reference, in table order, and
- * goes to the tail of the free pool when no reference is left. */
+/* Drop seq_id: each of its blocks loses a reference, in table order
+ * (reverse table order while prefix caching is on), and goes to the tail of
+ * the free pool when no reference is left. */
 pa_status pa_alloc_free(pa_allocator* a, int64_t seq_id);
+
+/* Automatic prefix caching.
+ * Follows: "LLM推理优化：vLLM PagedAttention深度解析与工程实践", §4.2 (KV
+ * blocks of a prefix that an earlier request already holds are reused), and
+ * the Qwen2.5-7B vLLM 0.6.3 deployment page, §3.2 (a prompt is cut into
+ * fixed-size blocks, each keyed by its token ids chained to the blocks before
+ * it; a hit needs the same tokens, block-aligned, from the first token on).
+ * Off by default.  Turning it on or off forgets every cached block.  While
+ * on, the host memory it costs is block_size + 4 int32 per physical block
+ * plus one index entry per cached block (the first page, §六 pitfall 4: the
+ * table is worth its memory only when prompts share prefixes).
+ * PA_ERR_OOM if that memory cannot be had. */
+pa_status pa_alloc_set_prefix_caching(pa_allocator* a, int32_t enabled);
+
+/* Create sequence seq_id (PA_ERR_INVALID_ARG if it exists) holding the
+ * prompt tokens[0..num_tokens) (int32 token ids, host memory; read only
+ * during the call) in ceil(num_tokens / block_size) blocks.
+ * With prefix caching on, the longest cached block-aligned prefix of the
+ * prompt is reused (its blocks gain a reference; a cached block waiting in
+ * the free pool is taken out of it), never including the block that holds
+ * the last prompt token; the other blocks come from the pool head (a cached
+ * block handed out this way leaves the cache).  The prompt's full blocks
+ * that were not reused are then cached, unless their prefix is cached
+ * already.  *cached_tokens_out (may be NULL) = tokens whose K/V is already in
+ * the cache, a multiple of block_size: the caller writes K/V only for
+ * positions [*cached_tokens_out, num_tokens), whose slots pa_alloc_slots
+ * gives.  Cached blocks must hold the K/V of their tokens before a later
+ * prompt reuses them: write them in stream order before any later read.
+ * PA_ERR_OOM (nothing changed) when the pool cannot supply the blocks not
+ * reused plus the reused ones that wait in the pool.  With caching off this
+ * is pa_alloc_allocate on a new sequence, with *cached_tokens_out = 0. */
+pa_status pa_alloc_allocate_prompt(pa_allocator* a, int64_t seq_id,
+                                   const int32_t* tokens, int32_t num_tokens,
+                                   int32_t* cached_tokens_out);
+
+/* Blocks currently cached (held or waiting in the free pool), or -1. */
+int32_t pa_alloc_num_cached_blocks(const pa_allocator* a);
 
 /* Copy seq_id's block table (physical ids in logical order) to out[0..cap);
  * *n_out = number of blocks (PA_ERR_INVALID_ARG if cap is too small). */

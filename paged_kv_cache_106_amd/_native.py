@@ -73,6 +73,9 @@ _sig("pa_write_step", _i32, [_vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _vp,
 _sig("pa_alloc_share_prefix", _i32, [_vp, _i64, _i64, _i32])
 _sig("pa_alloc_fork", _i32, [_vp, _i64, _i64])
 _sig("pa_alloc_free", _i32, [_vp, _i64])
+_sig("pa_alloc_set_prefix_caching", _i32, [_vp, _i32])
+_sig("pa_alloc_allocate_prompt", _i32, [_vp, _i64, _i32p, _i32, _i32p])
+_sig("pa_alloc_num_cached_blocks", _i32, [_vp])
 _sig("pa_alloc_block_table", _i32, [_vp, _i64, _i32p, _i32, _i32p])
 _sig("pa_alloc_block_tables", _i32, [_vp, _i64p, _i32, _i32p, _i32, _i32, _i32p])
 _sig("pa_alloc_slots", _i32, [_vp, _i64, _i32, _i32, _i64p])
@@ -290,7 +293,7 @@ def _np_ptr(a, ctype):
 class Allocator:
     """Owns one pa_allocator handle; each method is one pa_alloc_* call."""
 
-    def __init__(self, num_blocks, block_size, initial_free_order=None):
+    def __init__(self, num_blocks, block_size, initial_free_order=None, prefix_caching=False):
         self.num_blocks = int(num_blocks)
         self.block_size = int(block_size)
         h = _vp()
@@ -302,6 +305,8 @@ class Allocator:
             order = _np_ptr(self._order, ctypes.c_int32)
         _check(_lib.pa_alloc_create(self.num_blocks, self.block_size, order, ctypes.byref(h)))
         self._h = h
+        if prefix_caching:
+            self.set_prefix_caching(True)
 
     def close(self):
         if getattr(self, "_h", None) and _lib is not None:
@@ -345,6 +350,21 @@ class Allocator:
 
     def free(self, seq_id):
         _check(_lib.pa_alloc_free(self._h, int(seq_id)))
+
+    def set_prefix_caching(self, enabled):
+        _check(_lib.pa_alloc_set_prefix_caching(self._h, 1 if enabled else 0))
+
+    def allocate_prompt(self, seq_id, tokens):
+        """New sequence holding the prompt; returns the number of leading
+        tokens whose K/V the prefix cache already holds."""
+        ids = np.ascontiguousarray(tokens, dtype=np.int32).reshape(-1)
+        cached = ctypes.c_int32()
+        _check(_lib.pa_alloc_allocate_prompt(self._h, int(seq_id), _np_ptr(ids, ctypes.c_int32),
+                                             ids.shape[0], ctypes.byref(cached)))
+        return cached.value
+
+    def num_cached_blocks(self):
+        return int(_lib.pa_alloc_num_cached_blocks(self._h))
 
     def block_table(self, seq_id):
         n = ctypes.c_int32()

@@ -5,14 +5,31 @@
 // checked before any block is taken) with the sharing rules of
 // "vLLM 深度拆解：当大模型推理学会「分页注意力」", §3.3 (append_slot into the
 // current block or a fresh one, free returns blocks, shared blocks are
-// referenced and copied only before a sharer writes into one).
+// referenced and copied only before a sharer writes into one), and automatic
+// prefix caching (the first page, §4.2; the Qwen2.5-7B vLLM 0.6.3 deployment
+// page, §3.2): a prompt's full blocks are keyed by their token ids chained to
+// the key of the block before them, and a later prompt with the same
+// block-aligned token prefix reuses them.
 //
 // Data structures, sized once at creation:
-//   free pool   ring buffer of num_blocks ids: pop at head, push at tail, O(1)
+//   free pool   intrusive doubly linked list over block ids (next/prev
+//               arrays): pop at head, push at tail, unlink from the middle
+//               (a cached block taken back out of the pool), all O(1)
 //   refcount    one int32 per physical block (0 <=> the block is in the pool)
 //   sequences   hash map seq_id -> {block ids in logical order, token count}
+//   prefix      per block: node id (0: not cached), parent node id, its
+//   cache       block_size token ids; a hash index (parent node, tokens) ->
+//               block, every hit verified token by token, so a match is
+//               exact whatever the hash does
 // Every failing call returns before changing anything.
-
+//
+// Why node ids and not content hashes: a cached block's key names its parent
+// by the node id the parent got when it was cached, so equal keys mean equal
+// token prefixes, with no collision possible.  The keys stay valid because
+// the cached prefixes are closed under shortening: a block is only ever held
+// together with the blocks of its prefix, and frees return a sequence's
+// blocks deepest first, so a parent never goes back out of the pool before
+// its cached children.
 #include <algorithm>
 #include <cstdint>
 #include <cstring>
@@ -28,9 +45,9 @@
 struct pa_allocator {
   int32_t num_blocks = 0;
   int32_t block_size = 0;
-  std::vector<int32_t> ring;  // free pool storage
-  int64_t head = 0;           // index of the pool's first id in ring
-  int64_t count = 0;          // ids in the pool
+  std::vector<int32_t> next, prev;  // free pool links, -1 at the ends
+  int32_t head = -1, tail = -1;
+  int64_t count = 0;                // ids in the pool
   std::vector<int32_t> refcount;
   struct Seq {
     std::vector<int32_t> blocks;
@@ -38,16 +55,86 @@ struct pa_allocator {
   };
   std::unordered_map<int64_t, Seq> seqs;
 
-  int32_t pop_front() {
-    const int32_t id = ring[static_cast<size_t>(head)];
-    head = (head + 1) % num_blocks;
+  // prefix cache (arrays sized when caching is first turned on)
+  bool caching = false;
+  uint64_t next_node = 1;
+  std::vector<uint64_t> node;        // node id of a cached block, 0 if not cached
+  std::vector<uint64_t> parent;      // node id of the block before it (0: first block)
+  std::vector<int32_t> cached_ids;   // [num_blocks][block_size] token ids
+  std::unordered_multimap<uint64_t, int32_t> index;
+
+  void unlink(int32_t id) {
+    const int32_t p = prev[static_cast<size_t>(id)], n = next[static_cast<size_t>(id)];
+    if (p >= 0) next[static_cast<size_t>(p)] = n; else head = n;
+    if (n >= 0) prev[static_cast<size_t>(n)] = p; else tail = p;
     --count;
-    return id;
   }
   void push_back(int32_t id) {
-    ring[static_cast<size_t>((head + count) % num_blocks)] = id;
+    prev[static_cast<size_t>(id)] = tail;
+    next[static_cast<size_t>(id)] = -1;
+    if (tail >= 0) next[static_cast<size_t>(tail)] = id; else head = id;
+    tail = id;
     ++count;
   }
+  // take the pool's first block; a cached block leaves the cache as it goes
+  int32_t pop_front() {
+    const int32_t id = head;
+    unlink(id);
+    forget(id);
+    return id;
+  }
+
+  // mixing step of SplitMix64 (Steele, Lea and Flood, "Fast splittable
+  // pseudorandom number generators", OOPSLA 2014); only spreads the index
+  static uint64_t mix(uint64_t x) {
+    x ^= x >> 30;
+    x *= 0xbf58476d1ce4e5b9ULL;
+    x ^= x >> 27;
+    x *= 0x94d049bb133111ebULL;
+    return x ^ (x >> 31);
+  }
+  uint64_t key_hash(uint64_t parent_node, const int32_t* ids) const {
+    uint64_t h = mix(parent_node + 0x9e3779b97f4a7c15ULL);
+    for (int32_t i = 0; i < block_size; ++i) h = mix(h ^ static_cast<uint32_t>(ids[i]));
+    return h;
+  }
+  const int32_t* ids_of(int32_t b) const {
+    return cached_ids.data() + static_cast<size_t>(b) * static_cast<size_t>(block_size);
+  }
+  // the cached block whose prefix is (parent_node's prefix, ids), or -1
+  int32_t lookup(uint64_t parent_node, const int32_t* ids) const {
+    auto range = index.equal_range(key_hash(parent_node, ids));
+    for (auto it = range.first; it != range.second; ++it) {
+      const int32_t b = it->second;
+      if (parent[static_cast<size_t>(b)] == parent_node &&
+          std::memcmp(ids_of(b), ids, sizeof(int32_t) * static_cast<size_t>(block_size)) == 0)
+        return b;
+    }
+    return -1;
+  }
+  void remember(int32_t b, uint64_t parent_node, const int32_t* ids) {
+    node[static_cast<size_t>(b)] = next_node++;
+    parent[static_cast<size_t>(b)] = parent_node;
+    std::memcpy(cached_ids.data() + static_cast<size_t>(b) * static_cast<size_t>(block_size), ids,
+                sizeof(int32_t) * static_cast<size_t>(block_size));
+    index.emplace(key_hash(parent_node, ids), b);
+  }
+  void forget(int32_t b) {
+    if (node.empty() || node[static_cast<size_t>(b)] == 0) return;
+    auto range = index.equal_range(key_hash(parent[static_cast<size_t>(b)], ids_of(b)));
+    for (auto it = range.first; it != range.second; ++it) {
+      if (it->second == b) {
+        index.erase(it);
+        break;
+      }
+    }
+    node[static_cast<size_t>(b)] = 0;
+  }
+  void forget_all() {
+    index.clear();
+    std::fill(node.begin(), node.end(), uint64_t{0});
+  }
+
   int64_t capacity_of(const Seq& s) const {
     return static_cast<int64_t>(s.blocks.size()) * block_size;
   }
@@ -114,7 +201,8 @@ pa_status pa_alloc_create(int32_t num_blocks, int32_t block_size,
   if (!a) return pa::fail(PA_ERR_OOM, "pa_alloc_create: host allocation failed");
   a->num_blocks = num_blocks;
   a->block_size = block_size;
-  a->ring.resize(static_cast<size_t>(num_blocks));
+  a->next.assign(static_cast<size_t>(num_blocks), -1);
+  a->prev.assign(static_cast<size_t>(num_blocks), -1);
   a->refcount.assign(static_cast<size_t>(num_blocks), 0);
   if (initial_free_order) {
     std::vector<char> seen(static_cast<size_t>(num_blocks), 0);
@@ -125,13 +213,11 @@ pa_status pa_alloc_create(int32_t num_blocks, int32_t block_size,
         return invalid("pa_alloc_create: initial_free_order is not a permutation");
       }
       seen[static_cast<size_t>(id)] = 1;
-      a->ring[static_cast<size_t>(i)] = id;
     }
+    for (int32_t i = 0; i < num_blocks; ++i) a->push_back(initial_free_order[i]);
   } else {
-    for (int32_t i = 0; i < num_blocks; ++i) a->ring[static_cast<size_t>(i)] = i;
+    for (int32_t i = 0; i < num_blocks; ++i) a->push_back(i);
   }
-  a->head = 0;
-  a->count = num_blocks;
   *out = a;
   return PA_OK;
 }
@@ -228,7 +314,11 @@ pa_status pa_alloc_free(pa_allocator* a, int64_t seq_id) {
   if (!a) return invalid("pa_alloc_free: allocator is NULL");
   auto it = a->seqs.find(seq_id);
   if (it == a->seqs.end()) return PA_OK;
-  for (int32_t id : it->second.blocks) {
+  const std::vector<int32_t>& blocks = it->second.blocks;
+  const size_t nb = blocks.size();
+  for (size_t k = 0; k < nb; ++k) {
+    // with caching on, deepest block first: a cached prefix leaves the pool end first
+    const int32_t id = blocks[a->caching ? nb - 1 - k : k];
     int32_t& rc = a->refcount[static_cast<size_t>(id)];
     rc -= 1;
     if (rc == 0) a->push_back(id);
@@ -308,9 +398,88 @@ pa_status pa_alloc_free_list(const pa_allocator* a, int32_t* out, int32_t cap, i
   *n_out = static_cast<int32_t>(a->count);
   if (a->count > cap || (a->count > 0 && !out))
     return invalid("pa_alloc_free_list: output too small");
-  for (int64_t k = 0; k < a->count; ++k)
-    out[k] = a->ring[static_cast<size_t>((a->head + k) % a->num_blocks)];
+  int64_t k = 0;
+  for (int32_t id = a->head; id >= 0; id = a->next[static_cast<size_t>(id)]) out[k++] = id;
   return PA_OK;
+}
+
+pa_status pa_alloc_set_prefix_caching(pa_allocator* a, int32_t enabled) {
+  pa::clear_error();
+  if (!a) return invalid("pa_alloc_set_prefix_caching: allocator is NULL");
+  if (enabled && a->node.empty()) {
+    const size_t nb = static_cast<size_t>(a->num_blocks);
+    const size_t ids = nb * static_cast<size_t>(a->block_size);
+    try {
+      a->node.assign(nb, 0);
+      a->parent.assign(nb, 0);
+      a->cached_ids.assign(ids, 0);
+    } catch (const std::bad_alloc&) {
+      a->node.clear();
+      a->parent.clear();
+      a->cached_ids.clear();
+      return pa::fail(PA_ERR_OOM, "pa_alloc_set_prefix_caching: host allocation failed");
+    }
+  }
+  a->forget_all();
+  a->caching = enabled != 0;
+  return PA_OK;
+}
+
+pa_status pa_alloc_allocate_prompt(pa_allocator* a, int64_t seq_id, const int32_t* tokens,
+                                   int32_t num_tokens, int32_t* cached_tokens_out) {
+  pa::clear_error();
+  if (!a) return invalid("pa_alloc_allocate_prompt: allocator is NULL");
+  if (num_tokens < 0 || (num_tokens > 0 && !tokens))
+    return invalid("pa_alloc_allocate_prompt: bad token array");
+  if (find(a, seq_id)) return invalid("pa_alloc_allocate_prompt: sequence exists");
+  const int32_t bs = a->block_size;
+  const int64_t nblk = (static_cast<int64_t>(num_tokens) + bs - 1) / bs;
+  // longest cached block-aligned prefix, short of the block holding the last token
+  std::vector<int32_t> hits;
+  uint64_t chain = 0;
+  if (a->caching && num_tokens > 0) {
+    const int64_t cap = (static_cast<int64_t>(num_tokens) - 1) / bs;
+    for (int64_t i = 0; i < cap; ++i) {
+      const int32_t b = a->lookup(chain, tokens + i * bs);
+      if (b < 0) break;
+      hits.push_back(b);
+      chain = a->node[static_cast<size_t>(b)];
+    }
+  }
+  int64_t from_pool = nblk - static_cast<int64_t>(hits.size());
+  for (int32_t b : hits) from_pool += a->refcount[static_cast<size_t>(b)] == 0 ? 1 : 0;
+  if (from_pool > a->count)
+    return pa::fail(PA_ERR_OOM, "pa_alloc_allocate_prompt: not enough free blocks");
+  pa_allocator::Seq& s = a->seqs[seq_id];
+  s.blocks.reserve(static_cast<size_t>(nblk));
+  for (int32_t b : hits) {
+    int32_t& rc = a->refcount[static_cast<size_t>(b)];
+    if (rc == 0) a->unlink(b);
+    rc += 1;
+    s.blocks.push_back(b);
+  }
+  for (int64_t k = static_cast<int64_t>(hits.size()); k < nblk; ++k) {
+    const int32_t id = a->pop_front();
+    a->refcount[static_cast<size_t>(id)] = 1;
+    s.blocks.push_back(id);
+  }
+  // cache the prompt's other full blocks; a prefix cached already keeps its block
+  if (a->caching) {
+    for (int64_t i = static_cast<int64_t>(hits.size()); i < num_tokens / bs; ++i) {
+      const int32_t* ids = tokens + i * bs;
+      const int32_t have = a->lookup(chain, ids);
+      const int32_t b = have >= 0 ? have : s.blocks[static_cast<size_t>(i)];
+      if (have < 0) a->remember(b, chain, ids);
+      chain = a->node[static_cast<size_t>(b)];
+    }
+  }
+  s.tokens = num_tokens;
+  if (cached_tokens_out) *cached_tokens_out = static_cast<int32_t>(hits.size()) * bs;
+  return PA_OK;
+}
+
+int32_t pa_alloc_num_cached_blocks(const pa_allocator* a) {
+  return a ? static_cast<int32_t>(a->index.size()) : -1;
 }
 
 pa_status pa_partition_work_items(const int32_t* context_lens, int32_t num_seqs,

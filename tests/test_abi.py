@@ -152,7 +152,7 @@ def test_partition_work_items_random():
 
 
 def test_workspace_size_formula():
-    # [S][Hq][nP][D] fp32 accumulators + [S][Hq][nP] max + [S][Hq][nP] sum, 256-byte aligned parts
+    # [S][nP][Hq][D] fp32 accumulators + [S][nP][Hq] max + [S][nP][Hq] sum, 256-byte aligned parts
     S, Hq, D, maxlen, P = 64, 28, 128, 32768, 512
     nP = -(-maxlen // P)
     rows = S * Hq * nP
