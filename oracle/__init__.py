@@ -72,6 +72,19 @@ def lib():
         L.pao_decode.restype = i32
         L.pao_decode_partitioned.argtypes = [f32p, u16p] + common + [i32]
         L.pao_decode_partitioned.restype = i32
+        i8p = ctypes.POINTER(ctypes.c_int8)
+        L.pao_quantize_rows.argtypes = [u16p, i64, i32, i32, i8p, f32p]
+        L.pao_quantize_rows.restype = i32
+        L.pao_cache_write_int8.argtypes = [u16p, u16p, i8p, i8p, f32p, f32p, i64p, i32, i32, i32,
+                                           i32, i32, i32]
+        L.pao_cache_write_int8.restype = i32
+        L.pao_gather_int8.argtypes = [f32p, f32p, i8p, i8p, f32p, f32p, i32p, i32, i32, i32, i32,
+                                      i32, i32]
+        L.pao_gather_int8.restype = i32
+        L.pao_decode_int8_pairs.argtypes = [f32p, u16p, u16p, i8p, i8p, f32p, f32p, i32p, i32,
+                                            i32p, i32, i32, i32, i32, i32, i32, ctypes.c_float,
+                                            i32, i32p, i32, i32]
+        L.pao_decode_int8_pairs.restype = i32
         L.pao_kv_bytes_per_token.argtypes = [i32, i32, i32, i32]
         L.pao_kv_bytes_per_token.restype = ctypes.c_uint64
         L.pao_kv_bytes_gathered.argtypes = [i32p, i32, i32, i32, i32]
@@ -225,6 +238,89 @@ def decode_partitioned(q, key_cache, value_cache, block_tables, context_lens, sc
         _ptr(key_cache, ctypes.c_uint16), _ptr(value_cache, ctypes.c_uint16),
         _ptr(block_tables, ctypes.c_int32), mb, _ptr(context_lens, ctypes.c_int32),
         s, hq, hkv, d, bs, nb, float(scale), DTYPES[dtype], int(partition_size)))
+    return out_f32, out_t
+
+
+# -- INT8 KV cache ------------------------------------------------------------------------
+# codes int8 [nb][bs][hkv][d]; scales float32 [nb][hkv][bs]
+
+def quantize_rows(x_bits, dtype):
+    """Rows [..., d] of 16-bit patterns -> (int8 codes [..., d], float32 scales [...])."""
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    d = x.shape[-1]
+    rows = x.size // d
+    codes = np.empty(x.shape, np.int8)
+    scales = np.empty(x.shape[:-1], np.float32)
+    _check(lib().pao_quantize_rows(_ptr(x, ctypes.c_uint16), rows, d, DTYPES[dtype],
+                                   _ptr(codes, ctypes.c_int8), _ptr(scales, ctypes.c_float)))
+    return codes, scales
+
+
+def cache_write_int8(key, value, key_cache, value_cache, key_scale, value_scale, slot_mapping,
+                     dtype):
+    """Quantise each token's K/V rows into its slot of the INT8 pools (in place)."""
+    _need(key, np.uint16, "key"); _need(value, np.uint16, "value")
+    _need(key_cache, np.int8, "key_cache"); _need(value_cache, np.int8, "value_cache")
+    _need(key_scale, np.float32, "key_scale"); _need(value_scale, np.float32, "value_scale")
+    _need(slot_mapping, np.int64, "slot_mapping")
+    nb, bs, hkv, d = key_cache.shape
+    n = slot_mapping.shape[0]
+    if (key.shape != (n, hkv, d) or value.shape != (n, hkv, d) or
+            value_cache.shape != key_cache.shape or key_scale.shape != (nb, hkv, bs) or
+            value_scale.shape != (nb, hkv, bs)):
+        raise ValueError("shape mismatch")
+    _check(lib().pao_cache_write_int8(
+        _ptr(key, ctypes.c_uint16), _ptr(value, ctypes.c_uint16),
+        _ptr(key_cache, ctypes.c_int8), _ptr(value_cache, ctypes.c_int8),
+        _ptr(key_scale, ctypes.c_float), _ptr(value_scale, ctypes.c_float),
+        _ptr(slot_mapping, ctypes.c_int64), n, hkv, d, bs, nb, DTYPES[dtype]))
+
+
+def gather_int8(key_cache, value_cache, key_scale, value_scale, block_table_row, L, g):
+    nb, bs, hkv, d = key_cache.shape
+    row = np.ascontiguousarray(block_table_row, dtype=np.int32)
+    k = np.empty((L, d), np.float32)
+    v = np.empty((L, d), np.float32)
+    _check(lib().pao_gather_int8(
+        _ptr(k, ctypes.c_float), _ptr(v, ctypes.c_float), _ptr(key_cache, ctypes.c_int8),
+        _ptr(value_cache, ctypes.c_int8), _ptr(key_scale, ctypes.c_float),
+        _ptr(value_scale, ctypes.c_float), _ptr(row, ctypes.c_int32), L, g, hkv, d, bs, nb))
+    return k, v
+
+
+def decode_int8(q, key_cache, value_cache, key_scale, value_scale, block_tables, context_lens,
+                scale, dtype, pairs=None, nthreads=1):
+    """fp32 decode over the INT8 cache, rows dequantised as scale x code.
+    pairs None: every (sequence, q head), outputs [S][Hq][D]; else [n][D]."""
+    _need(q, np.uint16, "q"); _need(key_cache, np.int8, "key_cache")
+    _need(value_cache, np.int8, "value_cache"); _need(key_scale, np.float32, "key_scale")
+    _need(value_scale, np.float32, "value_scale")
+    _need(block_tables, np.int32, "block_tables"); _need(context_lens, np.int32, "context_lens")
+    s, hq, d = q.shape
+    nb, bs, hkv, d2 = key_cache.shape
+    if (d2 != d or value_cache.shape != key_cache.shape or key_scale.shape != (nb, hkv, bs) or
+            value_scale.shape != key_scale.shape):
+        raise ValueError("shape mismatch")
+    if block_tables.shape[0] != s or context_lens.shape != (s,):
+        raise ValueError("metadata shape mismatch")
+    mb = block_tables.shape[1]
+    shape = None
+    if pairs is None:
+        pairs = np.stack(np.meshgrid(np.arange(s), np.arange(hq), indexing="ij"), -1)
+        shape = (s, hq, d)
+    pairs = np.ascontiguousarray(pairs, dtype=np.int32).reshape(-1, 2)
+    n = pairs.shape[0]
+    out_f32 = np.empty((n, d), np.float32)
+    out_t = np.empty((n, d), np.uint16)
+    _check(lib().pao_decode_int8_pairs(
+        _ptr(out_f32, ctypes.c_float), _ptr(out_t, ctypes.c_uint16), _ptr(q, ctypes.c_uint16),
+        _ptr(key_cache, ctypes.c_int8), _ptr(value_cache, ctypes.c_int8),
+        _ptr(key_scale, ctypes.c_float), _ptr(value_scale, ctypes.c_float),
+        _ptr(block_tables, ctypes.c_int32), mb, _ptr(context_lens, ctypes.c_int32),
+        s, hq, hkv, d, bs, nb, float(scale), DTYPES[dtype], _ptr(pairs, ctypes.c_int32), n,
+        int(nthreads)))
+    if shape is not None:
+        return out_f32.reshape(shape), out_t.reshape(shape)
     return out_f32, out_t
 
 

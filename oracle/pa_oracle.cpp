@@ -195,19 +195,9 @@ int32_t pao_gather(float* k_out, float* v_out, const uint16_t* key_cache,
 // share one kv head.
 // ---------------------------------------------------------------------------
 
-static int32_t decode_one(float* out, const uint16_t* q_row,
-                          const uint16_t* key_cache, const uint16_t* value_cache,
-                          const int32_t* table_row, int32_t mb, int32_t L,
-                          int32_t g, int32_t hkv, int32_t d, int32_t bs,
-                          int32_t nb, float scale, int32_t dtype) {
-  if (L <= 0 || L > static_cast<int64_t>(mb) * bs) return PAO_BAD_LEN;
-  std::vector<float> K(static_cast<size_t>(L) * d), V(static_cast<size_t>(L) * d);
-  const int32_t rc = pao_gather(K.data(), V.data(), key_cache, value_cache,
-                                table_row, L, g, hkv, d, bs, nb, dtype);
-  if (rc != PAO_OK) return rc;
-  std::vector<float> qf(d);
-  for (int32_t e = 0; e < d; ++e) qf[e] = widen(q_row[e], dtype);
-
+// The definition above on gathered rows K, V [L][d] and the widened query.
+static void attend(float* out, const std::vector<float>& qf, const std::vector<float>& K,
+                   const std::vector<float>& V, int32_t L, int32_t d, float scale) {
   std::vector<float> s(L);
   for (int32_t j = 0; j < L; ++j) {
     float acc = 0.0f;
@@ -227,6 +217,21 @@ static int32_t decode_one(float* out, const uint16_t* q_row,
     for (int32_t j = 0; j < L; ++j) acc = acc + w[j] * V[static_cast<size_t>(j) * d + e];
     out[e] = acc / l;
   }
+}
+
+static int32_t decode_one(float* out, const uint16_t* q_row,
+                          const uint16_t* key_cache, const uint16_t* value_cache,
+                          const int32_t* table_row, int32_t mb, int32_t L,
+                          int32_t g, int32_t hkv, int32_t d, int32_t bs,
+                          int32_t nb, float scale, int32_t dtype) {
+  if (L <= 0 || L > static_cast<int64_t>(mb) * bs) return PAO_BAD_LEN;
+  std::vector<float> K(static_cast<size_t>(L) * d), V(static_cast<size_t>(L) * d);
+  const int32_t rc = pao_gather(K.data(), V.data(), key_cache, value_cache,
+                                table_row, L, g, hkv, d, bs, nb, dtype);
+  if (rc != PAO_OK) return rc;
+  std::vector<float> qf(d);
+  for (int32_t e = 0; e < d; ++e) qf[e] = widen(q_row[e], dtype);
+  attend(out, qf, K, V, L, d, scale);
   return PAO_OK;
 }
 
@@ -388,6 +393,154 @@ int32_t pao_decode_partitioned(float* out_f32, uint16_t* out_t,
     }
   }
   return PAO_OK;
+}
+
+// ---------------------------------------------------------------------------
+// INT8 KV cache.  The pages say only that quantising the KV cache to INT8
+// halves its bytes ("LLM推理优化技术地图：从KV Cache到量化与投机解码", §4.3);
+// the convention is this library's: symmetric, one fp32 scale per (token,
+// kv head) row of d elements, all in fp32:
+//   a    = max_e |x_e|                      (x widened exactly)
+//   s    = a / 127
+//   c_e  = clamp(round_half_even(x_e / s), -127, 127),   c = 0 when a = 0
+// and the row dequantises to s * c_e (one fp32 product).  A row holding inf
+// or NaN gets s = NaN and c = 0.  Codes live in the paged pools
+// [nb][bs][hkv][d] (int8); scales in [nb][hkv][bs] (fp32).
+// ---------------------------------------------------------------------------
+
+static void quantize_row(const uint16_t* x, int32_t d, int32_t dtype, int8_t* c, float* s) {
+  float a = 0.0f;
+  bool finite = true;
+  for (int32_t e = 0; e < d; ++e) {
+    const float v = widen(x[e], dtype);
+    if (!std::isfinite(v)) finite = false;
+    a = std::max(a, std::fabs(v));
+  }
+  if (!finite) {
+    *s = std::numeric_limits<float>::quiet_NaN();
+    for (int32_t e = 0; e < d; ++e) c[e] = 0;
+    return;
+  }
+  const float sc = a / 127.0f;
+  *s = sc;
+  for (int32_t e = 0; e < d; ++e) {
+    if (a == 0.0f) {
+      c[e] = 0;
+      continue;
+    }
+    const float r = std::nearbyint(widen(x[e], dtype) / sc);
+    c[e] = static_cast<int8_t>(std::min(127.0f, std::max(-127.0f, r)));
+  }
+}
+
+int32_t pao_quantize_rows(const uint16_t* x, int64_t rows, int32_t d, int32_t dtype,
+                          int8_t* codes, float* scales) {
+  if (rows < 0 || d <= 0 || (dtype != PAO_F16 && dtype != PAO_BF16)) return PAO_BAD_ARG;
+  if (rows > 0 && (!x || !codes || !scales)) return PAO_BAD_ARG;
+  for (int64_t r = 0; r < rows; ++r) quantize_row(x + r * d, d, dtype, codes + r * d, scales + r);
+  return PAO_OK;
+}
+
+int32_t pao_cache_write_int8(const uint16_t* key, const uint16_t* value, int8_t* key_cache,
+                             int8_t* value_cache, float* key_scale, float* value_scale,
+                             const int64_t* slot_mapping, int32_t n, int32_t hkv, int32_t d,
+                             int32_t bs, int32_t nb, int32_t dtype) {
+  if (n < 0 || hkv <= 0 || d <= 0 || bs <= 0 || nb <= 0 ||
+      (dtype != PAO_F16 && dtype != PAO_BF16))
+    return PAO_BAD_ARG;
+  if (n > 0 && (!key || !value || !key_cache || !value_cache || !key_scale || !value_scale ||
+                !slot_mapping))
+    return PAO_BAD_ARG;
+  const int64_t num_slots = static_cast<int64_t>(nb) * bs;
+  std::vector<int64_t> used;
+  for (int32_t t = 0; t < n; ++t) {
+    if (slot_mapping[t] < 0) continue;
+    if (slot_mapping[t] >= num_slots) return PAO_BAD_SLOT;
+    used.push_back(slot_mapping[t]);
+  }
+  std::sort(used.begin(), used.end());
+  if (std::adjacent_find(used.begin(), used.end()) != used.end()) return PAO_DUP_SLOT;
+  for (int32_t t = 0; t < n; ++t) {
+    const int64_t slot = slot_mapping[t];
+    if (slot < 0) continue;
+    const int64_t blk = slot / bs, off = slot % bs;
+    for (int32_t g = 0; g < hkv; ++g) {
+      const int64_t src = (static_cast<int64_t>(t) * hkv + g) * d;
+      const int64_t dst = ((blk * bs + off) * hkv + g) * d;
+      const int64_t sdst = (blk * hkv + g) * bs + off;
+      quantize_row(key + src, d, dtype, key_cache + dst, key_scale + sdst);
+      quantize_row(value + src, d, dtype, value_cache + dst, value_scale + sdst);
+    }
+  }
+  return PAO_OK;
+}
+
+int32_t pao_gather_int8(float* k_out, float* v_out, const int8_t* key_cache,
+                        const int8_t* value_cache, const float* key_scale,
+                        const float* value_scale, const int32_t* block_table_row, int32_t L,
+                        int32_t g, int32_t hkv, int32_t d, int32_t bs, int32_t nb) {
+  if (L <= 0) return PAO_BAD_LEN;
+  if (g < 0 || g >= hkv) return PAO_BAD_ARG;
+  for (int32_t j = 0; j < L; ++j) {
+    const int64_t blk = block_table_row[j / bs];
+    if (blk < 0 || blk >= nb) return PAO_BAD_BLOCK;
+    const int64_t off = j % bs;
+    const int64_t row = ((blk * bs + off) * hkv + g) * d;
+    const float ks = key_scale[(blk * hkv + g) * bs + off];
+    const float vs = value_scale[(blk * hkv + g) * bs + off];
+    for (int32_t e = 0; e < d; ++e) {
+      k_out[static_cast<int64_t>(j) * d + e] = ks * static_cast<float>(key_cache[row + e]);
+      v_out[static_cast<int64_t>(j) * d + e] = vs * static_cast<float>(value_cache[row + e]);
+    }
+  }
+  return PAO_OK;
+}
+
+int32_t pao_decode_int8_pairs(float* out_f32, uint16_t* out_t, const uint16_t* q,
+                              const int8_t* key_cache, const int8_t* value_cache,
+                              const float* key_scale, const float* value_scale,
+                              const int32_t* block_tables, int32_t mb,
+                              const int32_t* context_lens, int32_t s, int32_t hq, int32_t hkv,
+                              int32_t d, int32_t bs, int32_t nb, float scale, int32_t dtype,
+                              const int32_t* pairs, int32_t n_pairs, int32_t nthreads) {
+  if (!shapes_ok(s, hq, hkv, d, bs, nb, mb, dtype) || n_pairs < 0) return PAO_BAD_ARG;
+  for (int32_t p = 0; p < n_pairs; ++p)
+    if (pairs[2 * p] < 0 || pairs[2 * p] >= s || pairs[2 * p + 1] < 0 || pairs[2 * p + 1] >= hq)
+      return PAO_BAD_ARG;
+  const int32_t group = hq / hkv;
+  int32_t T = nthreads > 0 ? nthreads
+                           : static_cast<int32_t>(std::thread::hardware_concurrency());
+  T = std::max(1, std::min(T, std::max(n_pairs, 1)));
+  std::atomic<int32_t> next(0), status(PAO_OK);
+  auto worker = [&]() {
+    for (int32_t p; (p = next.fetch_add(1)) < n_pairs;) {
+      const int32_t i = pairs[2 * p], h = pairs[2 * p + 1];
+      const int32_t L = context_lens[i];
+      if (L <= 0 || L > static_cast<int64_t>(mb) * bs) {
+        status.store(PAO_BAD_LEN);
+        continue;
+      }
+      std::vector<float> K(static_cast<size_t>(L) * d), V(static_cast<size_t>(L) * d), qf(d);
+      const int32_t rc = pao_gather_int8(K.data(), V.data(), key_cache, value_cache, key_scale,
+                                         value_scale, block_tables + static_cast<int64_t>(i) * mb,
+                                         L, /* kv head */ h / group, hkv, d, bs, nb);
+      if (rc != PAO_OK) {
+        status.store(rc);
+        continue;
+      }
+      for (int32_t e = 0; e < d; ++e)
+        qf[e] = widen(q[(static_cast<int64_t>(i) * hq + h) * d + e], dtype);
+      float* o = out_f32 + static_cast<int64_t>(p) * d;
+      attend(o, qf, K, V, L, d, scale);
+      if (out_t)
+        for (int32_t e = 0; e < d; ++e) out_t[static_cast<int64_t>(p) * d + e] = narrow(o[e], dtype);
+    }
+  };
+  std::vector<std::thread> pool;
+  for (int32_t t = 1; t < T; ++t) pool.emplace_back(worker);
+  worker();
+  for (auto& th : pool) th.join();
+  return status.load();
 }
 
 uint64_t pao_kv_bytes_per_token(int32_t layers, int32_t kv_heads,

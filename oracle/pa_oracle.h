@@ -23,6 +23,11 @@
  *   - the split-context form (partial max / sum / accumulator per partition,
  *     then the log-sum-exp merge), used only to check itself against the
  *     single-pass form (first page §4.1, "partial accumulate, then merge");
+ *   - an INT8 KV cache (page "LLM推理优化技术地图：从KV Cache到量化与投机解码",
+ *     §4.3: INT8 halves the KV bytes; the pages fix no convention, so the one
+ *     here is this library's): symmetric codes with one fp32 scale per
+ *     (token, kv head) row, s = max|x| / 127, c = round_half_even(x / s)
+ *     clamped to +-127, dequantised as s * c, then the same attention;
  *   - KV bytes per token, 2 x layers x kv_heads x head_dim x bytes (first page
  *     §二; page www.mhpq.cn/news/468822 §1.2; page
  *     "LLM推理优化技术地图：从KV Cache到量化与投机解码" §2.2).
@@ -117,6 +122,34 @@ int32_t pao_decode_partitioned(float* out_f32, uint16_t* out_t,
                                int32_t hq, int32_t hkv, int32_t d, int32_t bs,
                                int32_t nb, float scale, int32_t dtype,
                                int32_t partition_size);
+
+/* INT8 KV: quantise rows [rows][d] of 16-bit values into codes [rows][d]
+ * and scales [rows] (the convention above). */
+int32_t pao_quantize_rows(const uint16_t* x, int64_t rows, int32_t d, int32_t dtype,
+                          int8_t* codes, float* scales);
+
+/* INT8 cache write: token t's K and V rows [hkv][d] are quantised per kv
+ * head into codes key_cache/value_cache [nb][bs][hkv][d] and scales
+ * key_scale/value_scale [nb][hkv][bs] at slot_mapping[t] (< 0: no write). */
+int32_t pao_cache_write_int8(const uint16_t* key, const uint16_t* value, int8_t* key_cache,
+                             int8_t* value_cache, float* key_scale, float* value_scale,
+                             const int64_t* slot_mapping, int32_t n, int32_t hkv, int32_t d,
+                             int32_t bs, int32_t nb, int32_t dtype);
+
+/* Gather of kv head g with each row dequantised (scale x code, fp32). */
+int32_t pao_gather_int8(float* k_out, float* v_out, const int8_t* key_cache,
+                        const int8_t* value_cache, const float* key_scale,
+                        const float* value_scale, const int32_t* block_table_row, int32_t L,
+                        int32_t g, int32_t hkv, int32_t d, int32_t bs, int32_t nb);
+
+/* pao_decode_pairs over an INT8 cache (same arguments, plus the scales). */
+int32_t pao_decode_int8_pairs(float* out_f32, uint16_t* out_t, const uint16_t* q,
+                              const int8_t* key_cache, const int8_t* value_cache,
+                              const float* key_scale, const float* value_scale,
+                              const int32_t* block_tables, int32_t mb,
+                              const int32_t* context_lens, int32_t s, int32_t hq, int32_t hkv,
+                              int32_t d, int32_t bs, int32_t nb, float scale, int32_t dtype,
+                              const int32_t* pairs, int32_t n_pairs, int32_t nthreads);
 
 /* KV-cache bytes per token: 2 (K and V) x layers x kv_heads x head_dim x
  * bytes per element. */

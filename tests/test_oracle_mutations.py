@@ -26,6 +26,16 @@ MUTATIONS = [
     ("merge weight dropped", "num = num + wp[p] * accp", "num = num + accp", "partitioned"),
     ("cache write offset", "const int64_t dst = (b * bs + o) * row;",
      "const int64_t dst = (o * bs + b) * row;", "cache_write or workload"),
+    ("int8 scale over 128", "const float sc = a / 127.0f;", "const float sc = a / 128.0f;",
+     "int8_quantize"),
+    ("int8 codes truncated", "std::nearbyint(widen(x[e], dtype) / sc)",
+     "std::trunc(widen(x[e], dtype) / sc)", "int8_quantize"),
+    ("int8 scale index [blk][off][g]", "const int64_t sdst = (blk * hkv + g) * bs + off;",
+     "const int64_t sdst = (blk * bs + off) * hkv + g;", "int8_cache_write or int8_decode"),
+    ("int8 dequant drops the scale", "ks * static_cast<float>(key_cache[row + e])",
+     "static_cast<float>(key_cache[row + e])", "int8_decode"),
+    ("int8 V scale from K", "const float vs = value_scale[(blk * hkv + g) * bs + off];",
+     "const float vs = key_scale[(blk * hkv + g) * bs + off];", "int8_decode"),
 ]
 
 

@@ -477,3 +477,162 @@ def test_workload_small_paged_equals_contiguous(cfg):
         ref = brute_force(st.q[i], K, V, np.float32(w.scale), w.dtype)
         got = out32[[n for n, (a, _) in enumerate(pairs) if a == i]]
         assert np.abs(got - ref).max() <= 1e-5 * max(1.0, np.abs(ref).max())
+
+
+# ---------------------------------------------------------------------------
+# INT8 KV cache: quantisation properties, scatter, decode vs fp64 brute force
+# ---------------------------------------------------------------------------
+
+def _rows(rng, n, d, dtype, mags=(1e-3, 1.0, 30.0, 4000.0)):
+    x = np.concatenate([rng.standard_normal((n, d)) * m for m in mags]).astype(np.float32)
+    return to_bits(x, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_int8_quantize_properties(dtype):
+    """Round-to-nearest bound: with q = fl(x / s) = (x / s)(1 + d), |d| <= 2^-24
+    and |x / s| <= 127, |x - s c| <= s (1/2 + 127 * 2^-24); the largest
+    magnitude maps to +-127, s * 127 is the row's largest magnitude, and
+    negation commutes."""
+    rng = np.random.default_rng(21)
+    bits = _rows(rng, 64, 128, dtype)
+    x = ref_widen64(bits, dtype)
+    codes, scales = oracle.quantize_rows(bits, dtype)
+    s = scales.astype(np.float64)[:, None]
+    amax = np.abs(x).max(axis=1)
+    assert np.all(np.abs(x - s * codes) <= s * (0.5 + 128 * 2.0 ** -24))
+    assert np.all(np.abs(s[:, 0] * 127 - amax) <= amax * 2 ** -23)
+    top = np.abs(x).argmax(axis=1)
+    assert np.array_equal(np.abs(codes[np.arange(len(x)), top]), np.full(len(x), 127))
+    assert np.abs(codes).max() <= 127
+    neg = bits ^ np.uint16(0x8000)
+    c2, s2 = oracle.quantize_rows(neg, dtype)
+    assert np.array_equal(c2, -codes) and np.array_equal(s2, scales)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_int8_quantize_exact_on_scaled_integers(dtype):
+    """Rows of integers times 2^k whose largest magnitude is 127 * 2^k quantise
+    losslessly: scale exactly 2^k, codes equal to the integers."""
+    rng = np.random.default_rng(22)
+    for k in range(-8, 9):
+        ints = rng.integers(-127, 128, (16, 64))
+        ints[:, 5] = 127 * rng.choice([-1, 1], 16)
+        bits = to_bits((ints * 2.0 ** k).astype(np.float32), dtype)
+        codes, scales = oracle.quantize_rows(bits, dtype)
+        assert np.all(scales == np.float32(2.0 ** k))
+        assert np.array_equal(codes, ints)
+
+
+def test_int8_quantize_ties_to_even_zero_and_nonfinite():
+    row = np.array([127, 2.5, 3.5, -2.5, -0.5, 0.5, 1.5, -1.5], np.float32)
+    codes, scales = oracle.quantize_rows(to_bits(row, "bf16")[None], "bf16")
+    assert scales[0] == 1.0
+    assert codes[0].tolist() == [127, 2, 4, -2, 0, 0, 2, -2]
+    codes, scales = oracle.quantize_rows(np.zeros((1, 8), np.uint16), "bf16")
+    assert scales[0] == 0.0 and not codes.any()
+    inf_row = to_bits(np.array([1.0, np.inf, 2.0, 3.0], np.float32), "f16")[None]
+    codes, scales = oracle.quantize_rows(inf_row, "f16")
+    assert np.isnan(scales[0]) and not codes.any()
+
+
+def test_int8_cache_write_scatter_readback():
+    rng = np.random.default_rng(23)
+    nb, bs, hkv, d, n, dtype = 12, 16, 3, 32, 41, "bf16"
+    kc = np.full((nb, bs, hkv, d), -128, np.int8)
+    vc = kc.copy()
+    ks = np.full((nb, hkv, bs), np.nan, np.float32)
+    vs = ks.copy()
+    slots = rng.choice(nb * bs, n, replace=False).astype(np.int64)
+    slots[3] = -1
+    k = _rows(rng, n * hkv, d, dtype, (1.0,)).reshape(n, hkv, d)
+    v = _rows(rng, n * hkv, d, dtype, (1.0,)).reshape(n, hkv, d)
+    oracle.cache_write_int8(k, v, kc, vc, ks, vs, slots, dtype)
+    kq, ksc = oracle.quantize_rows(k, dtype)
+    vq, vsc = oracle.quantize_rows(v, dtype)
+    touched = np.zeros((nb, bs), bool)
+    for t, s in enumerate(slots):
+        if s < 0:
+            continue
+        b, o = s // bs, s % bs
+        assert np.array_equal(kc[b, o], kq[t]) and np.array_equal(vc[b, o], vq[t])
+        for g in range(hkv):              # scales are [block][kv head][offset]
+            assert ks[b, g, o] == ksc[t, g] and vs[b, g, o] == vsc[t, g]
+        touched[b, o] = True
+    assert np.all(kc[~touched] == -128) and np.all(vc[~touched] == -128)
+    assert np.isnan(ks.transpose(0, 2, 1)[~touched]).all()
+
+
+def int8_tiny_case(rng, S, Hq, Hkv, D, bs, lens, dtype):
+    """An INT8 pool filled by the oracle's own cache write; the test reads it
+    back with its own index arithmetic for the brute force."""
+    q, kc16, vc16, bt, cl, Ks, Vs = tiny_case(rng, S, Hq, Hkv, D, bs, lens, dtype)
+    nb = kc16.shape[0]
+    kc = np.full((nb, bs, Hkv, D), -128, np.int8)
+    vc = kc.copy()
+    ks = np.full((nb, Hkv, bs), np.nan, np.float32)
+    vs = ks.copy()
+    for i, L in enumerate(lens):
+        slots = np.array([bt[i, j // bs] * bs + j % bs for j in range(L)], np.int64)
+        oracle.cache_write_int8(Ks[i], Vs[i], kc, vc, ks, vs, slots, dtype)
+    return q, kc, vc, ks, vs, bt, cl
+
+
+def dequant64(codes, scales, bt_row, L, bs):
+    """[L][Hkv][D] fp64 rows scale x code, read back from the pools."""
+    return np.stack([codes[bt_row[j // bs], j % bs].astype(np.float64) *
+                     scales[bt_row[j // bs], :, j % bs].astype(np.float64)[:, None]
+                     for j in range(L)])
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_int8_decode_matches_fp64_brute_force(case):
+    S, Hq, Hkv, D, bs, lens, dtype = case
+    rng = np.random.default_rng(hash(str(case)) % (1 << 31) + 5)
+    q, kc, vc, ks, vs, bt, cl = int8_tiny_case(rng, S, Hq, Hkv, D, bs, lens, dtype)
+    scale = 1.0 / math.sqrt(D)
+    out32, outT = oracle.decode_int8(q, kc, vc, ks, vs, bt, cl, scale, dtype)
+    G = Hq // Hkv
+    for i in range(S):
+        K = dequant64(kc, ks, bt[i], lens[i], bs)
+        V = dequant64(vc, vs, bt[i], lens[i], bs)
+        qq = ref_widen64(q[i], dtype)
+        for h in range(Hq):
+            s = np.float64(np.float32(scale)) * (K[:, h // G] @ qq[h])
+            p = np.exp(s - s.max())
+            ref = (p @ V[:, h // G]) / p.sum()
+            assert np.abs(out32[i, h] - ref).max() <= 1e-5 * max(1.0, np.abs(ref).max())
+        assert np.array_equal(outT[i], oracle.narrow(out32[i], dtype))
+
+
+def test_int8_lossless_rows_equal_16bit_decode():
+    """Rows whose values are integers with largest magnitude 127 dequantise to
+    themselves, so the INT8 decode equals the 16-bit decode bit for bit."""
+    rng = np.random.default_rng(24)
+    S, Hq, Hkv, D, bs, lens = 3, 8, 2, 64, 16, [20, 1, 47]
+    q, kc16, vc16, bt, cl, _, _ = tiny_case(rng, S, Hq, Hkv, D, bs, lens, "bf16")
+    nb = kc16.shape[0]
+    kc = np.full((nb, bs, Hkv, D), -128, np.int8); vc = kc.copy()
+    ks = np.full((nb, Hkv, bs), np.nan, np.float32); vs = ks.copy()
+    for i, L in enumerate(lens):
+        K = rng.integers(-127, 128, (L, Hkv, D)); K[:, :, 0] = 127
+        V = rng.integers(-127, 128, (L, Hkv, D)); V[:, :, 3] = -127
+        Kb, Vb = to_bits(K.astype(np.float32), "bf16"), to_bits(V.astype(np.float32), "bf16")
+        slots = np.array([bt[i, j // bs] * bs + j % bs for j in range(L)], np.int64)
+        oracle.cache_write(Kb, Vb, kc16, vc16, slots)
+        oracle.cache_write_int8(Kb, Vb, kc, vc, ks, vs, slots, "bf16")
+    a32, aT = oracle.decode(q, kc16, vc16, bt, cl, 0.01, "bf16")
+    b32, bT = oracle.decode_int8(q, kc, vc, ks, vs, bt, cl, 0.01, "bf16")
+    assert np.array_equal(a32.view(np.uint32), b32.view(np.uint32)) and np.array_equal(aT, bT)
+
+
+def test_int8_decode_pairs_and_poison():
+    rng = np.random.default_rng(25)
+    q, kc, vc, ks, vs, bt, cl = int8_tiny_case(rng, 3, 8, 2, 64, 16, [17, 5, 33], "f16")
+    full, fullT = oracle.decode_int8(q, kc, vc, ks, vs, bt, cl, 0.125, "f16")
+    assert np.isfinite(full).all()                      # NaN scales of unused slots stay out
+    pairs = np.array([[2, 7], [0, 1]], np.int32)
+    sub, subT = oracle.decode_int8(q, kc, vc, ks, vs, bt, cl, 0.125, "f16", pairs=pairs,
+                                   nthreads=2)
+    for n, (i, h) in enumerate(pairs):
+        assert np.array_equal(sub[n], full[i, h]) and np.array_equal(subT[n], fullT[i, h])
