@@ -6,7 +6,7 @@ the new tokens (a3) and the decode (split-context partitions + merge, or
 single pass, by workload).  Inputs are synthetic and seeded (workloads/),
 resident in HBM before the timed region.
 
-    python bench.py [--steps K] [--warmup W] [--config 3] [--block-size 16]
+    python bench.py [--steps K] [--warmup W] [--config 3] [--block-size 16] [--kv-dtype int8]
 
 Prints one JSON line on stdout.  value = algorithmic K/V bytes read by the
 timed steps' decodes / wall time of the timed steps (GB/s); the decode call
@@ -35,16 +35,16 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def cpu_baseline(w, budget_s):
+def cpu_baseline(w, budget_s, int8=False):
     """The oracle as it stands, timed on the host cores over whole sequences of
     the same workload (in a seeded order, cycling) until about budget_s
     seconds of work."""
     import oracle
     from tests import oracle_side
 
-    o = oracle_side.build(w)
+    o = oracle_side.build_int8(w) if int8 else oracle_side.build(w)
     threads = len(os.sched_getaffinity(0))
-    per_tok = 2 * w.Hkv * w.D * w.elem_bytes
+    per_tok = 2 * w.Hkv * (w.D + 4) if int8 else 2 * w.Hkv * w.D * w.elem_bytes
     spent, done_bytes, nseq, ntok = 0.0, 0, 0, 0
     order = np.random.default_rng(1234).permutation(w.S)
     k = 0
@@ -53,8 +53,13 @@ def cpu_baseline(w, budget_s):
         k += 4
         pairs = np.array([[i, h] for i in batch for h in range(w.Hq)], np.int32)
         t0 = time.perf_counter()
-        oracle.decode_pairs(o.q, o.key_cache, o.value_cache, o.block_tables, o.context_lens,
-                            w.scale, w.dtype, pairs, nthreads=threads)
+        if int8:
+            oracle.decode_int8(o.q, o.key_cache, o.value_cache, o.key_scale, o.value_scale,
+                               o.block_tables, o.context_lens, w.scale, w.dtype, pairs=pairs,
+                               nthreads=threads)
+        else:
+            oracle.decode_pairs(o.q, o.key_cache, o.value_cache, o.block_tables, o.context_lens,
+                                w.scale, w.dtype, pairs, nthreads=threads)
         spent += time.perf_counter() - t0
         toks = int(sum(int(w.lengths[i]) for i in batch))
         done_bytes += toks * per_tok
@@ -67,7 +72,8 @@ def cpu_baseline(w, budget_s):
         "kind": "oracle",
         "sample": (f"{nseq} sequence decodes drawn cyclically from the workload's {w.S} "
                    f"(all {w.Hq} q heads each, {ntok} tokens), {spent:.1f} s of oracle time; "
-                   "logical K/V bytes of the sample / oracle decode time"),
+                   ("stored K/V bytes (codes + scales)" if int8 else "logical K/V bytes") +
+                   " of the sample / oracle decode time"),
         "seqs_per_s": nseq / spent,
     }
 
@@ -87,13 +93,14 @@ def kernel_source_sha256():
     return h.hexdigest()
 
 
-def recorded_traffic(config_id, block_size):
+def recorded_traffic(config_id, block_size, int8=False):
     """HBM bytes per decode call from the committed PMC summary of this
     workload, or None if there is none or the kernel sources changed since."""
     import glob
     import re
-    names = {3: "decode_qwen25_7b_gqa_64seq_pmc.md"}
-    name = names.get(config_id) if block_size in (None, 16) else None
+    names = {(3, False): "decode_qwen25_7b_gqa_64seq_pmc.md",
+             (3, True): "decode_qwen25_7b_gqa_64seq_int8_pmc.md"}
+    name = names.get((config_id, int8)) if block_size in (None, 16) else None
     if not name:
         return None
     path = os.path.join(ROOT, "profiles", name)
@@ -114,6 +121,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--block-size", type=int, default=None, choices=[16, 32])
+    ap.add_argument("--kv-dtype", default=None, choices=["int8"],
+                    help="INT8 KV pools (codes + fp32 row scales) instead of 16-bit ones")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--gc", dest="no_gc", action="store_false",
@@ -147,7 +156,8 @@ def main():
     w = workload(args.config, "full", **overrides)
     log(f"[bench] {w.spec.name}; bs={w.bs}; S={w.S}; KV bytes/step ~{w.kv_bytes()/1e6:.1f} MB")
     t0 = time.perf_counter()
-    g = gpu_side.build(w, extra_tokens=args.warmup + args.steps + 1)
+    int8 = args.kv_dtype == "int8"
+    g = gpu_side.build(w, extra_tokens=args.warmup + args.steps + 1, kv_dtype=args.kv_dtype)
     log(f"[bench] inputs resident in HBM ({time.perf_counter() - t0:.1f} s)")
     step = g.step
     stream = step.stream
@@ -198,6 +208,9 @@ def main():
     achieved = kv_per_call / dec_avg / 1e9
     kernel_name = ("pa_decode_partitioned: partition kernel + merge kernel"
                    if w.spec.kernel == "partitioned" else "pa_decode: single-pass kernel")
+    if int8:
+        kernel_name = kernel_name.replace("pa_decode", "pa_decode_int8").replace(
+            "pa_decode_int8_partitioned", "pa_decode_partitioned_int8")
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -218,8 +231,10 @@ def main():
             "block_size": w.bs, "kernel": w.spec.kernel,
             "partition_size": w.spec.partition_size if w.spec.kernel == "partitioned" else None,
             "mean_context_len": float(step.host_context_lens.mean()),
+            "kv_dtype": "int8 codes + fp32 row scales" if int8 else w.dtype,
             "kv_bytes_per_step": int(kv_per_call),
-            "kv_bytes_counting": "unique (a shared prefix once)" if shared else "logical",
+            "kv_bytes_counting": ("unique (a shared prefix once)" if shared else "logical") +
+                                 (", codes + scales as stored" if int8 else ""),
         },
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "seqs_per_s_per_layer": round(w.S * args.steps / elapsed, 1),
@@ -239,7 +254,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": recorded_traffic(args.config, args.block_size),
+            "traffic": recorded_traffic(args.config, args.block_size, int8),
             "traffic_unit": "bytes per decode call (FETCH_SIZE x2 + WRITE_SIZE, copy-calibrated)",
         },
     }
@@ -247,7 +262,7 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample")
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, int8)
     print(json.dumps(result), flush=True)
 
 

@@ -267,6 +267,88 @@ pa_status pa_copy_blocks(void* key_cache, void* value_cache,
                          pa_dtype dtype, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * INT8 KV cache.
+ * Follows: "LLM推理优化技术地图：从KV Cache到量化与投机解码", §4.3 (quantising
+ * the KV cache to INT8 halves its bytes; accuracy is model-dependent).  The
+ * pages fix no convention; this library's is symmetric per-row quantisation
+ * with one fp32 scale per (token, KV head) row of head_dim elements:
+ *   a = max |x|,  s = a / 127,  code = clamp(round_half_even(x / s), -127, 127)
+ * computed in fp32 (correctly rounded division) when the row is written; the
+ * row reads back as s * code.  a = 0 gives codes 0 and s = 0; a row holding
+ * inf or NaN gives s = NaN and codes 0.
+ *   key_cache / value_cache  [num_blocks][block_size][num_kv_heads][head_dim]
+ *                            int8 codes
+ *   key_scale / value_scale  [num_blocks][num_kv_heads][block_size] fp32
+ * head_dim is 64 or 128.  Queries, outputs and the K/V rows handed to the
+ * writes stay 16-bit (dtype); every other argument is as for the 16-bit call
+ * of the same name.
+ * ---------------------------------------------------------------------- */
+
+/* pa_reshape_and_cache into INT8 pools: each token's K and V rows are
+ * quantised per KV head and written with their scales.  Alignment: key /
+ * value 16 bytes, codes and slot_mapping 8, scales 4. */
+pa_status pa_reshape_and_cache_int8(const void* key, const void* value,
+                                    int8_t* key_cache, int8_t* value_cache,
+                                    float* key_scale, float* value_scale,
+                                    const int64_t* slot_mapping,
+                                    int32_t num_tokens, int32_t num_kv_heads,
+                                    int32_t head_dim, int32_t block_size,
+                                    int32_t num_blocks, pa_dtype dtype,
+                                    hipStream_t stream);
+
+/* pa_write_step into INT8 pools (the step's K/V rows quantised as above). */
+pa_status pa_write_step_int8(const int64_t* staged_slots,
+                             const int32_t* staged_lens,
+                             const int32_t* staged_items, int32_t num_items,
+                             int64_t* slot_mapping, int32_t* context_lens,
+                             int32_t* work_items, int32_t* block_tables,
+                             int32_t max_blocks_per_seq, const void* key,
+                             const void* value, int8_t* key_cache,
+                             int8_t* value_cache, float* key_scale,
+                             float* value_scale, int32_t num_seqs,
+                             int32_t num_kv_heads, int32_t head_dim,
+                             int32_t block_size, int32_t num_blocks,
+                             pa_dtype dtype, hipStream_t stream,
+                             hipEvent_t done_event);
+
+/* pa_decode over INT8 pools: K and V rows are read as scale x code; the
+ * output is as for pa_decode (fp32 arithmetic, rounded once to dtype).
+ * Pools 16-byte aligned, scales 4. */
+pa_status pa_decode_int8(void* out, const void* query, const int8_t* key_cache,
+                         const int8_t* value_cache, const float* key_scale,
+                         const float* value_scale, const int32_t* block_tables,
+                         int32_t max_blocks_per_seq,
+                         const int32_t* context_lens, int32_t num_seqs,
+                         int32_t num_q_heads, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t block_size,
+                         int32_t num_blocks, int32_t max_context_len,
+                         float scale, pa_dtype dtype, hipStream_t stream,
+                         hipEvent_t start_event, hipEvent_t stop_event);
+
+/* pa_decode_partitioned over INT8 pools (same workspace size). */
+pa_status pa_decode_partitioned_int8(
+    void* out, const void* query, const int8_t* key_cache,
+    const int8_t* value_cache, const float* key_scale, const float* value_scale,
+    const int32_t* block_tables, int32_t max_blocks_per_seq,
+    const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+    int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t num_blocks, int32_t max_context_len, float scale, pa_dtype dtype,
+    int32_t partition_size, const int32_t* work_items, int32_t num_work_items,
+    void* workspace, size_t workspace_bytes, hipStream_t stream,
+    hipEvent_t start_event, hipEvent_t stop_event);
+
+/* pa_copy_blocks for INT8 pools: codes and scales of each pair's src block
+ * are copied to its dst block.  head_dim a multiple of 16 and
+ * num_kv_heads * block_size a multiple of 4; pools and scales 16-byte
+ * aligned. */
+pa_status pa_copy_blocks_int8(int8_t* key_cache, int8_t* value_cache,
+                              float* key_scale, float* value_scale,
+                              const int32_t* block_pairs, int32_t num_pairs,
+                              int32_t num_kv_heads, int32_t head_dim,
+                              int32_t block_size, int32_t num_blocks,
+                              hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Host block allocator (no device memory; not thread-safe: one caller at a
  * time per handle).
  * Follows: the BlockManager of "LLM推理优化：vLLM PagedAttention深度解析与

@@ -62,6 +62,15 @@ _sig("pa_decode", _i32, _DEC + [_vp, _vp, _vp])
 _sig("pa_decode_partitioned_workspace_size", _sz, [_i32, _i32, _i32, _i32, _i32])
 _sig("pa_decode_partitioned", _i32, _DEC + [_i32, _vp, _i32, _vp, _sz, _vp, _vp, _vp])
 _sig("pa_copy_blocks", _i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp])
+_sig("pa_reshape_and_cache_int8", _i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                         _i32, _i32, _vp])
+_sig("pa_write_step_int8", _i32, [_vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp,
+                                  _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp])
+_DEC8 = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+         _f32, _i32]
+_sig("pa_decode_int8", _i32, _DEC8 + [_vp, _vp, _vp])
+_sig("pa_decode_partitioned_int8", _i32, _DEC8 + [_i32, _vp, _i32, _vp, _sz, _vp, _vp, _vp])
+_sig("pa_copy_blocks_int8", _i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp])
 _sig("pa_alloc_create", _i32, [_i32, _i32, _i32p, ctypes.POINTER(_vp)])
 _sig("pa_alloc_destroy", None, [_vp])
 _sig("pa_alloc_allocate", _i32, [_vp, _i64, _i32])
@@ -241,6 +250,119 @@ def pa_decode_partitioned(out, query, key_cache, value_cache, block_tables, cont
                                       _dptr(workspace, "workspace"),
                                       workspace.numel() * workspace.element_size(),
                                       _stream(stream), _event(start_event), _event(stop_event)))
+
+
+# -- INT8 pools: codes int8 [NB][bs][Hkv][D], scales float32 [NB][Hkv][bs] ---------------
+
+def _check_q8_pools(key_cache, value_cache, key_scale, value_scale):
+    nb, bs, hkv, d = key_cache.shape
+    if tuple(value_cache.shape) != (nb, bs, hkv, d):
+        raise ValueError("key_cache and value_cache shapes differ")
+    if tuple(key_scale.shape) != (nb, hkv, bs) or tuple(value_scale.shape) != (nb, hkv, bs):
+        raise ValueError("scales must be [NB][Hkv][bs]")
+    return nb, bs, hkv, d
+
+
+def _q8_ptrs(key_cache, value_cache, key_scale, value_scale):
+    return [_dptr(key_cache, "key_cache", 1), _dptr(value_cache, "value_cache", 1),
+            _dptr(key_scale, "key_scale", 4), _dptr(value_scale, "value_scale", 4)]
+
+
+def pa_reshape_and_cache_int8(key, value, key_cache, value_cache, key_scale, value_scale,
+                              slot_mapping, dtype, stream=None):
+    """Quantise key/value [N][Hkv][D] (16-bit) into the INT8 pools at slot_mapping."""
+    nb, bs, hkv, d = _check_q8_pools(key_cache, value_cache, key_scale, value_scale)
+    n = slot_mapping.shape[0]
+    if tuple(key.shape) != (n, hkv, d) or tuple(value.shape) != (n, hkv, d):
+        raise ValueError("key/value must be [N][Hkv][D] matching the caches and slot_mapping")
+    _check(_lib.pa_reshape_and_cache_int8(
+        _dptr(key, "key", 2), _dptr(value, "value", 2),
+        *_q8_ptrs(key_cache, value_cache, key_scale, value_scale),
+        _dptr(slot_mapping, "slot_mapping", 8), n, hkv, d, bs, nb, _dtype_code(dtype),
+        _stream(stream)))
+
+
+def pa_write_step_int8(staged_slots, staged_lens, staged_items, slot_mapping, context_lens,
+                       work_items, block_tables, key, value, key_cache, value_cache, key_scale,
+                       value_scale, dtype, stream=None, done_event=None):
+    """pa_write_step into INT8 pools (arguments as there, plus the scales)."""
+    nb, bs, hkv, d = _check_q8_pools(key_cache, value_cache, key_scale, value_scale)
+    s = staged_slots.shape[0]
+    if tuple(staged_lens.shape) != (s,) or tuple(slot_mapping.shape) != (s,) or \
+            tuple(context_lens.shape) != (s,):
+        raise ValueError("staged and device slots / lengths must be [S]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != s:
+        raise ValueError("block_tables must be [S][MB]")
+    if tuple(key.shape) != (s, hkv, d) or tuple(value.shape) != (s, hkv, d):
+        raise ValueError("key/value must be [S][Hkv][D] matching the caches")
+    n = 0 if staged_items is None else int(staged_items.shape[0])
+    if n and (staged_items.dim() != 2 or staged_items.shape[1] != 2 or
+              work_items.shape[0] < n or work_items.shape[1] != 2):
+        raise ValueError("work lists must be [n][2], the device one at least as long")
+    _check(_lib.pa_write_step_int8(
+        _pinned_ptr(staged_slots, "staged_slots", 8), _pinned_ptr(staged_lens, "staged_lens", 4),
+        _pinned_ptr(staged_items, "staged_items", 4) if n else None, n,
+        _dptr(slot_mapping, "slot_mapping", 8), _dptr(context_lens, "context_lens", 4),
+        _dptr(work_items, "work_items", 4) if n else None, _dptr(block_tables, "block_tables", 4),
+        block_tables.shape[1], _dptr(key, "key", 2), _dptr(value, "value", 2),
+        *_q8_ptrs(key_cache, value_cache, key_scale, value_scale), s, hkv, d, bs, nb,
+        _dtype_code(dtype), _stream(stream), _event(done_event)))
+
+
+def _decode_int8_args(out, query, key_cache, value_cache, key_scale, value_scale, block_tables,
+                      context_lens, max_context_len, scale, dtype):
+    s, hq, d = query.shape
+    nb, bs, hkv, d2 = _check_q8_pools(key_cache, value_cache, key_scale, value_scale)
+    if d2 != d:
+        raise ValueError("cache shapes do not match the query")
+    if tuple(out.shape) != tuple(query.shape):
+        raise ValueError("out must have the query's shape")
+    if block_tables.dim() != 2 or block_tables.shape[0] != s or tuple(context_lens.shape) != (s,):
+        raise ValueError("block_tables must be [S][MB] and context_lens [S]")
+    return [_dptr(out, "out", 2), _dptr(query, "query", 2),
+            *_q8_ptrs(key_cache, value_cache, key_scale, value_scale),
+            _dptr(block_tables, "block_tables", 4), block_tables.shape[1],
+            _dptr(context_lens, "context_lens", 4), s, hq, hkv, d, bs, nb, int(max_context_len),
+            float(scale), _dtype_code(dtype)]
+
+
+def pa_decode_int8(out, query, key_cache, value_cache, key_scale, value_scale, block_tables,
+                   context_lens, max_context_len, scale, dtype, stream=None, start_event=None,
+                   stop_event=None):
+    """Single-pass paged decode over INT8 pools; writes out [S][Hq][D] (16-bit)."""
+    args = _decode_int8_args(out, query, key_cache, value_cache, key_scale, value_scale,
+                             block_tables, context_lens, max_context_len, scale, dtype)
+    _check(_lib.pa_decode_int8(*args, _stream(stream), _event(start_event), _event(stop_event)))
+
+
+def pa_decode_partitioned_int8(out, query, key_cache, value_cache, key_scale, value_scale,
+                               block_tables, context_lens, max_context_len, scale, dtype,
+                               partition_size, workspace, work_items=None, stream=None,
+                               start_event=None, stop_event=None):
+    """Split-context paged decode + merge over INT8 pools (workspace as for
+    pa_decode_partitioned)."""
+    args = _decode_int8_args(out, query, key_cache, value_cache, key_scale, value_scale,
+                             block_tables, context_lens, max_context_len, scale, dtype)
+    if work_items is None:
+        wi, nwi = None, 0
+    else:
+        if work_items.dim() != 2 or work_items.shape[1] != 2:
+            raise ValueError("work_items must be [n][2]")
+        wi, nwi = (_dptr(work_items, "work_items", 4) if work_items.shape[0] else None), work_items.shape[0]
+    _check(_lib.pa_decode_partitioned_int8(*args, int(partition_size), wi, int(nwi),
+                                           _dptr(workspace, "workspace"),
+                                           workspace.numel() * workspace.element_size(),
+                                           _stream(stream), _event(start_event),
+                                           _event(stop_event)))
+
+
+def pa_copy_blocks_int8(key_cache, value_cache, key_scale, value_scale, block_pairs, stream=None):
+    """Copy-on-write copies of INT8 blocks (codes and scales); block_pairs int32 [n][2]."""
+    nb, bs, hkv, d = _check_q8_pools(key_cache, value_cache, key_scale, value_scale)
+    n = block_pairs.shape[0]
+    _check(_lib.pa_copy_blocks_int8(*_q8_ptrs(key_cache, value_cache, key_scale, value_scale),
+                                    _dptr(block_pairs, "block_pairs", 4) if n else None, n, hkv,
+                                    d, bs, nb, _stream(stream)))
 
 
 def partition_work_items(context_lens, partition_size, max_parts=None, out=None):

@@ -34,6 +34,10 @@ SOURCES = [
     "pa_attn_f16_d128.hip",
     "pa_attn_bf16_d64.hip",
     "pa_attn_bf16_d128.hip",
+    "pa_attn_q8_f16_d64.hip",
+    "pa_attn_q8_f16_d128.hip",
+    "pa_attn_q8_bf16_d64.hip",
+    "pa_attn_q8_bf16_d128.hip",
     "pa_allocator.cpp",
 ]
 

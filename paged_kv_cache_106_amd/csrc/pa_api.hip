@@ -44,10 +44,27 @@ Workspace workspace_layout(int64_t num_seqs, int64_t num_q_heads, int64_t head_d
   return w;
 }
 
-int (*attn_launcher(pa_dtype dtype, int32_t head_dim))(int, const AttnParams&, hipStream_t,
-                                                       hipEvent_t, hipEvent_t) {
+int (*attn_launcher(pa_dtype dtype, int32_t head_dim, bool q8 = false))(
+    int, const AttnParams&, hipStream_t, hipEvent_t, hipEvent_t) {
+  if (q8) {
+    if (dtype == PA_F16) return head_dim == 64 ? launch_attn_q8_f16_d64 : launch_attn_q8_f16_d128;
+    return head_dim == 64 ? launch_attn_q8_bf16_d64 : launch_attn_q8_bf16_d128;
+  }
   if (dtype == PA_F16) return head_dim == 64 ? launch_attn_f16_d64 : launch_attn_f16_d128;
   return head_dim == 64 ? launch_attn_bf16_d64 : launch_attn_bf16_d128;
+}
+
+// The INT8 scale arrays of a decode: present and 4-byte aligned.
+pa_status check_scales(const float* key_scale, const float* value_scale, int32_t num_seqs,
+                       AttnParams* p) {
+  if (num_seqs > 0) {
+    if (!key_scale || !value_scale) return fail(PA_ERR_INVALID_ARG, "NULL scale array");
+    if (!aligned(key_scale, 4) || !aligned(value_scale, 4))
+      return fail(PA_ERR_INVALID_ARG, "scale arrays must be 4-byte aligned");
+  }
+  p->k_scale = key_scale;
+  p->v_scale = value_scale;
+  return PA_OK;
 }
 
 // Shared checks of pa_decode / pa_decode_partitioned; fills p on success.
@@ -140,6 +157,13 @@ pa_status fail(pa_status st, const char* msg) {
   g_last_error = msg;
   return st;
 }
+
+// The split-context decode after the shared checks (16-bit or INT8 pools).
+pa_status partitioned(AttnParams& p, bool q8, pa_dtype dtype, int32_t head_dim,
+                      int32_t block_size, int32_t max_context_len, int32_t partition_size,
+                      const int32_t* work_items, int32_t num_work_items, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream, hipEvent_t start_event,
+                      hipEvent_t stop_event, const char* what);
 
 void clear_error() { g_last_error.clear(); }
 
@@ -268,6 +292,29 @@ pa_status pa_decode(void* out, const void* query, const void* key_cache, const v
                       "pa_decode");
 }
 
+pa_status pa_decode_int8(void* out, const void* query, const int8_t* key_cache,
+                         const int8_t* value_cache, const float* key_scale,
+                         const float* value_scale, const int32_t* block_tables,
+                         int32_t max_blocks_per_seq, const int32_t* context_lens,
+                         int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                         int32_t max_context_len, float scale, pa_dtype dtype, hipStream_t stream,
+                         hipEvent_t start_event, hipEvent_t stop_event) {
+  pa::clear_error();
+  pa::AttnParams p;
+  pa_status st = pa::check_decode(out, query, key_cache, value_cache, block_tables,
+                                  max_blocks_per_seq, context_lens, num_seqs, num_q_heads,
+                                  num_kv_heads, head_dim, block_size, num_blocks, max_context_len,
+                                  scale, dtype, &p);
+  if (st == PA_OK) st = pa::check_scales(key_scale, value_scale, num_seqs, &p);
+  if (st != PA_OK) return st;
+  if (num_seqs == 0) return pa::mark_events(start_event, stop_event, stream, "pa_decode_int8");
+  p.chunk = pa::kSingleChunk;
+  return pa::launched(
+      pa::attn_launcher(dtype, head_dim, true)(0, p, stream, start_event, stop_event),
+      "pa_decode_int8");
+}
+
 size_t pa_decode_partitioned_workspace_size(int32_t num_seqs, int32_t num_q_heads,
                                             int32_t head_dim, int32_t max_context_len,
                                             int32_t partition_size) {
@@ -295,6 +342,42 @@ pa_status pa_decode_partitioned(void* out, const void* query, const void* key_ca
                                         num_kv_heads, head_dim, block_size, num_blocks,
                                         max_context_len, scale, dtype, &p);
   if (st != PA_OK) return st;
+  return pa::partitioned(p, false, dtype, head_dim, block_size, max_context_len, partition_size,
+                         work_items, num_work_items, workspace, workspace_bytes, stream,
+                         start_event, stop_event, "pa_decode_partitioned");
+}
+
+pa_status pa_decode_partitioned_int8(
+    void* out, const void* query, const int8_t* key_cache, const int8_t* value_cache,
+    const float* key_scale, const float* value_scale, const int32_t* block_tables,
+    int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t num_blocks, int32_t max_context_len, float scale, pa_dtype dtype,
+    int32_t partition_size, const int32_t* work_items, int32_t num_work_items, void* workspace,
+    size_t workspace_bytes, hipStream_t stream, hipEvent_t start_event, hipEvent_t stop_event) {
+  pa::clear_error();
+  pa::AttnParams p;
+  pa_status st = pa::check_decode(out, query, key_cache, value_cache, block_tables,
+                                  max_blocks_per_seq, context_lens, num_seqs, num_q_heads,
+                                  num_kv_heads, head_dim, block_size, num_blocks, max_context_len,
+                                  scale, dtype, &p);
+  if (st == PA_OK) st = pa::check_scales(key_scale, value_scale, num_seqs, &p);
+  if (st != PA_OK) return st;
+  return pa::partitioned(p, true, dtype, head_dim, block_size, max_context_len, partition_size,
+                         work_items, num_work_items, workspace, workspace_bytes, stream,
+                         start_event, stop_event, "pa_decode_partitioned_int8");
+}
+
+}  // extern "C"
+
+namespace pa {
+
+pa_status partitioned(AttnParams& p, bool q8, pa_dtype dtype, int32_t head_dim,
+                      int32_t block_size, int32_t max_context_len, int32_t partition_size,
+                      const int32_t* work_items, int32_t num_work_items, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream, hipEvent_t start_event,
+                      hipEvent_t stop_event, const char* what) {
+  const int32_t num_seqs = p.num_seqs, num_q_heads = p.num_q_heads;
   if (partition_size < block_size || partition_size > pa::kMaxPartition ||
       partition_size % block_size != 0)
     return fail(PA_ERR_INVALID_ARG,
@@ -304,8 +387,7 @@ pa_status pa_decode_partitioned(void* out, const void* query, const void* key_ca
     return fail(PA_ERR_INVALID_ARG, "work_items must be NULL or a 4-byte aligned device array");
   if ((static_cast<int64_t>(num_work_items) + 7) * p.num_kv_heads * p.head_chunks > INT32_MAX)
     return fail(PA_ERR_UNSUPPORTED, "num_work_items * num_kv_heads * head chunks overflows int32");
-  if (num_seqs == 0)
-    return pa::mark_events(start_event, stop_event, stream, "pa_decode_partitioned");
+  if (num_seqs == 0) return pa::mark_events(start_event, stop_event, stream, what);
   const int64_t parts = (static_cast<int64_t>(max_context_len) + partition_size - 1) / partition_size;
   if (parts >= pa::kMaxGrid) return fail(PA_ERR_UNSUPPORTED, "more than 65534 partitions");
   const pa::Workspace w = pa::workspace_layout(num_seqs, num_q_heads, head_dim, parts);
@@ -321,16 +403,18 @@ pa_status pa_decode_partitioned(void* out, const void* query, const void* key_ca
   p.grid_parts = static_cast<int32_t>(parts | 1);
   p.work_items = num_work_items > 0 ? work_items : nullptr;
   p.num_work_items = num_work_items;
-  auto launch = pa::attn_launcher(dtype, head_dim);
+  auto launch = pa::attn_launcher(dtype, head_dim, q8);
   const bool any = work_items ? num_work_items > 0 : parts > 0;
   if (any) {
-    const pa_status s1 =
-        pa::launched(launch(1, p, stream, start_event, nullptr), "pa_decode_partitioned (partitions)");
+    const pa_status s1 = pa::launched(launch(1, p, stream, start_event, nullptr), what);
     if (s1 != PA_OK) return s1;
   }
-  return pa::launched(launch(2, p, stream, any ? nullptr : start_event, stop_event),
-                      "pa_decode_partitioned (merge)");
+  return pa::launched(launch(2, p, stream, any ? nullptr : start_event, stop_event), what);
 }
+
+}  // namespace pa
+
+extern "C" {
 
 pa_status pa_update_block_tables(int32_t* block_tables, int32_t max_blocks_per_seq,
                                  const int32_t* context_lens, const int64_t* slot_mapping,
@@ -372,4 +456,123 @@ pa_status pa_copy_blocks(void* key_cache, void* value_cache, const int32_t* bloc
                       "pa_copy_blocks");
 }
 
+
+pa_status pa_reshape_and_cache_int8(const void* key, const void* value, int8_t* key_cache,
+                                    int8_t* value_cache, float* key_scale, float* value_scale,
+                                    const int64_t* slot_mapping, int32_t num_tokens,
+                                    int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                    int32_t num_blocks, pa_dtype dtype, hipStream_t stream) {
+  pa::clear_error();
+  if (dtype != PA_F16 && dtype != PA_BF16) return fail(PA_ERR_INVALID_ARG, "unknown dtype");
+  if (num_tokens < 0) return fail(PA_ERR_INVALID_ARG, "num_tokens < 0");
+  if (num_kv_heads <= 0 || block_size <= 0 || num_blocks <= 0)
+    return fail(PA_ERR_INVALID_ARG, "num_kv_heads, block_size, num_blocks must be positive");
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PA_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (num_tokens == 0) return PA_OK;
+  if (!key || !value || !key_cache || !value_cache || !key_scale || !value_scale || !slot_mapping)
+    return fail(PA_ERR_INVALID_ARG, "NULL device pointer");
+  if (!pa::aligned(key, 16) || !pa::aligned(value, 16) || !pa::aligned(key_cache, 8) ||
+      !pa::aligned(value_cache, 8) || !pa::aligned(key_scale, 4) ||
+      !pa::aligned(value_scale, 4) || !pa::aligned(slot_mapping, 8))
+    return fail(PA_ERR_INVALID_ARG,
+                "misaligned buffer (K/V 16 bytes, codes and slots 8, scales 4)");
+  const int64_t chunks_per_tok = static_cast<int64_t>(num_kv_heads) * head_dim / 8;
+  if (chunks_per_tok > INT32_MAX) return fail(PA_ERR_UNSUPPORTED, "token row too large");
+  const int64_t num_chunks = static_cast<int64_t>(num_tokens) * chunks_per_tok;
+  if ((num_chunks + 255) / 256 > INT32_MAX) return fail(PA_ERR_UNSUPPORTED, "too many tokens");
+  return pa::launched(
+      pa::launch_cache_write_q8(key, value, key_cache, value_cache, key_scale, value_scale,
+                                slot_mapping, num_tokens, head_dim,
+                                static_cast<int32_t>(chunks_per_tok),
+                                static_cast<int64_t>(num_blocks) * block_size, block_size,
+                                dtype == PA_BF16 ? 1 : 0, stream),
+      "pa_reshape_and_cache_int8");
+}
+
+pa_status pa_write_step_int8(const int64_t* staged_slots, const int32_t* staged_lens,
+                             const int32_t* staged_items, int32_t num_items,
+                             int64_t* slot_mapping, int32_t* context_lens, int32_t* work_items,
+                             int32_t* block_tables, int32_t max_blocks_per_seq, const void* key,
+                             const void* value, int8_t* key_cache, int8_t* value_cache,
+                             float* key_scale, float* value_scale, int32_t num_seqs,
+                             int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                             int32_t num_blocks, pa_dtype dtype, hipStream_t stream,
+                             hipEvent_t done_event) {
+  pa::clear_error();
+  if (dtype != PA_F16 && dtype != PA_BF16) return fail(PA_ERR_INVALID_ARG, "unknown dtype");
+  if (num_seqs < 0 || num_items < 0) return fail(PA_ERR_INVALID_ARG, "negative count");
+  if (num_kv_heads <= 0 || block_size <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0)
+    return fail(PA_ERR_INVALID_ARG,
+                "num_kv_heads, block_size, num_blocks, max_blocks_per_seq must be positive");
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PA_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (num_seqs == 0 && num_items == 0)
+    return pa::mark_events(nullptr, done_event, stream, "pa_write_step_int8");
+  if (num_seqs > 0 && (!staged_slots || !staged_lens || !slot_mapping || !context_lens ||
+                       !block_tables || !key || !value || !key_cache || !value_cache ||
+                       !key_scale || !value_scale))
+    return fail(PA_ERR_INVALID_ARG, "NULL pointer");
+  if (num_items > 0 && (!staged_items || !work_items))
+    return fail(PA_ERR_INVALID_ARG, "NULL work list");
+  if (!pa::aligned(staged_slots, 8) || !pa::aligned(staged_lens, 4) ||
+      !pa::aligned(staged_items, 8) || !pa::aligned(slot_mapping, 8) ||
+      !pa::aligned(context_lens, 4) || !pa::aligned(work_items, 8) ||
+      !pa::aligned(block_tables, 4) || !pa::aligned(key, 16) || !pa::aligned(value, 16) ||
+      !pa::aligned(key_cache, 8) || !pa::aligned(value_cache, 8) ||
+      !pa::aligned(key_scale, 4) || !pa::aligned(value_scale, 4))
+    return fail(PA_ERR_INVALID_ARG,
+                "misaligned buffer (K/V 16 bytes; codes, slots and work list 8; lengths, tables "
+                "and scales 4)");
+  const int64_t chunks_per_tok = static_cast<int64_t>(num_kv_heads) * head_dim / 8;
+  if (chunks_per_tok > INT32_MAX) return fail(PA_ERR_UNSUPPORTED, "token row too large");
+  const int64_t num_chunks = static_cast<int64_t>(num_seqs) * chunks_per_tok;
+  if ((num_chunks + 255) / 256 + (static_cast<int64_t>(num_items) + 255) / 256 > INT32_MAX)
+    return fail(PA_ERR_UNSUPPORTED, "too many tokens");
+  const void *ds, *dl, *di;
+  if (!device_view(staged_slots, &ds) || !device_view(staged_lens, &dl) ||
+      !device_view(staged_items, &di))
+    return fail(PA_ERR_INVALID_ARG,
+                "staged arrays must be pinned host memory the device can read (hipHostMalloc)");
+  return pa::launched(
+      pa::launch_write_step_q8(static_cast<const int64_t*>(ds), static_cast<const int32_t*>(dl),
+                               static_cast<const int32_t*>(di), num_items, slot_mapping,
+                               context_lens, work_items, block_tables, max_blocks_per_seq,
+                               block_size, key, value, key_cache, value_cache, key_scale,
+                               value_scale, num_seqs, head_dim,
+                               static_cast<int32_t>(chunks_per_tok),
+                               static_cast<int64_t>(num_blocks) * block_size,
+                               dtype == PA_BF16 ? 1 : 0, stream, done_event),
+      "pa_write_step_int8");
+}
+
+pa_status pa_copy_blocks_int8(int8_t* key_cache, int8_t* value_cache, float* key_scale,
+                              float* value_scale, const int32_t* block_pairs, int32_t num_pairs,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                              int32_t num_blocks, hipStream_t stream) {
+  pa::clear_error();
+  if (num_pairs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
+    return fail(PA_ERR_INVALID_ARG, "bad size");
+  if (head_dim % 16 != 0 || (static_cast<int64_t>(num_kv_heads) * block_size) % 4 != 0)
+    return fail(PA_ERR_UNSUPPORTED,
+                "head_dim must be a multiple of 16 and num_kv_heads * block_size of 4");
+  if (num_pairs == 0) return PA_OK;
+  if (num_pairs > pa::kMaxGrid) return fail(PA_ERR_UNSUPPORTED, "more than 65535 pairs");
+  if (!key_cache || !value_cache || !key_scale || !value_scale || !block_pairs)
+    return fail(PA_ERR_INVALID_ARG, "NULL pointer");
+  if (!pa::aligned(key_cache, 16) || !pa::aligned(value_cache, 16) ||
+      !pa::aligned(key_scale, 16) || !pa::aligned(value_scale, 16) ||
+      !pa::aligned(block_pairs, 4))
+    return fail(PA_ERR_INVALID_ARG, "misaligned device buffer (pools and scales 16 bytes)");
+  const int64_t code_chunks = static_cast<int64_t>(block_size) * num_kv_heads * head_dim / 16;
+  const int64_t scale_chunks = static_cast<int64_t>(num_kv_heads) * block_size / 4;
+  const pa_status st =
+      pa::launched(pa::launch_copy_blocks(key_cache, value_cache, block_pairs, num_pairs,
+                                          code_chunks, num_blocks, stream),
+                   "pa_copy_blocks_int8 (codes)");
+  if (st != PA_OK) return st;
+  return pa::launched(pa::launch_copy_blocks(key_scale, value_scale, block_pairs, num_pairs,
+                                             scale_chunks, num_blocks, stream),
+                      "pa_copy_blocks_int8 (scales)");
+}
 }  // extern "C"

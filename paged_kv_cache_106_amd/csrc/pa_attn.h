@@ -36,6 +36,15 @@
 // block ids arrive in one vector load (lane i: its unit i) and are read back
 // with readlane; tail tokens of the last block are masked by select (the
 // pools' unused slots may hold NaN).
+//
+// INT8 pools (Q8): the pools hold one signed byte per element and the rows'
+// fp32 scales sit in [NB][Hkv][bs] arrays (a row dequantises to scale x
+// code; "LLM推理优化技术地图：从KV Cache到量化与投机解码", §4.3 for INT8
+// halving the KV bytes, the convention being this library's).  Each lane
+// widens its codes into exact 16-bit pairs (|code| <= 127) for the same v_dot2
+// products and multiplies the finished dot product by the token's K scale;
+// in P.V the probability is multiplied by the token's V scale before the
+// accumulation.  The scales ride in the same unit rings as the codes.
 #pragma once
 
 #include <hip/hip_ext.h>
@@ -87,6 +96,10 @@ struct Fmt<PA_F16> {
   __device__ static inline uint16_t narrow(float x) {
     return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
   }
+  // two floats that are integers of magnitude <= 2048 as an exact f16 pair
+  __device__ static inline uint32_t pack_int(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+  }
 };
 
 template <>
@@ -102,6 +115,11 @@ struct Fmt<PA_BF16> {
     const uint32_t u = __float_as_uint(x);
     if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x0040u);
     return static_cast<uint16_t>((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+  }
+  // two floats that are integers of magnitude <= 256 as an exact bf16 pair
+  // (their low 16 bits are zero)
+  __device__ static inline uint32_t pack_int(float lo, float hi) {
+    return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
   }
 };
 
@@ -184,6 +202,32 @@ struct Tile {
   static_assert(KC >= 1 && VL <= 32 && KGROUPS >= 1, "layout");
 };
 
+// QK layout over INT8 pools: QL lanes per token, each holding KB bytes (= KB
+// dims) of the K row in one load; q needs QC 16-byte pieces (8 dims each) per
+// head.  The narrow layout halves KB (and q) for groups of many heads.  P.V
+// keeps Tile's lanes (VW codes per lane), so the wave combine is shared.
+template <int D, bool NARROW>
+struct TileQK8 {
+  static constexpr int KB = (NARROW || D < 128) ? 8 : 16;
+  static constexpr int QL = D / KB;
+  static constexpr int KTOK = 64 / QL;
+  static constexpr int KGROUPS = 16 / KTOK;
+  static constexpr int QC = KB / 8;
+  static_assert(QL == 8 || QL == 16, "group_sum covers 8 or 16 lanes");
+};
+
+// One unit's loads in a wave's ring: the data words and, for INT8 pools, the
+// scale of the token each lane's words belong to.
+template <typename Vec, int N, int NS>
+struct UnitBuf {
+  Vec d[N];
+  float sc[NS];
+};
+template <typename Vec, int N>
+struct UnitBuf<Vec, N, 0> {
+  Vec d[N];
+};
+
 // Query heads per workgroup from which the narrow layout is used.
 #ifndef PA_NARROW_MIN_GT
 #define PA_NARROW_MIN_GT 5
@@ -246,6 +290,46 @@ __device__ inline uint2 load8(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t 
   return make_uint2(v[0], v[1]);
 }
 
+__device__ inline uint32_t load4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+
+template <typename Vec>
+__device__ inline Vec load_vec(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  if constexpr (std::is_same<Vec, uint4>::value) return load16(r, voff, soff);
+  else if constexpr (std::is_same<Vec, uint2>::value) return load8(r, voff, soff);
+  else return load4(r, voff, soff);
+}
+
+// The 32-bit words of a lane's load, in memory order.
+template <typename Vec>
+struct Words;
+template <>
+struct Words<uint4> {
+  static constexpr int N = 4;
+  __device__ static inline void get(const uint4& v, uint32_t (&w)[4]) {
+    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+  }
+};
+template <>
+struct Words<uint2> {
+  static constexpr int N = 2;
+  __device__ static inline void get(const uint2& v, uint32_t (&w)[2]) {
+    w[0] = v.x; w[1] = v.y;
+  }
+};
+template <>
+struct Words<uint32_t> {
+  static constexpr int N = 1;
+  __device__ static inline void get(const uint32_t& v, uint32_t (&w)[1]) { w[0] = v; }
+};
+
+// Byte k of w as a signed integer, widened to fp32 (one SDWA conversion).
+template <int K>
+__device__ inline float code_at(uint32_t w) {
+  return static_cast<float>(static_cast<int8_t>(w >> (8 * K)));
+}
+
 // Wave-wide reductions that leave the result in every lane: a DPP butterfly
 // inside each 16-lane row, then the four row results read back as scalars.
 __device__ inline float wave_max_all(float x) {
@@ -279,16 +363,28 @@ __device__ inline void wave_lds_sync() {
 // Per-wave pieces shared by the single-pass and split kernels.  Everything
 // here is wave-uniform except what a lane holds of q, K, V, the block ids
 // and the accumulators.
-template <int DT, int D, int GT>
+template <int DT, int D, int GT, bool Q8 = false>
 struct WaveAttn {
   using F = Fmt<DT>;
   using TL = Tile<D, GT, kNarrow<GT>>;
-  static constexpr int UNIT = TL::UNIT, QL = TL::QL, KC = TL::KC, KTOK = TL::KTOK,
-                       KGROUPS = TL::KGROUPS, KLOADS = TL::KLOADS;
+  using T8 = TileQK8<D, kNarrow<GT>>;
+  static constexpr int UNIT = TL::UNIT;
+  // QK: KC = 16-byte q pieces per head; KLOADS = K loads per lane per unit
+  static constexpr int QL = Q8 ? T8::QL : TL::QL, KC = Q8 ? T8::QC : TL::KC,
+                       KTOK = Q8 ? T8::KTOK : TL::KTOK,
+                       KGROUPS = Q8 ? T8::KGROUPS : TL::KGROUPS,
+                       KLOADS = Q8 ? T8::KGROUPS : TL::KLOADS;
   static constexpr int VW = TL::VW, VL = TL::VL, VTOK = TL::VTOK, VLOADS = TL::VLOADS,
                        GTP = TL::GTP;
-  // a lane's piece of a V row: 16 bytes (8 dims) or 8 bytes (4 dims)
-  using VVec = typename std::conditional<VW == 8, uint4, uint2>::type;
+  static constexpr int EB = Q8 ? 1 : 2;   // bytes per pool element
+  // a lane's piece of a K row (16 bytes, or 8 for narrow INT8 rows)
+  using KVec = typename std::conditional<!Q8 || T8::KB == 16, uint4, uint2>::type;
+  // a lane's piece of a V row: VW elements
+  using VVec = typename std::conditional<
+      Q8, typename std::conditional<VW == 8, uint2, uint32_t>::type,
+      typename std::conditional<VW == 8, uint4, uint2>::type>::type;
+  using KBuf = UnitBuf<KVec, KLOADS, Q8 ? KGROUPS : 0>;
+  using VBuf = UnitBuf<VVec, VLOADS, Q8 ? VLOADS : 0>;
 
   // Tokens [c0, c0 + n) of one sequence as one wave sees them: its units are
   // u = wave, wave + 4, ... below ceil(n / UNIT), cnt of them.  Lane i of blk
@@ -305,6 +401,12 @@ struct WaveAttn {
   const uint16_t* q;
   int64_t block_bytes;
   uint32_t tok_bytes, koff, voff;
+  // INT8 scales [NB][Hkv][bs]: block stride, and per-lane offsets of the
+  // lane's first token inside a unit for this KV head
+  const char* ksbase;
+  const char* vsbase;
+  int64_t sc_block_bytes;
+  uint32_t ksoff, vsoff;
   int bs_mask, log2_bs, num_blocks;
   float scale_log2;
   float* s_lds;   // [chunk][GTP]: logits, then probabilities; a unit's rows belong to its wave
@@ -320,11 +422,19 @@ struct WaveAttn {
     kbase = static_cast<const char*>(p.k_cache);
     vbase = static_cast<const char*>(p.v_cache);
     q = static_cast<const uint16_t*>(p.q);
-    block_bytes = p.block_stride * 2;
-    tok_bytes = static_cast<uint32_t>(p.num_kv_heads) * D * 2;
-    const uint32_t head_off = static_cast<uint32_t>(kvh) * D * 2;
-    koff = static_cast<uint32_t>(krow) * tok_bytes + head_off + kcol * 16;
-    voff = static_cast<uint32_t>(vrow) * tok_bytes + head_off + vcol * VW * 2;
+    block_bytes = p.block_stride * EB;
+    tok_bytes = static_cast<uint32_t>(p.num_kv_heads) * D * EB;
+    const uint32_t head_off = static_cast<uint32_t>(kvh) * D * EB;
+    koff = static_cast<uint32_t>(krow) * tok_bytes + head_off + kcol * (Q8 ? T8::KB : 16);
+    voff = static_cast<uint32_t>(vrow) * tok_bytes + head_off + vcol * VW * EB;
+    if constexpr (Q8) {
+      ksbase = reinterpret_cast<const char*>(p.k_scale);
+      vsbase = reinterpret_cast<const char*>(p.v_scale);
+      sc_block_bytes = static_cast<int64_t>(p.num_kv_heads) * p.block_size * 4;
+      const uint32_t sc_head = static_cast<uint32_t>(kvh) * p.block_size * 4;
+      ksoff = sc_head + static_cast<uint32_t>(krow) * 4;
+      vsoff = sc_head + static_cast<uint32_t>(vrow) * 4;
+    }
     bs_mask = p.block_size - 1;
     log2_bs = p.log2_block_size;
     num_blocks = p.num_blocks;
@@ -354,28 +464,55 @@ struct WaveAttn {
     const int t0 = s.c0 + (wave + kWaves * j) * UNIT;
     return blk * block_bytes + static_cast<int64_t>(t0 & bs_mask) * tok_bytes;
   }
+  // The same unit in a scale array [NB][Hkv][bs] (KV head offset excluded).
+  __device__ __forceinline__ int64_t unit_scale_off(const Span& s, int i) const {
+    const int j = max(0, min(i, s.cnt - 1));
+    int blk = __builtin_amdgcn_readlane(s.blk, j);
+    blk = static_cast<unsigned>(blk) < static_cast<unsigned>(num_blocks) ? blk : 0;
+    const int t0 = s.c0 + (wave + kWaves * j) * UNIT;
+    return blk * sc_block_bytes + static_cast<int64_t>(t0 & bs_mask) * 4;
+  }
 
   // Loads of unit i >= cnt go through an empty descriptor and fetch nothing.
-  __device__ __forceinline__ void load_k(uint4 (&dst)[KLOADS], const Span& s, int i) const {
+  __device__ __forceinline__ void load_k(KBuf& dst, const Span& s, int i) const {
     const auto r = block_rsrc(kbase + unit_off(s, i), i < s.cnt);
+    if constexpr (Q8) {
+      const auto rs = block_rsrc(ksbase + unit_scale_off(s, i), i < s.cnt);
 #pragma unroll
-    for (int j = 0; j < KGROUPS; ++j)
+      for (int j = 0; j < KGROUPS; ++j) {
+        dst.d[j] = load_vec<KVec>(r, koff, j * KTOK * tok_bytes);
+        dst.sc[j] = __uint_as_float(load4(rs, ksoff, j * KTOK * 4));
+      }
+    } else {
 #pragma unroll
-      for (int c = 0; c < KC; ++c)
-        dst[j * KC + c] = load16(r, koff + c * QL * 16, j * KTOK * tok_bytes);
+      for (int j = 0; j < KGROUPS; ++j)
+#pragma unroll
+        for (int c = 0; c < KC; ++c)
+          dst.d[j * KC + c] = load16(r, koff + c * QL * 16, j * KTOK * tok_bytes);
+    }
   }
-  __device__ __forceinline__ void load_v(VVec (&dst)[VLOADS], const Span& s, int i) const {
+  __device__ __forceinline__ void load_v(VBuf& dst, const Span& s, int i) const {
     const auto r = block_rsrc(vbase + unit_off(s, i), i < s.cnt);
+    if constexpr (Q8) {
+      const auto rs = block_rsrc(vsbase + unit_scale_off(s, i), i < s.cnt);
 #pragma unroll
-    for (int j = 0; j < VLOADS; ++j) {
-      if constexpr (VW == 8)
-        dst[j] = load16(r, voff, j * VTOK * tok_bytes);
-      else
-        dst[j] = load8(r, voff, j * VTOK * tok_bytes);
+      for (int j = 0; j < VLOADS; ++j) {
+        dst.d[j] = load_vec<VVec>(r, voff, j * VTOK * tok_bytes);
+        dst.sc[j] = __uint_as_float(load4(rs, vsoff, j * VTOK * 4));
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < VLOADS; ++j) {
+        if constexpr (VW == 8)
+          dst.d[j] = load16(r, voff, j * VTOK * tok_bytes);
+        else
+          dst.d[j] = load8(r, voff, j * VTOK * tok_bytes);
+      }
     }
   }
 
-  // q slices for the QK layout: chunk c of head hh = dims c*8*QL + kcol*8 .. +8.
+  // q slices for the QK layout: chunk c of head hh = dims c*8*QL + kcol*8 .. +8
+  // (INT8: dims kcol*KB + c*8 .. +8, the lane's codes).
   // Heads past nact reread the last active head (their results are never
   // stored): loads on every path keep the wait counts exact.
   __device__ __forceinline__ void load_q(uint4 (&qv)[GT][KC], int64_t row0, int nact) const {
@@ -383,30 +520,55 @@ struct WaveAttn {
     for (int hh = 0; hh < GT; ++hh)
 #pragma unroll
       for (int c = 0; c < KC; ++c)
-        qv[hh][c] = *reinterpret_cast<const uint4*>(q + (row0 + min(hh, nact - 1)) * D +
-                                                     c * 8 * QL + kcol * 8);
+        qv[hh][c] = *reinterpret_cast<const uint4*>(
+            q + (row0 + min(hh, nact - 1)) * D + (Q8 ? kcol * T8::KB + c * 8 : c * 8 * QL + kcol * 8));
   }
 
   // Logits of the wave's unit i (raw q.k; scaled in the softmax), written by
   // the lane holding column 0 of each token.
-  __device__ __forceinline__ void qk_unit(const uint4 (&qv)[GT][KC], const uint4 (&kx)[KLOADS],
+  __device__ __forceinline__ void qk_unit(const uint4 (&qv)[GT][KC], const KBuf& kx,
                                           int i) const {
     const int u = wave + kWaves * i;
 #pragma unroll
     for (int j = 0; j < KGROUPS; ++j) {
       float sv[GTP];
+      if constexpr (Q8) {
+        // the lane's codes as exact 16-bit pairs, in dim order: pair m holds
+        // dims 2m, 2m + 1 of the lane's KB
+        constexpr int NW = Words<KVec>::N;
+        uint32_t w[NW], kp[2 * NW];
+        Words<KVec>::get(kx.d[j], w);
 #pragma unroll
-      for (int hh = 0; hh < GT; ++hh) {
-        float a = 0.f;
-#pragma unroll
-        for (int c = 0; c < KC; ++c) {
-          const uint4 k = kx[j * KC + c];
-          a = F::dot2(qv[hh][c].x, k.x, a);
-          a = F::dot2(qv[hh][c].y, k.y, a);
-          a = F::dot2(qv[hh][c].z, k.z, a);
-          a = F::dot2(qv[hh][c].w, k.w, a);
+        for (int m = 0; m < NW; ++m) {
+          kp[2 * m] = F::pack_int(code_at<0>(w[m]), code_at<1>(w[m]));
+          kp[2 * m + 1] = F::pack_int(code_at<2>(w[m]), code_at<3>(w[m]));
         }
-        sv[hh] = group_sum<QL>(a);
+#pragma unroll
+        for (int hh = 0; hh < GT; ++hh) {
+          float a = 0.f;
+#pragma unroll
+          for (int c = 0; c < KC; ++c) {
+            a = F::dot2(qv[hh][c].x, kp[4 * c], a);
+            a = F::dot2(qv[hh][c].y, kp[4 * c + 1], a);
+            a = F::dot2(qv[hh][c].z, kp[4 * c + 2], a);
+            a = F::dot2(qv[hh][c].w, kp[4 * c + 3], a);
+          }
+          sv[hh] = group_sum<QL>(a) * kx.sc[j];
+        }
+      } else {
+#pragma unroll
+        for (int hh = 0; hh < GT; ++hh) {
+          float a = 0.f;
+#pragma unroll
+          for (int c = 0; c < KC; ++c) {
+            const uint4 k = kx.d[j * KC + c];
+            a = F::dot2(qv[hh][c].x, k.x, a);
+            a = F::dot2(qv[hh][c].y, k.y, a);
+            a = F::dot2(qv[hh][c].z, k.z, a);
+            a = F::dot2(qv[hh][c].w, k.w, a);
+          }
+          sv[hh] = group_sum<QL>(a);
+        }
       }
 #pragma unroll
       for (int hh = GT; hh < GTP; ++hh) sv[hh] = 0.f;
@@ -416,37 +578,66 @@ struct WaveAttn {
 
   // P.V of the wave's unit i; tokens past n get V = 0 (their p is 0 and their
   // slots may hold NaN).
-  __device__ __forceinline__ void pv_unit(float (&acc)[GT][VW], const VVec (&vx)[VLOADS],
+  __device__ __forceinline__ void pv_unit(float (&acc)[GT][VW], const VBuf& vx,
                                           const Span& s, int i) const {
     const int u = wave + kWaves * i;
     const bool tail = (u + 1) * UNIT > s.n;
+    if constexpr (Q8) {
 #pragma unroll
-    for (int j = 0; j < VLOADS; ++j) {
-      const int t = u * UNIT + j * VTOK + vrow;
-      uint32_t w[VW / 2];
-      if constexpr (VW == 8) {
-        w[0] = vx[j].x; w[1] = vx[j].y; w[2] = vx[j].z; w[3] = vx[j].w;
-      } else {
-        w[0] = vx[j].x; w[1] = vx[j].y;
+      for (int j = 0; j < VLOADS; ++j) {
+        const int t = u * UNIT + j * VTOK + vrow;
+        // a tail token's scale may be NaN: its weight is 0 by select
+        const float vs = (tail && t >= s.n) ? 0.f : vx.sc[j];
+        constexpr int NW = Words<VVec>::N;
+        uint32_t w[NW];
+        Words<VVec>::get(vx.d[j], w);
+        float vf[VW];
+#pragma unroll
+        for (int m = 0; m < NW; ++m) {
+          vf[4 * m] = code_at<0>(w[m]);
+          vf[4 * m + 1] = code_at<1>(w[m]);
+          vf[4 * m + 2] = code_at<2>(w[m]);
+          vf[4 * m + 3] = code_at<3>(w[m]);
+        }
+        float pr[GTP];
+        lds_load(pr, s_lds + t * GTP);
+#pragma unroll
+        for (int hh = 0; hh < GT; ++hh) {
+          const float pw = pr[hh] * vs;
+#pragma unroll
+          for (int e = 0; e < VW; ++e) acc[hh][e] = fmaf(pw, vf[e], acc[hh][e]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      if (tail && t >= s.n) {
+    } else {
 #pragma unroll
-        for (int e = 0; e < VW / 2; ++e) w[e] = 0;
+      for (int j = 0; j < VLOADS; ++j) {
+        const int t = u * UNIT + j * VTOK + vrow;
+        uint32_t w[VW / 2];
+        if constexpr (VW == 8) {
+          w[0] = vx.d[j].x; w[1] = vx.d[j].y; w[2] = vx.d[j].z; w[3] = vx.d[j].w;
+        } else {
+          w[0] = vx.d[j].x; w[1] = vx.d[j].y;
+        }
+        if (tail && t >= s.n) {
+#pragma unroll
+          for (int e = 0; e < VW / 2; ++e) w[e] = 0;
+        }
+        float pr[GTP];
+        lds_load(pr, s_lds + t * GTP);
+        float vf[VW];
+#pragma unroll
+        for (int e = 0; e < VW / 2; ++e) {
+          vf[2 * e] = F::lo(w[e]);
+          vf[2 * e + 1] = F::hi(w[e]);
+        }
+#pragma unroll
+        for (int hh = 0; hh < GT; ++hh)
+#pragma unroll
+          for (int e = 0; e < VW; ++e) acc[hh][e] = fmaf(pr[hh], vf[e], acc[hh][e]);
+        // keep each group's probabilities and widened V short-lived
+        __builtin_amdgcn_sched_barrier(0);
       }
-      float pr[GTP];
-      lds_load(pr, s_lds + t * GTP);
-      float vf[VW];
-#pragma unroll
-      for (int e = 0; e < VW / 2; ++e) {
-        vf[2 * e] = F::lo(w[e]);
-        vf[2 * e + 1] = F::hi(w[e]);
-      }
-#pragma unroll
-      for (int hh = 0; hh < GT; ++hh)
-#pragma unroll
-        for (int e = 0; e < VW; ++e) acc[hh][e] = fmaf(pr[hh], vf[e], acc[hh][e]);
-      // keep each group's probabilities and widened V short-lived
-      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
@@ -457,7 +648,7 @@ struct WaveAttn {
   // every path the compiler's wait counts see the ring in issue order and
   // wait for one unit at a time (a skipped refill would make it wait for all).
   template <int DEPTH>
-  __device__ __forceinline__ void logits(const uint4 (&qv)[GT][KC], uint4 (&kb)[DEPTH][KLOADS],
+  __device__ __forceinline__ void logits(const uint4 (&qv)[GT][KC], KBuf (&kb)[DEPTH],
                                          const Span& s) const {
     for (int i = 0; i < s.cnt; i += DEPTH) {
 #pragma unroll
@@ -520,7 +711,7 @@ struct WaveAttn {
   // P.V over all the wave's units through a ring of DEPTH unit buffers, as
   // the logits.
   template <int DEPTH>
-  __device__ __forceinline__ void values(float (&acc)[GT][VW], VVec (&vb)[DEPTH][VLOADS],
+  __device__ __forceinline__ void values(float (&acc)[GT][VW], VBuf (&vb)[DEPTH],
                                          const Span& s) const {
     for (int i = 0; i < s.cnt; i += DEPTH) {
 #pragma unroll
@@ -621,9 +812,9 @@ __device__ __forceinline__ void combine_waves(const AttnParams& p,
 // walks the whole context in chunks of p.chunk tokens, each wave keeping its
 // own running max / sum / accumulator across chunks (rescaled by alpha),
 // and writes the normalised output.
-template <int DT, int D, int GT>
+template <int DT, int D, int GT, bool Q8>
 __global__ __launch_bounds__(kThreads) void single_kernel(AttnParams p) {
-  using W = WaveAttn<DT, D, GT>;
+  using W = WaveAttn<DT, D, GT, Q8>;
   extern __shared__ float lds[];
   const int kvhc = blockIdx.x;
   const int seq = blockIdx.y;
@@ -658,12 +849,12 @@ __global__ __launch_bounds__(kThreads) void single_kernel(AttnParams p) {
     {
       uint4 qv[GT][W::KC];
       w.load_q(qv, row0, nact);                    // first: waiting for q must not wait for K
-      uint4 kb[kDepthSingle][W::KLOADS];
+      typename W::KBuf kb[kDepthSingle];
 #pragma unroll
       for (int b = 0; b < kDepthSingle; ++b) w.load_k(kb[b], s, b);
       w.template logits<kDepthSingle>(qv, kb, s);
     }
-    typename W::VVec vb[kDepthSingle][W::VLOADS];             // streams in during the softmax
+    typename W::VBuf vb[kDepthSingle];             // streams in during the softmax
 #pragma unroll
     for (int b = 0; b < kDepthSingle; ++b) w.load_v(vb[b], s, b);
     wave_lds_sync();
@@ -693,9 +884,9 @@ __global__ __launch_bounds__(kThreads) void single_kernel(AttnParams p) {
 //         linear id, and an odd stride rotates each sequence's partition p
 //         across them (partition p exists only for sequences longer than
 //         p * P, so a fixed mapping would load the XCDs unevenly).
-template <int DT, int D, int GT>
+template <int DT, int D, int GT, bool Q8>
 __global__ __launch_bounds__(kThreads) void split_kernel(AttnParams p) {
-  using W = WaveAttn<DT, D, GT>;
+  using W = WaveAttn<DT, D, GT, Q8>;
   extern __shared__ float lds[];
   int seq, kvhc, part;
   if (p.work_items) {
@@ -738,11 +929,11 @@ __global__ __launch_bounds__(kThreads) void split_kernel(AttnParams p) {
   if (s.cnt > 0) {                                 // uniform: this wave has tokens
     // Issue order matters: loads complete in order for the wait counts, so q
     // goes first (waiting for it must not wait for the rings).
-    typename W::VVec vb[kDepthSplit][W::VLOADS];
+    typename W::VBuf vb[kDepthSplit];
     {
       uint4 qv[GT][W::KC];
       w.load_q(qv, row0, nact);
-      uint4 kb[kDepthSplit][W::KLOADS];
+      typename W::KBuf kb[kDepthSplit];
 #pragma unroll
       for (int b = 0; b < kDepthSplit; ++b) w.load_k(kb[b], s, b);
       if constexpr (kEarlyV && !kNarrow<GT>) {
@@ -897,7 +1088,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(AttnParams p) {
   }
 }
 
-template <int DT, int D, int GT>
+template <int DT, int D, int GT, bool Q8>
 int launch_attn_gt(int kind, const AttnParams& p, hipStream_t stream, hipEvent_t start,
                    hipEvent_t stop) {
   using TL = Tile<D, GT, kNarrow<GT>>;
@@ -906,17 +1097,18 @@ int launch_attn_gt(int kind, const AttnParams& p, hipStream_t stream, hipEvent_t
   if (kind == 0) {
     const size_t lds = lds_floats(D, GT, TL::GTP, p.chunk) * sizeof(float);
     const dim3 grid(nkv, p.num_seqs, 1);
-    hipExtLaunchKernelGGL((single_kernel<DT, D, GT>), grid, block, lds, stream, start, stop, 0, p);
+    hipExtLaunchKernelGGL((single_kernel<DT, D, GT, Q8>), grid, block, lds, stream, start, stop, 0, p);
   } else {
     const size_t lds = lds_floats(D, GT, TL::GTP, p.chunk) * sizeof(float);
     const dim3 grid = p.work_items ? dim3(((p.num_work_items + 7) / 8) * 8 * nkv, 1, 1)
                                    : dim3(p.grid_parts, nkv, p.num_seqs);
-    hipExtLaunchKernelGGL((split_kernel<DT, D, GT>), grid, block, lds, stream, start, stop, 0, p);
+    hipExtLaunchKernelGGL((split_kernel<DT, D, GT, Q8>), grid, block, lds, stream, start, stop, 0, p);
   }
   return static_cast<int>(hipGetLastError());
 }
 
-template <int DT, int D>
+// Q8: the pools hold INT8 codes with fp32 row scales (p.k_scale, p.v_scale).
+template <int DT, int D, bool Q8 = false>
 int launch_attn(int kind, const AttnParams& p, hipStream_t stream, hipEvent_t start,
                 hipEvent_t stop) {
   if (kind == 2) {
@@ -925,14 +1117,14 @@ int launch_attn(int kind, const AttnParams& p, hipStream_t stream, hipEvent_t st
     return static_cast<int>(hipGetLastError());
   }
   switch (p.heads_per_wg) {
-    case 1: return launch_attn_gt<DT, D, 1>(kind, p, stream, start, stop);
-    case 2: return launch_attn_gt<DT, D, 2>(kind, p, stream, start, stop);
-    case 3: return launch_attn_gt<DT, D, 3>(kind, p, stream, start, stop);
-    case 4: return launch_attn_gt<DT, D, 4>(kind, p, stream, start, stop);
-    case 5: return launch_attn_gt<DT, D, 5>(kind, p, stream, start, stop);
-    case 6: return launch_attn_gt<DT, D, 6>(kind, p, stream, start, stop);
-    case 7: return launch_attn_gt<DT, D, 7>(kind, p, stream, start, stop);
-    case 8: return launch_attn_gt<DT, D, 8>(kind, p, stream, start, stop);
+    case 1: return launch_attn_gt<DT, D, 1, Q8>(kind, p, stream, start, stop);
+    case 2: return launch_attn_gt<DT, D, 2, Q8>(kind, p, stream, start, stop);
+    case 3: return launch_attn_gt<DT, D, 3, Q8>(kind, p, stream, start, stop);
+    case 4: return launch_attn_gt<DT, D, 4, Q8>(kind, p, stream, start, stop);
+    case 5: return launch_attn_gt<DT, D, 5, Q8>(kind, p, stream, start, stop);
+    case 6: return launch_attn_gt<DT, D, 6, Q8>(kind, p, stream, start, stop);
+    case 7: return launch_attn_gt<DT, D, 7, Q8>(kind, p, stream, start, stop);
+    case 8: return launch_attn_gt<DT, D, 8, Q8>(kind, p, stream, start, stop);
     default: return static_cast<int>(hipErrorInvalidValue);
   }
 }

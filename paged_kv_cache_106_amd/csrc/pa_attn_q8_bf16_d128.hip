@@ -1,0 +1,9 @@
+// Attention kernels over INT8 pools instantiated for bf16 queries, head_dim 128.
+#include "pa_attn.h"
+
+namespace pa {
+int launch_attn_q8_bf16_d128(int kind, const AttnParams& p, hipStream_t stream, hipEvent_t start,
+                            hipEvent_t stop) {
+  return launch_attn<PA_BF16, 128, true>(kind, p, stream, start, stop);
+}
+}  // namespace pa

@@ -41,6 +41,8 @@ struct AttnParams {
   const int32_t* work_items;  // [num_work_items][2] (seq, partition), or NULL: dense grid
   int32_t num_work_items;
   float scale_log2;           // scale * log2(e): logits live in the base-2 domain
+  const float* k_scale;       // INT8 pools only: [NB][Hkv][bs] fp32 row scales
+  const float* v_scale;
 };
 
 // Launchers; each returns the hipError_t of its launch.
@@ -55,6 +57,16 @@ int launch_attn_bf16_d64(int kind, const AttnParams& p, hipStream_t stream, hipE
                          hipEvent_t stop);
 int launch_attn_bf16_d128(int kind, const AttnParams& p, hipStream_t stream, hipEvent_t start,
                           hipEvent_t stop);
+// INT8 pools (codes, with the row scales in p.k_scale / p.v_scale); kind 2
+// (merge) is the same kernel as for 16-bit pools.
+int launch_attn_q8_f16_d64(int kind, const AttnParams& p, hipStream_t stream, hipEvent_t start,
+                           hipEvent_t stop);
+int launch_attn_q8_f16_d128(int kind, const AttnParams& p, hipStream_t stream, hipEvent_t start,
+                            hipEvent_t stop);
+int launch_attn_q8_bf16_d64(int kind, const AttnParams& p, hipStream_t stream, hipEvent_t start,
+                            hipEvent_t stop);
+int launch_attn_q8_bf16_d128(int kind, const AttnParams& p, hipStream_t stream, hipEvent_t start,
+                             hipEvent_t stop);
 int launch_cache_write(const void* key, const void* value, void* k_cache, void* v_cache,
                        const int64_t* slots, int32_t n, int32_t chunks_per_tok,
                        int64_t num_slots, hipStream_t stream);
@@ -66,6 +78,17 @@ int launch_write_step(const int64_t* staged_slots, const int32_t* staged_lens,
                       int32_t bs, const void* key, const void* value, void* k_cache,
                       void* v_cache, int32_t n, int32_t chunks_per_tok, int64_t num_slots,
                       hipStream_t stream, hipEvent_t done);
+int launch_cache_write_q8(const void* key, const void* value, void* k_codes, void* v_codes,
+                          float* k_scale, float* v_scale, const int64_t* slots, int32_t n,
+                          int32_t head_dim, int32_t chunks_per_tok, int64_t num_slots, int32_t bs,
+                          int32_t bf16, hipStream_t stream);
+int launch_write_step_q8(const int64_t* staged_slots, const int32_t* staged_lens,
+                         const int32_t* staged_items, int32_t num_items, int64_t* slot_mapping,
+                         int32_t* context_lens, int32_t* work_items, int32_t* tables, int32_t mb,
+                         int32_t bs, const void* key, const void* value, void* k_codes,
+                         void* v_codes, float* k_scale, float* v_scale, int32_t n,
+                         int32_t head_dim, int32_t chunks_per_tok, int64_t num_slots,
+                         int32_t bf16, hipStream_t stream, hipEvent_t done);
 int launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int32_t num_pairs,
                        int64_t chunks_per_block, int32_t num_blocks, hipStream_t stream);
 

@@ -1,7 +1,8 @@
 """A paged KV cache on one GPU and its decode step.
 
 ``PagedKVCache`` owns the two device pools ([num_blocks][block_size][Hkv][D],
-16-bit) and the host block allocator.  ``DecodeStep`` runs one decode step for
+16-bit, or INT8 codes with fp32 row scales [num_blocks][Hkv][block_size]) and
+the host block allocator.  ``DecodeStep`` runs one decode step for
 a fixed batch of sequences, in the order the pages describe for a step
 ("vLLM 深度拆解：当大模型推理学会「分页注意力」", §3.1 data flow and §3.3):
 
@@ -30,6 +31,7 @@ from . import _native as pa
 from ._hip import Event
 
 POISON = {"f16": 0x7E00, "bf16": 0x7FC0}   # quiet-NaN patterns for unused slots
+POISON_CODE = -128                          # no quantised row holds it (codes are within +-127)
 
 
 def _dtype(dtype):
@@ -37,19 +39,38 @@ def _dtype(dtype):
 
 
 class PagedKVCache:
+    """kv_dtype None: pools in the model's 16-bit dtype; "int8": INT8 codes
+    with one fp32 scale per (token, KV head) row (key_scale / value_scale
+    [num_blocks][Hkv][block_size]), quantised by the library's writes."""
+
     def __init__(self, num_blocks, block_size, num_kv_heads, head_dim, dtype,
-                 initial_free_order=None, device="cuda", poison=True):
+                 initial_free_order=None, device="cuda", poison=True, kv_dtype=None,
+                 prefix_caching=False):
         self.num_blocks = int(num_blocks)
         self.block_size = int(block_size)
         self.num_kv_heads = int(num_kv_heads)
         self.head_dim = int(head_dim)
         self.dtype = _dtype(dtype)
+        if kv_dtype not in (None, "int8"):
+            raise ValueError(f"kv_dtype must be None or 'int8', not {kv_dtype!r}")
+        self.int8 = kv_dtype == "int8"
         self.device = torch.device(device)
         shape = (self.num_blocks, self.block_size, self.num_kv_heads, self.head_dim)
-        fill = POISON[self.dtype] if poison else 0
-        self.key_cache = torch.full(shape, fill, dtype=torch.int16, device=self.device)
-        self.value_cache = torch.full(shape, fill, dtype=torch.int16, device=self.device)
-        self.allocator = pa.Allocator(self.num_blocks, self.block_size, initial_free_order)
+        if self.int8:
+            fill = POISON_CODE if poison else 0
+            self.key_cache = torch.full(shape, fill, dtype=torch.int8, device=self.device)
+            self.value_cache = torch.full(shape, fill, dtype=torch.int8, device=self.device)
+            sshape = (self.num_blocks, self.num_kv_heads, self.block_size)
+            sfill = float("nan") if poison else 0.0
+            self.key_scale = torch.full(sshape, sfill, dtype=torch.float32, device=self.device)
+            self.value_scale = torch.full(sshape, sfill, dtype=torch.float32, device=self.device)
+        else:
+            fill = POISON[self.dtype] if poison else 0
+            self.key_cache = torch.full(shape, fill, dtype=torch.int16, device=self.device)
+            self.value_cache = torch.full(shape, fill, dtype=torch.int16, device=self.device)
+            self.key_scale = self.value_scale = None
+        self.allocator = pa.Allocator(self.num_blocks, self.block_size, initial_free_order,
+                                      prefix_caching=prefix_caching)
 
     # -- writing tokens that are already in the sequence (history) ----------------
     def write_positions(self, spans, keys, values, stream=None):
@@ -65,9 +86,24 @@ class PagedKVCache:
         k = k.to(dev, non_blocking=False)
         v = v.to(dev, non_blocking=False)
         sl = torch.from_numpy(slots).to(dev)
-        pa.pa_reshape_and_cache(k, v, self.key_cache, self.value_cache, sl, self.dtype, stream)
+        if self.int8:
+            pa.pa_reshape_and_cache_int8(k, v, self.key_cache, self.value_cache, self.key_scale,
+                                         self.value_scale, sl, self.dtype, stream)
+        else:
+            pa.pa_reshape_and_cache(k, v, self.key_cache, self.value_cache, sl, self.dtype, stream)
+
+    def copy_blocks(self, pairs, stream=None):
+        """Copy-on-write copies; pairs: int32 GPU tensor [n][2] of (src, dst)."""
+        if self.int8:
+            pa.pa_copy_blocks_int8(self.key_cache, self.value_cache, self.key_scale,
+                                   self.value_scale, pairs, stream)
+        else:
+            pa.pa_copy_blocks(self.key_cache, self.value_cache, pairs, self.dtype, stream)
 
     def kv_bytes_per_token(self):
+        """Bytes of K and V one cached token holds (INT8: codes and scales)."""
+        if self.int8:
+            return 2 * self.num_kv_heads * (self.head_dim + 4)
         return 2 * self.num_kv_heads * self.head_dim * 2
 
 
@@ -157,25 +193,31 @@ class DecodeStep:
             self._items.shape[0], ctypes.byref(self._nitems)))
         o1, _, o3 = self._offsets()
         stream = self.stream.cuda_stream
+        pools = [c.key_cache.data_ptr(), c.value_cache.data_ptr()]
+        if c.int8:
+            pools += [c.key_scale.data_ptr(), c.value_scale.data_ptr()]
+        dt = [pa._dtype_code(c.dtype)] if c.int8 else []
+        self._write_fn = L.pa_write_step_int8 if c.int8 else L.pa_write_step
         self._write_args = []
         for h in self._host:
             base = h.data_ptr()
             self._write_args.append([
                 base, base + o1, base + o3, 0, self.slot_mapping.data_ptr(),
                 self.context_lens.data_ptr(), self.work_items.data_ptr(),
-                self.block_tables.data_ptr(), self.mb, None, None, c.key_cache.data_ptr(),
-                c.value_cache.data_ptr(), S, c.num_kv_heads, c.head_dim, c.block_size,
-                c.num_blocks, stream, None])
+                self.block_tables.data_ptr(), self.mb, None, None] + pools +
+                [S, c.num_kv_heads, c.head_dim, c.block_size, c.num_blocks] + dt + [stream, None])
         self._kv_shape = (S, c.num_kv_heads, c.head_dim)
         self._q_shape = (S, self.num_q_heads, c.head_dim)
-        dec = [self.out.data_ptr(), None, c.key_cache.data_ptr(), c.value_cache.data_ptr(),
-               self.block_tables.data_ptr(), self.mb, self.context_lens.data_ptr(), S,
-               self.num_q_heads, c.num_kv_heads, c.head_dim, c.block_size, c.num_blocks,
-               self.max_context_len, self.scale, pa._dtype_code(c.dtype)]
+        dec = [self.out.data_ptr(), None] + pools + [
+            self.block_tables.data_ptr(), self.mb, self.context_lens.data_ptr(), S,
+            self.num_q_heads, c.num_kv_heads, c.head_dim, c.block_size, c.num_blocks,
+            self.max_context_len, self.scale, pa._dtype_code(c.dtype)]
         if self.kernel == "single":
-            self._decode_fn, self._decode_args = L.pa_decode, dec + [stream, None, None]
+            self._decode_fn = L.pa_decode_int8 if c.int8 else L.pa_decode
+            self._decode_args = dec + [stream, None, None]
         else:
-            self._decode_fn = L.pa_decode_partitioned
+            self._decode_fn = L.pa_decode_partitioned_int8 if c.int8 else L.pa_decode_partitioned
+            self._nitems_arg = len(dec) + 2
             self._decode_args = dec + [self.partition_size, self.work_items.data_ptr(), 0,
                                        self.workspace.data_ptr(),
                                        self.workspace.numel(), stream, None, None]
@@ -271,8 +313,7 @@ class DecodeStep:
         c = self.cache
         b = self._cur
         if self._ncow_dev:
-            pa.pa_copy_blocks(c.key_cache, c.value_cache, self.cow_pairs[: self._ncow_dev],
-                              c.dtype, self.stream)
+            c.copy_blocks(self.cow_pairs[: self._ncow_dev], self.stream)
         args = self._write_args[b]
         args[3] = self._nitems_dev
         args[9] = self._check_input(k_new, self._kv_shape, "k_new")
@@ -282,8 +323,8 @@ class DecodeStep:
         if k % self.EVENT_EVERY == self.EVENT_EVERY - 1:
             ev = self._spare.pop()                 # the launch records it when it has run
             self._recorded.append((k, ev))
-        args[19] = None if ev is None else ev.handle
-        pa._check(pa.lib().pa_write_step(*args))
+        args[-1] = None if ev is None else ev.handle
+        pa._check(self._write_fn(*args))
 
     def attend(self, q, start_event=None, stop_event=None):
         """a4 or a5+a6: decode for q [S][Hq][D] into self.out.  Optional
@@ -292,7 +333,7 @@ class DecodeStep:
         args = self._decode_args
         args[1] = self._check_input(q, self._q_shape, "q")
         if self.kernel == "partitioned":
-            args[18] = self._nitems_dev
+            args[self._nitems_arg] = self._nitems_dev
         args[-2] = None if start_event is None else start_event.handle
         args[-1] = None if stop_event is None else stop_event.handle
         pa._check(self._decode_fn(*args))

@@ -49,9 +49,9 @@ def history_arrays(w: Workload):
 
 
 def build(w: Workload, kernel=None, partition_size=None, extra_tokens=0, poison=True,
-          mcl=None) -> GpuState:
+          mcl=None, kv_dtype=None) -> GpuState:
     cache = PagedKVCache(w.num_blocks, w.bs, w.Hkv, w.D, w.dtype, w.initial_free_order,
-                         poison=poison)
+                         poison=poison, kv_dtype=kv_dtype)
     for op in w.alloc_ops:
         if op[0] == "allocate":
             cache.allocator.allocate(op[1], op[2])

@@ -72,3 +72,42 @@ def build(w: Workload, poison: bool = True, write_new: bool = True) -> OracleSta
                        block_tables=tables_of(model, w.S, mb),
                        context_lens=w.lengths.copy(), new_slots=new_slots,
                        q=w.query(), k_new=k_new, v_new=v_new)
+
+
+@dataclass
+class OracleInt8State:
+    key_cache: np.ndarray         # int8 [NB][bs][Hkv][D]
+    value_cache: np.ndarray
+    key_scale: np.ndarray         # float32 [NB][Hkv][bs]
+    value_scale: np.ndarray
+    block_tables: np.ndarray
+    context_lens: np.ndarray
+    q: np.ndarray
+
+
+def build_int8(w: Workload, poison: bool = True) -> OracleInt8State:
+    """The workload's state over INT8 pools: the same replay and slots, every
+    row quantised by the oracle's INT8 cache write; unused codes -128, unused
+    scales NaN."""
+    model, new_slots = replay(w)
+    shape = (w.num_blocks, w.bs, w.Hkv, w.D)
+    kc = np.full(shape, -128 if poison else 0, np.int8)
+    vc = kc.copy()
+    ks = np.full((w.num_blocks, w.Hkv, w.bs), np.nan if poison else 0.0, np.float32)
+    vs = ks.copy()
+    if w.spec.prefix_seqs:
+        P = w.spec.prefix_len
+        slots = np.array(model.slots(0, 0, P), np.int64)
+        oracle.cache_write_int8(w.prefix_tokens("k"), w.prefix_tokens("v"), kc, vc, ks, vs, slots,
+                                w.dtype)
+    for i in range(w.S):
+        b, e = w.prefix_of(i), int(w.lengths[i]) - 1
+        if e > b:
+            slots = np.array(model.slots(i, b, e), np.int64)
+            oracle.cache_write_int8(w.private_history(i, "k"), w.private_history(i, "v"), kc, vc,
+                                    ks, vs, slots, w.dtype)
+    oracle.cache_write_int8(w.new_tokens("k"), w.new_tokens("v"), kc, vc, ks, vs, new_slots,
+                            w.dtype)
+    return OracleInt8State(key_cache=kc, value_cache=vc, key_scale=ks, value_scale=vs,
+                           block_tables=tables_of(model, w.S, w.max_blocks_per_seq()),
+                           context_lens=w.lengths.copy(), q=w.query())

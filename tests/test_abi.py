@@ -202,3 +202,35 @@ def test_one_hip_runtime_in_the_process():
     r = subprocess.run([os.sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
     assert r.stdout.strip() == "1"
+
+
+def test_int8_entry_points_reject_on_host():
+    f = L.pa_decode_int8
+    ok = [BAD, BAD, BAD, BAD, BAD, BAD, BAD, 4, BAD, 2, 8, 2, 128, 16, 10, 64, 0.088, 1]
+    assert f(*(ok[:9] + [0] + ok[10:]), None, None, None) == _native.PA_OK      # empty batch
+    for idx, val, status in [(4, None, _native.PA_ERR_INVALID_ARG),          # NULL K scales
+                             (5, MIS, _native.PA_ERR_INVALID_ARG),           # misaligned V scales
+                             (12, 96, _native.PA_ERR_UNSUPPORTED),           # head_dim
+                             (17, 7, _native.PA_ERR_INVALID_ARG)]:           # dtype
+        bad = list(ok); bad[idx] = val
+        assert f(*bad, None, None, None) == status
+    g = L.pa_decode_partitioned_int8
+    assert g(*ok, 500, None, 0, BAD, 1 << 30, None, None, None) == _native.PA_ERR_INVALID_ARG
+    bad = list(ok); bad[4] = None
+    assert g(*bad, 512, None, 0, BAD, 1 << 30, None, None, None) == _native.PA_ERR_INVALID_ARG
+    c = L.pa_reshape_and_cache_int8
+    ok = [BAD, BAD, BAD, BAD, BAD, BAD, BAD, 4, 2, 128, 16, 10, 1, None]
+    assert c(*(ok[:7] + [0] + ok[8:])) == _native.PA_OK                     # no tokens
+    for idx, val, status in [(9, 96, _native.PA_ERR_UNSUPPORTED), (4, None, _native.PA_ERR_INVALID_ARG),
+                             (2, MIS, _native.PA_ERR_INVALID_ARG), (12, 9, _native.PA_ERR_INVALID_ARG)]:
+        bad = list(ok); bad[idx] = val
+        assert c(*bad) == status
+    cb = L.pa_copy_blocks_int8
+    assert cb(BAD, BAD, BAD, BAD, BAD, 0, 2, 128, 16, 10, None) == _native.PA_OK
+    assert cb(BAD, BAD, BAD, BAD, None, 3, 2, 128, 16, 10, None) == _native.PA_ERR_INVALID_ARG
+    assert cb(BAD, BAD, BAD, BAD, BAD, 3, 2, 120, 16, 10, None) == _native.PA_ERR_UNSUPPORTED
+    w = L.pa_write_step_int8
+    assert w(None, None, None, 0, None, None, None, None, 4, None, None, None, None, None, None,
+             0, 2, 128, 16, 10, 1, None, None) == _native.PA_OK
+    assert w(BAD, BAD, None, 0, BAD, BAD, None, BAD, 4, BAD, BAD, BAD, BAD, BAD, BAD,
+             2, 2, 96, 16, 10, 1, None, None) == _native.PA_ERR_UNSUPPORTED

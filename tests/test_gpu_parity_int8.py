@@ -1,0 +1,226 @@
+"""GPU parity over INT8 KV pools: libpa (through its C ABI) against the CPU
+oracle's INT8 path on the same seeded inputs.
+
+Bars: codes and scales bit-exact (whole pools compared, poisoned unused slots
+included; the codes are integers decided in fp32 on both sides by the same
+operations); decode outputs within max|d| <= 1e-2 of the oracle's fp32 result
+and within half an ulp of the 16-bit format plus 1e-4 of it.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_106_amd as pa
+from workloads import make_workload, spec, workload
+from tests import gpu_side, oracle_side
+from tests.test_gpu_parity import check_outputs, free_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def check_pools(g, o, label):
+    c = g.cache
+    assert np.array_equal(c.key_cache.cpu().numpy(), o.key_cache), f"{label}: K codes"
+    assert np.array_equal(c.value_cache.cpu().numpy(), o.value_cache), f"{label}: V codes"
+    assert np.array_equal(c.key_scale.cpu().numpy().view(np.uint32),
+                          o.key_scale.view(np.uint32)), f"{label}: K scales"
+    assert np.array_equal(c.value_scale.cpu().numpy().view(np.uint32),
+                          o.value_scale.view(np.uint32)), f"{label}: V scales"
+    st = g.step
+    tbl = st.block_tables.cpu().numpy()
+    assert np.array_equal(tbl[:, : o.block_tables.shape[1]], o.block_tables), f"{label}: tables"
+
+
+def run_single(g, w):
+    out = torch.full((w.S, w.Hq, w.D), 0x7FFF, dtype=torch.int16, device="cuda")
+    c, st = g.cache, g.step
+    pa.pa_decode_int8(out, g.q, c.key_cache, c.value_cache, c.key_scale, c.value_scale,
+                      st.block_tables, st.context_lens, int(w.lengths.max()), w.scale, w.dtype)
+    torch.cuda.synchronize()
+    return gpu_side.to_host16(out)
+
+
+def run_partitioned(g, w, P, listed=False):
+    mcl = int(w.lengths.max())
+    ws = torch.empty(max(pa.pa_decode_partitioned_workspace_size(w.S, w.Hq, w.D, mcl, P), 16),
+                     dtype=torch.uint8, device="cuda")
+    out = torch.full((w.S, w.Hq, w.D), 0x7FFF, dtype=torch.int16, device="cuda")
+    c, st = g.cache, g.step
+    items = None
+    if listed:
+        items = torch.from_numpy(pa.partition_work_items(w.lengths, P)[::-1].copy()).cuda()
+    pa.pa_decode_partitioned_int8(out, g.q, c.key_cache, c.value_cache, c.key_scale,
+                                  c.value_scale, st.block_tables, st.context_lens, mcl, w.scale,
+                                  w.dtype, P, ws, items)
+    torch.cuda.synchronize()
+    return gpu_side.to_host16(out)
+
+
+def oracle_decode(o, w, pairs=None):
+    return oracle.decode_int8(o.q, o.key_cache, o.value_cache, o.key_scale, o.value_scale,
+                              o.block_tables, o.context_lens, w.scale, w.dtype, pairs=pairs,
+                              nthreads=0)
+
+
+SMALL = [(1, None), (2, None), (3, None), (4, None), (5, 16), (5, 32)]
+
+
+@pytest.mark.parametrize("cfg,bs", SMALL, ids=[f"cfg{c}-bs{b or 16}" for c, b in SMALL])
+def test_int8_small_workloads(cfg, bs):
+    w = workload(cfg, "small", **({"block_size": bs} if bs else {}))
+    label = f"int8 cfg{cfg} small bs{w.bs}"
+    print(f"\n[{label}] S={w.S} Hq={w.Hq} Hkv={w.Hkv} D={w.D} {w.dtype} lens={w.lengths.tolist()}",
+          flush=True)
+    g = gpu_side.build(w, kv_dtype="int8")
+    o = oracle_side.build_int8(w)
+    check_pools(g, o, label)
+    ref32, refT = oracle_decode(o, w)
+    check_outputs(run_single(g, w), ref32, refT, w.dtype, label + " single")
+    for P in sorted({w.bs, 3 * w.bs, 512}):
+        check_outputs(run_partitioned(g, w, P), ref32, refT, w.dtype, label + f" P={P}")
+        check_outputs(run_partitioned(g, w, P, listed=True), ref32, refT, w.dtype,
+                      label + f" P={P} listed")
+    del g
+    free_gpu()
+
+
+EDGE = [
+    # Hq, Hkv, D, bs, dtype
+    (4, 4, 64, 16, "f16"),        # MHA, D 64
+    (8, 1, 128, 16, "bf16"),      # MQA, G = 8 (narrow lanes)
+    (14, 2, 128, 32, "bf16"),     # G = 7, bs 32
+    (6, 2, 64, 16, "f16"),        # G = 3, D 64
+    (10, 2, 128, 16, "f16"),      # G = 5, f16 (narrow lanes)
+    (8, 2, 128, 16, "bf16"),      # G = 4 (wide lanes)
+    (24, 2, 128, 16, "bf16"),     # G = 12: two head chunks of 6
+]
+
+
+@pytest.mark.parametrize("Hq,Hkv,D,bs,dtype", EDGE,
+                         ids=[f"hq{a}-hkv{b}-d{c}-bs{d}-{e}" for a, b, c, d, e in EDGE])
+def test_int8_edge_lengths(Hq, Hkv, D, bs, dtype):
+    P = 4 * bs
+    lens = (1, bs - 1, bs, bs + 1, P - 1, P, P + 1, 2 * P, 2 * P + 3, 5 * P - 1)
+    s = spec(1, "full", num_seqs=len(lens), num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+             block_size=bs, dtype=dtype, fixed_lengths=lens, num_blocks=0, seed=31 + Hq)
+    w = make_workload(s)
+    label = f"int8 edge Hq{Hq} Hkv{Hkv} D{D} bs{bs} {dtype}"
+    print(f"\n[{label}] lens={list(lens)}", flush=True)
+    g = gpu_side.build(w, kv_dtype="int8")
+    o = oracle_side.build_int8(w)
+    check_pools(g, o, label)
+    ref32, refT = oracle_decode(o, w)
+    check_outputs(run_single(g, w), ref32, refT, dtype, label + " single")
+    for PP in (bs, P, 1024):
+        check_outputs(run_partitioned(g, w, PP), ref32, refT, dtype, label + f" P={PP}")
+        check_outputs(run_partitioned(g, w, PP, listed=True), ref32, refT, dtype,
+                      label + f" P={PP} listed")
+    del g
+    free_gpu()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_int8_quantisation_edge_rows(dtype):
+    """Zero rows, exact ties, scaled integers, tiny and huge magnitudes, inf and
+    NaN rows, a padding slot: codes and scales bit-exact against the oracle."""
+    hkv, d, bs, nb = 2, 128, 16, 4
+    rng = np.random.default_rng(41)
+    big = 60000.0 if dtype == "f16" else 1e30
+    tiny = 1e-6 if dtype == "f16" else 1e-30
+    rows = [np.zeros(d), np.r_[127.0, 2.5, 3.5, -2.5, -0.5, 0.5, 1.5, -1.5, np.zeros(d - 8)],
+            rng.integers(-127, 128, d) * 0.25, rng.standard_normal(d) * tiny,
+            rng.standard_normal(d) * big / 8, np.r_[np.inf, np.ones(d - 1)],
+            np.r_[np.nan, np.ones(d - 1)], rng.standard_normal(d),
+            # an fp32-subnormal scale (bf16 only; f16 has no such magnitudes)
+            rng.standard_normal(d) * (1e-37 if dtype == "bf16" else 1.0), rng.standard_normal(d)]
+    rows[2][7] = 127 * 0.25
+    x = np.stack(rows).astype(np.float32)
+    bits = oracle.narrow(x, dtype)
+    n = len(rows) // hkv
+    key = bits.reshape(n, hkv, d)
+    value = bits[::-1].copy().reshape(n, hkv, d)
+    slots = np.array([5, 17, 40, -1, 63], np.int64)[:n]
+    kc = np.full((nb, bs, hkv, d), -128, np.int8); vc = kc.copy()
+    ks = np.full((nb, hkv, bs), np.nan, np.float32); vs = ks.copy()
+    oracle.cache_write_int8(key, value, kc, vc, ks, vs, slots, dtype)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    gkc, gvc = dev(np.full_like(kc, -128)), dev(np.full_like(vc, -128))
+    gks, gvs = dev(np.full_like(ks, np.nan)), dev(np.full_like(vs, np.nan))
+    pa.pa_reshape_and_cache_int8(dev(key.view(np.int16)), dev(value.view(np.int16)), gkc, gvc,
+                                 gks, gvs, dev(slots), dtype)
+    torch.cuda.synchronize()
+    assert np.array_equal(gkc.cpu().numpy(), kc) and np.array_equal(gvc.cpu().numpy(), vc)
+    assert np.array_equal(gks.cpu().numpy().view(np.uint32), ks.view(np.uint32))
+    assert np.array_equal(gvs.cpu().numpy().view(np.uint32), vs.view(np.uint32))
+
+
+@pytest.mark.timeout(600)
+def test_int8_full_size_sampled():
+    """The Qwen2.5-7B-shaped layer (64 sequences, 28q/4kv, bf16, P = 512) over
+    INT8 pools through the engine, sampled outputs against the oracle."""
+    w = workload(3, "full")
+    label = "int8 cfg3 full"
+    print(f"\n[{label}] S={w.S} blocks={w.num_blocks}", flush=True)
+    g = gpu_side.build(w, kv_dtype="int8")
+    out = g.step.attend(g.q)
+    torch.cuda.synchronize()
+    got = gpu_side.to_host16(out)
+    print(f"[{label}] GPU done", flush=True)
+    o = oracle_side.build_int8(w)
+    check_pools(g, o, label)
+    del g
+    free_gpu()
+    rng = np.random.default_rng(3)
+    order = np.argsort(w.lengths)
+    seqs = sorted(set([int(order[0]), int(order[-1]), int(order[len(order) // 2])] +
+                      [int(x) for x in rng.choice(w.S, 5, replace=False)]))
+    pairs = np.array([[i, h] for i in seqs for h in rng.choice(w.Hq, 3, replace=False)], np.int32)
+    ref32, refT = oracle_decode(o, w, pairs)
+    check_outputs(np.stack([got[i, h] for i, h in pairs]), ref32, refT, w.dtype, label + " sampled")
+    allv = oracle.widen(got, w.dtype)
+    assert np.isfinite(allv).all() and np.abs(allv).max() <= 8.0
+
+
+def test_int8_engine_steps_with_copy_on_write():
+    """Several engine steps over INT8 pools (the one-launch step write
+    quantises each new token), with a fork whose shared partial block is
+    copied (codes and scales) before the first append lands in it."""
+    from paged_kv_cache_106_amd.engine import DecodeStep
+    w = workload(1, "full")
+    g = gpu_side.build(w, kv_dtype="int8", extra_tokens=8)
+    o = oracle_side.build_int8(w)
+    model, _ = oracle_side.replay(w)
+    g.cache.allocator.fork(3, 4)
+    model.fork(3, 4)
+    ids = np.arange(5)
+    step = DecodeStep(g.cache, ids, w.Hq, "partitioned", 32, max_context_len=64, scale=w.scale)
+    rng = np.random.default_rng(8)
+    q_all = np.concatenate([o.q, o.q[3:4]])
+    for k in range(3):
+        kn = oracle.narrow(rng.standard_normal((5, w.Hkv, w.D)).astype(np.float32), w.dtype)
+        vn = oracle.narrow(rng.standard_normal((5, w.Hkv, w.D)).astype(np.float32), w.dtype)
+        out = step(gpu_side.dev16(q_all), gpu_side.dev16(kn), gpu_side.dev16(vn))
+        torch.cuda.synchronize()
+        slots = []
+        for i in ids:
+            slot, cow = model.append_slot(int(i))
+            if cow is not None:
+                for a in (o.key_cache, o.value_cache):
+                    a[cow[1]] = a[cow[0]]
+                for a in (o.key_scale, o.value_scale):
+                    a[cow[1]] = a[cow[0]]
+            slots.append(slot)
+        oracle.cache_write_int8(kn, vn, o.key_cache, o.value_cache, o.key_scale, o.value_scale,
+                                np.array(slots, np.int64), w.dtype)
+        bt = oracle_side.tables_of(model, 5, step.mb)
+        cl = np.array([model.num_tokens[int(i)] for i in ids], np.int32)
+        assert np.array_equal(step.block_tables.cpu().numpy(), bt)
+        assert np.array_equal(g.cache.key_cache.cpu().numpy(), o.key_cache)
+        assert np.array_equal(g.cache.value_scale.cpu().numpy().view(np.uint32),
+                              o.value_scale.view(np.uint32))
+        ref32, refT = oracle.decode_int8(q_all, o.key_cache, o.value_cache, o.key_scale,
+                                         o.value_scale, bt, cl, w.scale, w.dtype)
+        check_outputs(gpu_side.to_host16(out), ref32, refT, w.dtype, f"int8 engine step {k}")
+    del g, step
+    free_gpu()
