@@ -72,6 +72,9 @@ def lib():
         L.pao_decode.restype = i32
         L.pao_decode_partitioned.argtypes = [f32p, u16p] + common + [i32]
         L.pao_decode_partitioned.restype = i32
+        L.pao_prefill.argtypes = [f32p, u16p, u16p, u16p, u16p, i32p, i32, i32p, i32p, i32, i32,
+                                  i32, i32, i32, i32, ctypes.c_float, i32, i32]
+        L.pao_prefill.restype = i32
         i8p = ctypes.POINTER(ctypes.c_int8)
         L.pao_quantize_rows.argtypes = [u16p, i64, i32, i32, i8p, f32p]
         L.pao_quantize_rows.restype = i32
@@ -238,6 +241,34 @@ def decode_partitioned(q, key_cache, value_cache, block_tables, context_lens, sc
         _ptr(key_cache, ctypes.c_uint16), _ptr(value_cache, ctypes.c_uint16),
         _ptr(block_tables, ctypes.c_int32), mb, _ptr(context_lens, ctypes.c_int32),
         s, hq, hkv, d, bs, nb, float(scale), DTYPES[dtype], int(partition_size)))
+    return out_f32, out_t
+
+
+# -- multi-token (chunked-prefill) attention -----------------------------------------------
+
+def prefill(q, key_cache, value_cache, block_tables, context_lens, query_start, scale, dtype,
+            nthreads=1):
+    """Causal attention of each sequence's query chunk (its last n_i cached
+    tokens) over its paged cache.  q [T][Hq][D] u16; query_start int32 [S+1].
+    Returns (out_f32 [T][Hq][D], out_t [T][Hq][D] u16)."""
+    _need(q, np.uint16, "q"); _need(key_cache, np.uint16, "key_cache")
+    _need(value_cache, np.uint16, "value_cache")
+    _need(block_tables, np.int32, "block_tables"); _need(context_lens, np.int32, "context_lens")
+    _need(query_start, np.int32, "query_start")
+    T, hq, d = q.shape
+    nb, bs, hkv, d2 = key_cache.shape
+    s = context_lens.shape[0]
+    if d2 != d or value_cache.shape != key_cache.shape or block_tables.shape[0] != s or \
+            query_start.shape != (s + 1,) or int(query_start[-1]) != T:
+        raise ValueError("shape mismatch")
+    out_f32 = np.empty((T, hq, d), np.float32)
+    out_t = np.empty((T, hq, d), np.uint16)
+    _check(lib().pao_prefill(
+        _ptr(out_f32, ctypes.c_float), _ptr(out_t, ctypes.c_uint16), _ptr(q, ctypes.c_uint16),
+        _ptr(key_cache, ctypes.c_uint16), _ptr(value_cache, ctypes.c_uint16),
+        _ptr(block_tables, ctypes.c_int32), block_tables.shape[1],
+        _ptr(context_lens, ctypes.c_int32), _ptr(query_start, ctypes.c_int32), s, hq, hkv, d, bs,
+        nb, float(scale), DTYPES[dtype], int(nthreads)))
     return out_f32, out_t
 
 

@@ -396,6 +396,65 @@ int32_t pao_decode_partitioned(float* out_f32, uint16_t* out_t,
 }
 
 // ---------------------------------------------------------------------------
+// Multi-token (chunked-prefill) attention over the paged cache.  Sequence i
+// holds L_i tokens in the cache, the last n_i of which are its query chunk
+// (written before the attention); query token k of the chunk sits at
+// position p = L_i - n_i + k and attends causally to tokens 0 .. p:
+//   out[k][h] = sum_{j <= p} softmax_j(scale * q[k][h] . K[j]) V[j]
+// i.e. the decode definition above with context length p + 1.
+// query_start [s + 1]: the chunk of sequence i is rows [query_start[i],
+// query_start[i + 1]) of q / out ([T][hq][d]).
+// ---------------------------------------------------------------------------
+
+int32_t pao_prefill(float* out_f32, uint16_t* out_t, const uint16_t* q,
+                    const uint16_t* key_cache, const uint16_t* value_cache,
+                    const int32_t* block_tables, int32_t mb, const int32_t* context_lens,
+                    const int32_t* query_start, int32_t s, int32_t hq, int32_t hkv, int32_t d,
+                    int32_t bs, int32_t nb, float scale, int32_t dtype, int32_t nthreads) {
+  if (!shapes_ok(s, hq, hkv, d, bs, nb, mb, dtype) || !query_start || query_start[0] != 0)
+    return PAO_BAD_ARG;
+  for (int32_t i = 0; i < s; ++i) {
+    const int32_t n = query_start[i + 1] - query_start[i];
+    if (n < 0 || n > context_lens[i] || context_lens[i] > static_cast<int64_t>(mb) * bs)
+      return PAO_BAD_LEN;
+  }
+  const int32_t G = hq / hkv;
+  const int32_t rows = query_start[s];
+  int32_t T = nthreads > 0 ? nthreads
+                           : static_cast<int32_t>(std::thread::hardware_concurrency());
+  T = std::max(1, std::min(T, std::max(rows * hq, 1)));
+  std::atomic<int32_t> next(0), status(PAO_OK);
+  auto worker = [&]() {
+    for (int32_t job; (job = next.fetch_add(1)) < rows * hq;) {
+      const int32_t row = job / hq, h = job % hq;
+      int32_t i = 0;
+      while (query_start[i + 1] <= row) ++i;
+      const int32_t n = query_start[i + 1] - query_start[i];
+      const int32_t pos = context_lens[i] - n + (row - query_start[i]);
+      const int32_t L = pos + 1;
+      std::vector<float> K(static_cast<size_t>(L) * d), V(static_cast<size_t>(L) * d), qf(d);
+      const int32_t rc = pao_gather(K.data(), V.data(), key_cache, value_cache,
+                                    block_tables + static_cast<int64_t>(i) * mb, L,
+                                    h / G /* kv head */, hkv, d, bs, nb, dtype);
+      if (rc != PAO_OK) {
+        status.store(rc);
+        continue;
+      }
+      const int64_t at = (static_cast<int64_t>(row) * hq + h) * d;
+      for (int32_t e = 0; e < d; ++e) qf[e] = widen(q[at + e], dtype);
+      attend(out_f32 + at, qf, K, V, L, d, scale);
+      if (out_t)
+        for (int32_t e = 0; e < d; ++e) out_t[at + e] = narrow(out_f32[at + e], dtype);
+    }
+  };
+  std::vector<std::thread> pool;
+  for (int32_t t = 1; t < T; ++t) pool.emplace_back(worker);
+  worker();
+  for (auto& th : pool) th.join();
+  return status.load();
+}
+
+// ---------------------------------------------------------------------------
 // INT8 KV cache.  The pages say only that quantising the KV cache to INT8
 // halves its bytes ("LLM推理优化技术地图：从KV Cache到量化与投机解码", §4.3);
 // the convention is this library's: symmetric, one fp32 scale per (token,

@@ -20,6 +20,11 @@
  *   - the gather of a sequence's K/V into contiguous logical order, then
  *     softmax(q K^T * scale) V in fp32 (first page, §二 formula and §4.1;
  *     paging changes no arithmetic, first page §九);
+ *   - multi-token (chunked-prefill) attention: several query tokens of a
+ *     sequence, the last tokens of its cache, each attending causally to the
+ *     tokens up to its own position (page "vLLM 深度拆解：当大模型推理学会
+ *     「分页注意力」", §2.3: prefill computes every prompt token at once, §5.1:
+ *     a long prompt's prefill cut into chunks that run between decode steps);
  *   - the split-context form (partial max / sum / accumulator per partition,
  *     then the log-sum-exp merge), used only to check itself against the
  *     single-pass form (first page §4.1, "partial accumulate, then merge");
@@ -122,6 +127,17 @@ int32_t pao_decode_partitioned(float* out_f32, uint16_t* out_t,
                                int32_t hq, int32_t hkv, int32_t d, int32_t bs,
                                int32_t nb, float scale, int32_t dtype,
                                int32_t partition_size);
+
+/* Multi-token (chunked-prefill) attention: for each sequence i, the last
+ * n_i = query_start[i+1] - query_start[i] of its context_lens[i] cached
+ * tokens are its query chunk; query row query_start[i] + k (position
+ * context_lens[i] - n_i + k) attends causally to tokens 0 .. that position.
+ * q / out_f32 / out_t: [query_start[s]][hq][d]; query_start: [s + 1], from 0. */
+int32_t pao_prefill(float* out_f32, uint16_t* out_t, const uint16_t* q,
+                    const uint16_t* key_cache, const uint16_t* value_cache,
+                    const int32_t* block_tables, int32_t mb, const int32_t* context_lens,
+                    const int32_t* query_start, int32_t s, int32_t hq, int32_t hkv, int32_t d,
+                    int32_t bs, int32_t nb, float scale, int32_t dtype, int32_t nthreads);
 
 /* INT8 KV: quantise rows [rows][d] of 16-bit values into codes [rows][d]
  * and scales [rows] (the convention above). */

@@ -34,6 +34,9 @@ MUTATIONS = [
      "const int64_t sdst = (blk * bs + off) * hkv + g;", "int8_cache_write or int8_decode"),
     ("int8 dequant drops the scale", "ks * static_cast<float>(key_cache[row + e])",
      "static_cast<float>(key_cache[row + e])", "int8_decode"),
+    ("prefill position one early", "const int32_t pos = context_lens[i] - n + (row - query_start[i]);",
+     "const int32_t pos = context_lens[i] - n + (row - query_start[i]) - 1;", "prefill"),
+    ("prefill kv head h % hkv", "h / G /* kv head */", "h % hkv /* kv head */", "prefill"),
     ("int8 V scale from K", "const float vs = value_scale[(blk * hkv + g) * bs + off];",
      "const float vs = key_scale[(blk * hkv + g) * bs + off];", "int8_decode"),
 ]

@@ -636,3 +636,65 @@ def test_int8_decode_pairs_and_poison():
                                    nthreads=2)
     for n, (i, h) in enumerate(pairs):
         assert np.array_equal(sub[n], full[i, h]) and np.array_equal(subT[n], fullT[i, h])
+
+
+# ---------------------------------------------------------------------------
+# multi-token (chunked-prefill) attention
+# ---------------------------------------------------------------------------
+
+PREFILL_CASES = [
+    # Hq, Hkv, D, bs, lens, chunk sizes, dtype
+    (4, 4, 8, 16, [1, 17, 40], [1, 5, 40], "f16"),          # MHA; a whole 40-token prompt
+    (8, 2, 64, 16, [33, 64, 20], [33, 16, 1], "bf16"),      # G = 4; first chunk of a prompt
+    (7, 1, 64, 32, [50, 9], [17, 9], "bf16"),              # MQA, G = 7, bs 32
+]
+
+
+@pytest.mark.parametrize("case", PREFILL_CASES)
+def test_prefill_matches_fp64_causal_brute_force(case):
+    Hq, Hkv, D, bs, lens, chunks, dtype = case
+    rng = np.random.default_rng(hash(str(case)) % (1 << 31) + 11)
+    S = len(lens)
+    _, kc, vc, bt, cl, Ks, Vs = tiny_case(rng, S, Hq, Hkv, D, bs, lens, dtype)
+    qs = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
+    q = to_bits(rng.standard_normal((int(qs[-1]), Hq, D)).astype(np.float32), dtype)
+    scale = 1.0 / math.sqrt(D)
+    out32, outT = oracle.prefill(q, kc, vc, bt, cl, qs, scale, dtype, nthreads=2)
+    G = Hq // Hkv
+    for i in range(S):
+        K, V = ref_widen64(Ks[i], dtype), ref_widen64(Vs[i], dtype)
+        for k in range(chunks[i]):
+            pos = lens[i] - chunks[i] + k
+            row = qs[i] + k
+            qq = ref_widen64(q[row], dtype)
+            for h in range(Hq):
+                sc = np.float64(np.float32(scale)) * (K[: pos + 1, h // G] @ qq[h])
+                p = np.exp(sc - sc.max())
+                ref = (p @ V[: pos + 1, h // G]) / p.sum()
+                assert np.abs(out32[row, h] - ref).max() <= 1e-5 * max(1.0, np.abs(ref).max()), \
+                    (i, k, h)
+    assert np.array_equal(outT, oracle.narrow(out32, dtype))
+
+
+def test_prefill_first_row_and_single_token_chunks():
+    """A whole prompt's first row sees only key 0 (its output is V[0]
+    exactly); chunks of one token are decode steps, bit for bit."""
+    rng = np.random.default_rng(13)
+    lens = [30, 7, 16]
+    qd, kc, vc, bt, cl, Ks, Vs = tiny_case(rng, 3, 4, 2, 64, 16, lens, "bf16")
+    qs = np.array([0, 30, 31, 32], np.int32)          # whole first prompt, then 1-token chunks
+    q = np.concatenate([to_bits(rng.standard_normal((30, 4, 64)).astype(np.float32), "bf16"),
+                        qd[1:]])
+    out32, outT = oracle.prefill(q, kc, vc, bt, cl, qs, 0.125, "bf16")
+    for h in range(4):
+        assert np.array_equal(outT[0, h], Vs[0][0, h // 2])
+    dec32, _ = oracle.decode(qd, kc, vc, bt, cl, 0.125, "bf16")
+    assert np.array_equal(out32[30:32].view(np.uint32), dec32[1:3].view(np.uint32))
+
+
+def test_prefill_rejects_bad_chunks():
+    rng = np.random.default_rng(14)
+    qd, kc, vc, bt, cl, _, _ = tiny_case(rng, 2, 4, 2, 64, 16, [5, 9], "f16")
+    q = np.zeros((12, 4, 64), np.uint16)
+    with pytest.raises(oracle.OracleError):                # a chunk longer than its sequence
+        oracle.prefill(q, kc, vc, bt, cl, np.array([0, 6, 12], np.int32), 0.125, "f16")
