@@ -7,6 +7,7 @@ single pass, by workload).  Inputs are synthetic and seeded (workloads/),
 resident in HBM before the timed region.
 
     python bench.py [--steps K] [--warmup W] [--config 3] [--block-size 16] [--kv-dtype int8]
+    python bench.py --prefill [--steps K] [--warmup W]     (chunked-prefill attention)
 
 Prints one JSON line on stdout.  value = algorithmic K/V bytes read by the
 timed steps' decodes / wall time of the timed steps (GB/s); the decode call
@@ -72,10 +73,94 @@ def cpu_baseline(w, budget_s, int8=False):
         "kind": "oracle",
         "sample": (f"{nseq} sequence decodes drawn cyclically from the workload's {w.S} "
                    f"(all {w.Hq} q heads each, {ntok} tokens), {spent:.1f} s of oracle time; "
-                   ("stored K/V bytes (codes + scales)" if int8 else "logical K/V bytes") +
-                   " of the sample / oracle decode time"),
+                   + ("stored K/V bytes (codes + scales)" if int8 else "logical K/V bytes")
+                   + " of the sample / oracle decode time"),
         "seqs_per_s": nseq / spent,
     }
+
+
+PREFILL_METRIC = "chunked-prefill attention TFLOP/s (causal, % of bf16 MFMA peak)"
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 / fp16 matrix peak, AMD's published figure
+
+
+def prefill_cpu_baseline(w, budget_s):
+    """The oracle's prefill on the last r query rows of every chunk (the same
+    positions as in the workload), r doubling until about budget_s seconds."""
+    import oracle
+    from tests.test_gpu_parity_prefill import build_oracle
+    from workloads import prefill_workload
+
+    kc, vc, bt = build_oracle(w)
+    threads = len(os.sched_getaffinity(0))
+    r = 1
+    while True:
+        sub = prefill_workload("full", chunks=tuple(min(r, int(n)) for n in w.chunks))
+        q = sub.query()
+        t0 = time.perf_counter()
+        oracle.prefill(q, kc, vc, bt, w.lengths, sub.query_start, w.scale, w.dtype,
+                       nthreads=threads)
+        spent = time.perf_counter() - t0
+        if spent > budget_s / 3 or r >= int(w.chunks.max()):
+            break
+        r *= 2
+    return {"value": sub.flops() / spent / 1e12, "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": (f"the last {r} query rows of each of the {w.S} chunks (all {w.Hq} heads, "
+                       f"{sub.T} rows), {spent:.1f} s of oracle time; causal FLOPs of the sample / "
+                       "oracle time")}
+
+
+def run_prefill(args):
+    import torch
+    from paged_kv_cache_106_amd import pa_prefill
+    from paged_kv_cache_106_amd._hip import Event
+    from tests.test_gpu_parity_prefill import build_gpu, dev
+    from workloads import prefill_workload
+
+    w = prefill_workload("full")
+    log(f"[bench] {w.spec.name}; rows={w.T}; {w.flops() / 1e9:.1f} GFLOP per call")
+    kc, vc, bt, lens, qs, _ = build_gpu(w)
+    q = dev(w.query())
+    out = torch.empty((w.T, w.Hq, w.D), dtype=torch.int16, device="cuda")
+    mql = int(w.chunks.max())
+    for _ in range(args.warmup):
+        pa_prefill(out, q, kc, vc, bt, lens, qs, mql, w.scale, w.dtype)
+    torch.cuda.synchronize()
+    ev = [(Event(timing=True), Event(timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for a, b in ev:
+        pa_prefill(out, q, kc, vc, bt, lens, qs, mql, w.scale, w.dtype, start_event=a, stop_event=b)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    t = np.array([a.elapsed_time(b) for a, b in ev]) * 1e-3
+    fl = w.flops()
+    value = fl * args.steps / elapsed / 1e12
+    achieved = fl / float(t.mean()) / 1e12
+    result = {
+        "metric": PREFILL_METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "accumulate": "f32",
+        "data": "synthetic (seeded N(0,1) q/k/v, seeded block scatter)",
+        "config": {"workload": w.spec.name, "num_seqs": w.S, "query_rows": w.T,
+                   "num_q_heads": w.Hq, "num_kv_heads": w.Hkv, "head_dim": w.D,
+                   "block_size": w.bs, "flops_per_call": fl,
+                   "flops_counting": "4 x head_dim per (query row, head, visible key)"},
+        "prefill_us": round(float(t.mean()) * 1e6, 2),
+        "prefill_us_p10_p90": [round(float(np.percentile(t, 10)) * 1e6, 2),
+                               round(float(np.percentile(t, 90)) * 1e6, 2)],
+        "query_tokens_per_s": round(w.T / float(t.mean()), 1),
+        "roofline": {"bound": "mfma", "kernel": "pa_prefill: prefill_kernel",
+                     "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": None},
+    }
+    del kc, vc
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a sample")
+        result["cpu_baseline"] = prefill_cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
 
 
 def kernel_source_sha256():
@@ -123,6 +208,8 @@ def main():
     ap.add_argument("--block-size", type=int, default=None, choices=[16, 32])
     ap.add_argument("--kv-dtype", default=None, choices=["int8"],
                     help="INT8 KV pools (codes + fp32 row scales) instead of 16-bit ones")
+    ap.add_argument("--prefill", action="store_true",
+                    help="time the chunked-prefill attention (pa_prefill) instead of a decode step")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--gc", dest="no_gc", action="store_false",
@@ -152,6 +239,8 @@ def main():
         print(json.dumps({"copy_calibration_bytes_read": 1 << 30, "bytes_written": 1 << 30,
                           "launches": 5}), flush=True)
         return
+    if args.prefill:
+        return run_prefill(args)
     overrides = {"block_size": args.block_size} if args.block_size else {}
     w = workload(args.config, "full", **overrides)
     log(f"[bench] {w.spec.name}; bs={w.bs}; S={w.S}; KV bytes/step ~{w.kv_bytes()/1e6:.1f} MB")

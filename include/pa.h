@@ -267,6 +267,37 @@ pa_status pa_copy_blocks(void* key_cache, void* value_cache,
                          pa_dtype dtype, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Multi-token (chunked-prefill) attention.
+ * Follows: "vLLM 深度拆解：当大模型推理学会「分页注意力」", §2.3 (prefill
+ * computes every prompt token at once) and §5.1 (chunked prefill: a long
+ * prompt's prefill cut into chunks that run between decode steps), over the
+ * paged cache of "LLM推理优化：vLLM PagedAttention深度解析与工程实践", §4.1.
+ * Sequence i holds context_lens[i] tokens in the cache; its last
+ * n_i = query_start[i+1] - query_start[i] tokens are its query chunk (their
+ * K/V written before this call, e.g. by pa_reshape_and_cache).  Query row
+ * query_start[i] + k (position context_lens[i] - n_i + k) attends causally
+ * to tokens 0 .. its position:
+ *   out[row][h] = sum_{j <= pos} softmax_j(scale * q[row][h] . K[j]) V[j]
+ *   query, out     [num_query_tokens][num_q_heads][head_dim] 16-bit
+ *   query_start    [num_seqs + 1] int32 device array, query_start[0] = 0
+ *   max_query_len  >= every n_i (sizes the grid; longer chunks are cut)
+ * Other arguments as for pa_decode.  Products run on the matrix cores with
+ * fp32 accumulation; the softmax weights enter the P.V product as a 16-bit
+ * part plus a 16-bit remainder (about 17 significant bits).  A chunk longer
+ * than its context, or rows outside [0, num_query_tokens), are skipped on
+ * the device (their outputs are left unwritten).
+ * ---------------------------------------------------------------------- */
+pa_status pa_prefill(void* out, const void* query, const void* key_cache,
+                     const void* value_cache, const int32_t* block_tables,
+                     int32_t max_blocks_per_seq, const int32_t* context_lens,
+                     const int32_t* query_start, int32_t num_seqs,
+                     int32_t num_query_tokens, int32_t max_query_len,
+                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                     int32_t block_size, int32_t num_blocks, float scale,
+                     pa_dtype dtype, hipStream_t stream, hipEvent_t start_event,
+                     hipEvent_t stop_event);
+
+/* ------------------------------------------------------------------------
  * INT8 KV cache.
  * Follows: "LLM推理优化技术地图：从KV Cache到量化与投机解码", §4.3 (quantising
  * the KV cache to INT8 halves its bytes; accuracy is model-dependent).  The

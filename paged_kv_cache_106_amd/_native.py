@@ -70,6 +70,8 @@ _DEC8 = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _
          _f32, _i32]
 _sig("pa_decode_int8", _i32, _DEC8 + [_vp, _vp, _vp])
 _sig("pa_decode_partitioned_int8", _i32, _DEC8 + [_i32, _vp, _i32, _vp, _sz, _vp, _vp, _vp])
+_sig("pa_prefill", _i32, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                          _i32, _i32, _i32, _f32, _i32, _vp, _vp, _vp])
 _sig("pa_copy_blocks_int8", _i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp])
 _sig("pa_alloc_create", _i32, [_i32, _i32, _i32p, ctypes.POINTER(_vp)])
 _sig("pa_alloc_destroy", None, [_vp])
@@ -363,6 +365,29 @@ def pa_copy_blocks_int8(key_cache, value_cache, key_scale, value_scale, block_pa
     _check(_lib.pa_copy_blocks_int8(*_q8_ptrs(key_cache, value_cache, key_scale, value_scale),
                                     _dptr(block_pairs, "block_pairs", 4) if n else None, n, hkv,
                                     d, bs, nb, _stream(stream)))
+
+
+def pa_prefill(out, query, key_cache, value_cache, block_tables, context_lens, query_start,
+               max_query_len, scale, dtype, stream=None, start_event=None, stop_event=None):
+    """Causal attention of each sequence's query chunk (its last n_i cached
+    tokens) over its paged cache.  query/out [T][Hq][D] 16-bit; query_start
+    int32 GPU tensor [S+1]; context_lens int32 [S]; block_tables int32 [S][MB]."""
+    t, hq, d = query.shape
+    nb, bs, hkv, d2 = key_cache.shape
+    if d2 != d or tuple(value_cache.shape) != tuple(key_cache.shape):
+        raise ValueError("cache shapes do not match the query")
+    if tuple(out.shape) != tuple(query.shape):
+        raise ValueError("out must have the query's shape")
+    s = context_lens.shape[0]
+    if block_tables.dim() != 2 or block_tables.shape[0] != s or tuple(query_start.shape) != (s + 1,):
+        raise ValueError("block_tables must be [S][MB] and query_start [S+1]")
+    _check(_lib.pa_prefill(
+        _dptr(out, "out", 2), _dptr(query, "query", 2), _dptr(key_cache, "key_cache", 2),
+        _dptr(value_cache, "value_cache", 2), _dptr(block_tables, "block_tables", 4),
+        block_tables.shape[1], _dptr(context_lens, "context_lens", 4),
+        _dptr(query_start, "query_start", 4), s, t, int(max_query_len), hq, hkv, d, bs, nb,
+        float(scale), _dtype_code(dtype), _stream(stream), _event(start_event),
+        _event(stop_event)))
 
 
 def partition_work_items(context_lens, partition_size, max_parts=None, out=None):

@@ -1,0 +1,410 @@
+// pa_prefill.hip -- multi-token (chunked-prefill) attention over the paged
+// cache, on the matrix cores of gfx950.
+//
+// Sequence i holds L_i tokens in the cache; its last n_i tokens are the
+// query chunk, written to the cache before this call.  Query token k of the
+// chunk sits at position p = L_i - n_i + k and attends causally to tokens
+// 0 .. p ("vLLM 深度拆解：当大模型推理学会「分页注意力」", §2.3: prefill
+// computes all prompt tokens at once; §5.1: chunked prefill cuts a long
+// prompt's prefill into pieces that run between decode steps; the paged
+// layout and the attention formula as for decode, "LLM推理优化：vLLM
+// PagedAttention深度解析与工程实践", §二 and §4.1).
+//
+// Rows are (query token, head of the group) pairs of one (sequence, KV head),
+// token-major: row r = k * G + h.  A workgroup of WAVES waves takes
+// 16 * WAVES consecutive rows; wave w's rows are the 16 "n" columns of its
+// matrix products.  The workgroup walks the keys [0, 1 + the largest position
+// among its rows) in tiles of 32: the tile's K rows go to LDS as they are,
+// its V rows transposed ([dim][key]), both read by every wave.  Per tile and
+// wave, in the transposed form that needs no transpose of Q or of the scores:
+//   S^T = K Q^T     v_mfma_f32_16x16x32 (A = 16 keys x 32 dims of K from LDS,
+//                   B = 32 dims x 16 rows of Q, resident in registers); the
+//                   result holds, in lane l, keys 4(l/16)+r of row l%16 ...
+//   online softmax  ... so each row's max and sum are a 4-lane exchange
+//                   (row swaps); masked keys (past the row's position) get
+//                   weight 0 by select;
+//   O^T += V^T P^T  v_mfma_f32_16x16x16 (A = 16 dims x 16 keys of V^T from
+//                   LDS, B = P^T straight from the S^T registers, whose
+//                   layout is this instruction's B layout).  P goes in as a
+//                   16-bit high part plus a 16-bit remainder, two products,
+//                   so the weights keep ~17 bits instead of 8.
+// Products of 16-bit values are exact in the fp32 accumulators; the output
+// is O / l rounded once to the 16-bit type.
+#include <hip/hip_ext.h>
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <type_traits>
+
+#include "pa.h"
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWavesP = 8;               // waves per workgroup
+constexpr int kThreadsP = 64 * kWavesP;
+constexpr int kRowsP = 16 * kWavesP;     // (token, head) rows per workgroup
+constexpr int kKeyTile = 32;             // keys per LDS tile
+
+// round-to-nearest-even narrowing and exact widening of the 16-bit types
+template <int DT>
+__device__ inline uint16_t narrow16(float x) {
+  if constexpr (DT == PA_F16) {
+    return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
+  } else {
+    const uint32_t u = __float_as_uint(x);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x0040u);
+    return static_cast<uint16_t>((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+  }
+}
+template <int DT>
+__device__ inline float widen16(uint16_t b) {
+  if constexpr (DT == PA_F16) return static_cast<float>(__builtin_bit_cast(_Float16, b));
+  else return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// 16 keys x 32 dims (A) times 32 dims x 16 rows (B), accumulated in c
+template <int DT>
+__device__ inline f32x4 mma_k32(uint4 a, uint4 b, f32x4 c) {
+  if constexpr (DT == PA_F16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+// 16 dims x 16 keys (A) times 16 keys x 16 rows (B)
+template <int DT>
+__device__ inline f32x4 mma_k16(uint2 a, uint2 b, f32x4 c) {
+  if constexpr (DT == PA_F16)
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
+                                                 __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                     __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+}
+
+// max / sum over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four lanes of one row)
+// with the CDNA4 row swaps: v_permlane16_swap(x, x) returns x[l] and
+// x[l ^ 16] in its two results, v_permlane32_swap x[l] and x[l ^ 32].
+__device__ inline float row4_max(float x) {
+  const uint32_t b = __float_as_uint(x);
+  const auto r16 = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+  x = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+  const uint32_t c = __float_as_uint(x);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(c, c, false, false);
+  return fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
+}
+__device__ inline float row4_sum(float x) {
+  const uint32_t b = __float_as_uint(x);
+  const auto r16 = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+  x = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+  const uint32_t c = __float_as_uint(x);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(c, c, false, false);
+  return __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
+}
+
+struct PrefillParams {
+  void* out;                   // [T][Hq][D] 16-bit
+  const void* q;               // [T][Hq][D] 16-bit
+  const void* k_cache;         // [NB][bs][Hkv][D]
+  const void* v_cache;
+  const int32_t* block_tables; // [S][mb]
+  const int32_t* context_lens; // [S]
+  const int32_t* query_start;  // [S + 1]
+  int32_t mb, num_seqs, num_tokens, max_query_len;
+  int32_t num_q_heads, num_kv_heads, group, block_size, num_blocks;
+  int32_t row_tiles;           // ceil(max_query_len * group / kRowsP)
+  float scale_log2;
+};
+
+// LDS: K tile [kKeyTile][D] with rows padded by 16 bytes (the 16 keys of an
+// A operand fall in different banks), V^T tile [D][kKeyTile] likewise.
+template <int D>
+struct PrefillLds {
+  static constexpr int KROW = D * 2 + 16;          // bytes per K row
+  static constexpr int VROW = kKeyTile * 2 + 16;   // bytes per V^T row
+  static constexpr int K_BYTES = kKeyTile * KROW;
+  static constexpr int BYTES = K_BYTES + D * VROW;
+};
+
+template <int DT, int D>
+__global__ __launch_bounds__(kThreadsP) void prefill_kernel(PrefillParams p) {
+  using L = PrefillLds<D>;
+  constexpr int KS = D / 32;          // k-steps of the S^T product
+  constexpr int DT_TILES = D / 16;    // 16-dim tiles of O^T
+  constexpr int CPK = D / 8;          // 16-byte chunks per K/V row
+  constexpr int CHUNKS = kKeyTile * CPK;
+  constexpr int LOADS = (CHUNKS + kThreadsP - 1) / kThreadsP;
+  __shared__ __attribute__((aligned(16))) char lds[L::BYTES];
+  char* k_lds = lds;
+  char* v_lds = lds + L::K_BYTES;
+
+  // blockIdx -> (sequence, KV head, row tile): the tiles of one (sequence,
+  // KV head) share blockIdx.x mod 8, hence an XCD and its L2
+  const int npairs = p.num_seqs * p.num_kv_heads;
+  const int id = blockIdx.x;
+  const int k8 = id >> 3;
+  const int pair = (k8 / p.row_tiles) * 8 + (id & 7);
+  const int tile = k8 % p.row_tiles;
+  if (pair >= npairs) return;                         // uniform: whole workgroup
+  const int seq = pair / p.num_kv_heads;
+  const int kvh = pair - seq * p.num_kv_heads;
+  const int G = p.group;
+
+  const int q0 = p.query_start[seq];
+  int L_ctx = p.context_lens[seq];
+  L_ctx = max(0, min(L_ctx, p.mb * p.block_size));
+  int n = p.query_start[seq + 1] - q0;
+  n = max(0, min(n, min(L_ctx, p.max_query_len)));
+  if (q0 < 0 || q0 + n > p.num_tokens) n = 0;
+  const int nrows = n * G;
+  const int r0 = tile * kRowsP;
+  if (r0 >= nrows) return;                            // uniform: whole workgroup
+  const int base_pos = L_ctx - n;                     // position of query token 0
+  const int last_row = min(r0 + kRowsP, nrows) - 1;
+  const int kend = base_pos + last_row / G + 1;       // keys this workgroup needs
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int lr = lane & 15;          // the row (n column) this lane serves
+  const int lg = lane >> 4;          // its group of 4 (k rows / keys)
+  const int row = r0 + wave * 16 + lr;
+  const bool row_ok = row < nrows;
+  const int rowc = row_ok ? row : nrows - 1;
+  const int tok = rowc / G;
+  const int head = kvh * G + (rowc - tok * G);
+  const int pos = base_pos + tok;
+  const int64_t qrow = static_cast<int64_t>(q0 + tok) * p.num_q_heads + head;
+
+  // Q^T operands: dims 8*lg + 32*ks .. +8 of this lane's row
+  uint4 qb[KS];
+  const uint16_t* qp = static_cast<const uint16_t*>(p.q) + qrow * D + 8 * lg;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) qb[ks] = *reinterpret_cast<const uint4*>(qp + 32 * ks);
+
+  const int32_t* bt = p.block_tables + static_cast<int64_t>(seq) * p.mb;
+  const uint4* kc = static_cast<const uint4*>(p.k_cache);
+  const uint4* vc = static_cast<const uint4*>(p.v_cache);
+  // chunk c of a tile: key c / CPK, dims 8 * (c % CPK) .. +8
+  auto load_tile = [&](int t, uint4 (&kr)[LOADS], uint4 (&vr)[LOADS]) {
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) {
+      const int c = tid + j * kThreadsP;
+      const int key = t * kKeyTile + c / CPK;
+      kr[j] = make_uint4(0, 0, 0, 0);
+      vr[j] = make_uint4(0, 0, 0, 0);
+      if (c < CHUNKS && key < kend) {
+        int blk = bt[key / p.block_size];
+        blk = static_cast<unsigned>(blk) < static_cast<unsigned>(p.num_blocks) ? blk : 0;
+        const int64_t at =
+            ((static_cast<int64_t>(blk) * p.block_size + key % p.block_size) * p.num_kv_heads +
+             kvh) * CPK + c % CPK;
+        kr[j] = kc[at];
+        vr[j] = vc[at];
+      }
+    }
+  };
+  auto store_tile = [&](const uint4 (&kr)[LOADS], const uint4 (&vr)[LOADS]) {
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) {
+      const int c = tid + j * kThreadsP;
+      if (c >= CHUNKS) continue;
+      const int key = c / CPK, col = c % CPK;
+      *reinterpret_cast<uint4*>(k_lds + key * L::KROW + col * 16) = kr[j];
+      const uint32_t w[4] = {vr[j].x, vr[j].y, vr[j].z, vr[j].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint16_t v = static_cast<uint16_t>(w[e / 2] >> (16 * (e & 1)));
+        *reinterpret_cast<uint16_t*>(v_lds + (col * 8 + e) * L::VROW + key * 2) = v;
+      }
+    }
+  };
+
+  f32x4 acc[DT_TILES];
+#pragma unroll
+  for (int dt = 0; dt < DT_TILES; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -__builtin_inff();
+  float l_lane = 0.f;                 // this lane's share of the row's sum
+
+  const int ntiles = (kend + kKeyTile - 1) / kKeyTile;
+  uint4 kr[LOADS], vr[LOADS];
+  load_tile(0, kr, vr);
+  for (int t = 0; t < ntiles; ++t) {
+    __syncthreads();                  // the previous tile is no longer read
+    store_tile(kr, vr);
+    __syncthreads();
+    if (t + 1 < ntiles) load_tile(t + 1, kr, vr);   // in flight during this tile
+
+    // S^T for keys t*32 + 16*mt + 4*lg + r of this lane's row
+    f32x4 s[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      s[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const uint4 a = *reinterpret_cast<const uint4*>(k_lds + (16 * mt + lr) * L::KROW +
+                                                        (8 * lg + 32 * ks) * 2);
+        s[mt] = mma_k32<DT>(a, qb[ks], s[mt]);
+      }
+    }
+    // online softmax of the row (base 2)
+    float x[8];
+    float tmax = -__builtin_inff();
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = t * kKeyTile + 16 * mt + 4 * lg + r;
+        const float v = key <= pos ? s[mt][r] * p.scale_log2 : -__builtin_inff();
+        x[4 * mt + r] = v;
+        tmax = fmaxf(tmax, v);
+      }
+    const float m_new = fmaxf(m_run, row4_max(tmax));
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 while m_run is -inf
+    m_run = m_new;
+    float psum = 0.f;
+    uint2 phi[2], plo[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      uint16_t h[4], lo[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float pr = x[4 * mt + r] == -__builtin_inff()
+                             ? 0.f : __builtin_amdgcn_exp2f(x[4 * mt + r] - m_new);
+        psum += pr;
+        h[r] = narrow16<DT>(pr);
+        lo[r] = narrow16<DT>(pr - widen16<DT>(h[r]));
+      }
+      phi[mt] = make_uint2(h[0] | (static_cast<uint32_t>(h[1]) << 16),
+                           h[2] | (static_cast<uint32_t>(h[3]) << 16));
+      plo[mt] = make_uint2(lo[0] | (static_cast<uint32_t>(lo[1]) << 16),
+                           lo[2] | (static_cast<uint32_t>(lo[3]) << 16));
+    }
+    l_lane = l_lane * alpha + psum;
+    // O^T = alpha O^T + V^T P^T
+#pragma unroll
+    for (int dt = 0; dt < DT_TILES; ++dt) {
+      f32x4 o = acc[dt] * alpha;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        const uint2 a = *reinterpret_cast<const uint2*>(v_lds + (16 * dt + lr) * L::VROW +
+                                                        (16 * mt + 4 * lg) * 2);
+        o = mma_k16<DT>(a, phi[mt], o);
+        o = mma_k16<DT>(a, plo[mt], o);
+      }
+      acc[dt] = o;
+    }
+  }
+
+  // out = O / l, dims 16*dt + 4*lg + r of this lane's row
+  const float l_row = row4_sum(l_lane);
+  if (row_ok) {
+    const float inv = 1.f / l_row;
+    uint16_t* op = static_cast<uint16_t*>(p.out) + qrow * D + 4 * lg;
+#pragma unroll
+    for (int dt = 0; dt < DT_TILES; ++dt) {
+      const uint32_t lo = narrow16<DT>(acc[dt][0] * inv) |
+                          (static_cast<uint32_t>(narrow16<DT>(acc[dt][1] * inv)) << 16);
+      const uint32_t hi = narrow16<DT>(acc[dt][2] * inv) |
+                          (static_cast<uint32_t>(narrow16<DT>(acc[dt][3] * inv)) << 16);
+      *reinterpret_cast<uint2*>(op + 16 * dt) = make_uint2(lo, hi);
+    }
+  }
+}
+
+bool aligned_p(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
+
+}  // namespace
+}  // namespace pa
+
+extern "C" pa_status pa_prefill(void* out, const void* query, const void* key_cache,
+                                const void* value_cache, const int32_t* block_tables,
+                                int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                const int32_t* query_start, int32_t num_seqs,
+                                int32_t num_query_tokens, int32_t max_query_len,
+                                int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                int32_t block_size, int32_t num_blocks, float scale,
+                                pa_dtype dtype, hipStream_t stream, hipEvent_t start_event,
+                                hipEvent_t stop_event) {
+  using pa::fail;
+  pa::clear_error();
+  if (dtype != PA_F16 && dtype != PA_BF16) return fail(PA_ERR_INVALID_ARG, "unknown dtype");
+  if (num_seqs < 0 || num_query_tokens < 0 || max_query_len < 0)
+    return fail(PA_ERR_INVALID_ARG, "negative count");
+  if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0)
+    return fail(PA_ERR_INVALID_ARG, "num_q_heads must be a positive multiple of num_kv_heads");
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PA_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (block_size <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0)
+    return fail(PA_ERR_INVALID_ARG, "block_size, num_blocks, max_blocks_per_seq must be positive");
+  if (static_cast<int64_t>(max_blocks_per_seq) * block_size > INT32_MAX)
+    return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq * block_size overflows int32");
+  if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale is not finite");
+  const int64_t group = num_q_heads / num_kv_heads;
+  const int64_t row_tiles = (static_cast<int64_t>(max_query_len) * group + pa::kRowsP - 1) /
+                            pa::kRowsP;
+  const int64_t pairs8 = (static_cast<int64_t>(num_seqs) * num_kv_heads + 7) / 8 * 8;
+  const int64_t blocks = pairs8 * row_tiles;
+  if (blocks > INT32_MAX) return fail(PA_ERR_UNSUPPORTED, "grid too large");
+  if (num_seqs == 0 || num_query_tokens == 0 || max_query_len == 0) {
+    for (hipEvent_t e : {start_event, stop_event})
+      if (e && hipEventRecord(e, stream) != hipSuccess)
+        return fail(PA_ERR_HIP, "pa_prefill: hipEventRecord failed");
+    return PA_OK;
+  }
+  if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens ||
+      !query_start)
+    return fail(PA_ERR_INVALID_ARG, "NULL device pointer");
+  if (!pa::aligned_p(out, 16) || !pa::aligned_p(query, 16) || !pa::aligned_p(key_cache, 16) ||
+      !pa::aligned_p(value_cache, 16) || !pa::aligned_p(block_tables, 4) ||
+      !pa::aligned_p(context_lens, 4) || !pa::aligned_p(query_start, 4))
+    return fail(PA_ERR_INVALID_ARG, "device buffers must be 16-byte aligned (metadata 4-byte)");
+  pa::PrefillParams p{};
+  p.out = out;
+  p.q = query;
+  p.k_cache = key_cache;
+  p.v_cache = value_cache;
+  p.block_tables = block_tables;
+  p.context_lens = context_lens;
+  p.query_start = query_start;
+  p.mb = max_blocks_per_seq;
+  p.num_seqs = num_seqs;
+  p.num_tokens = num_query_tokens;
+  p.max_query_len = max_query_len;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.group = static_cast<int32_t>(group);
+  p.block_size = block_size;
+  p.num_blocks = num_blocks;
+  p.row_tiles = static_cast<int32_t>(row_tiles);
+  p.scale_log2 = scale * 1.4426950408889634f;
+  const dim3 grid(static_cast<uint32_t>(blocks)), block(pa::kThreadsP);
+  if (dtype == PA_F16) {
+    if (head_dim == 64)
+      hipExtLaunchKernelGGL((pa::prefill_kernel<PA_F16, 64>), grid, block, 0, stream,
+                            start_event, stop_event, 0, p);
+    else
+      hipExtLaunchKernelGGL((pa::prefill_kernel<PA_F16, 128>), grid, block, 0, stream,
+                            start_event, stop_event, 0, p);
+  } else {
+    if (head_dim == 64)
+      hipExtLaunchKernelGGL((pa::prefill_kernel<PA_BF16, 64>), grid, block, 0, stream,
+                            start_event, stop_event, 0, p);
+    else
+      hipExtLaunchKernelGGL((pa::prefill_kernel<PA_BF16, 128>), grid, block, 0, stream,
+                            start_event, stop_event, 0, p);
+  }
+  const hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return fail(PA_ERR_HIP, hipGetErrorString(err));
+  return PA_OK;
+}

@@ -234,3 +234,18 @@ def test_int8_entry_points_reject_on_host():
              0, 2, 128, 16, 10, 1, None, None) == _native.PA_OK
     assert w(BAD, BAD, None, 0, BAD, BAD, None, BAD, 4, BAD, BAD, BAD, BAD, BAD, BAD,
              2, 2, 96, 16, 10, 1, None, None) == _native.PA_ERR_UNSUPPORTED
+
+
+def test_prefill_rejects_on_host():
+    f = L.pa_prefill
+    ok = [BAD, BAD, BAD, BAD, BAD, 4, BAD, BAD, 2, 10, 8, 8, 2, 128, 16, 10, 0.088, 1]
+    for idx, val, status in [(13, 96, _native.PA_ERR_UNSUPPORTED),     # head_dim
+                             (11, 7, _native.PA_ERR_INVALID_ARG),       # Hq not a multiple of Hkv
+                             (7, None, _native.PA_ERR_INVALID_ARG),     # NULL query_start
+                             (0, MIS, _native.PA_ERR_INVALID_ARG),      # misaligned out
+                             (17, 9, _native.PA_ERR_INVALID_ARG),       # dtype
+                             (16, float("nan"), _native.PA_ERR_INVALID_ARG)]:
+        bad = list(ok); bad[idx] = val
+        assert f(*bad, None, None, None) == status
+    empty = list(ok); empty[9] = 0                                      # no query tokens
+    assert f(*empty, None, None, None) == _native.PA_OK

@@ -1,0 +1,144 @@
+"""GPU parity of the multi-token (chunked-prefill) attention: libpa's
+pa_prefill (through the C ABI) against the oracle on the same seeded inputs.
+
+Each side builds its own state: libpa's allocator and cache write on the GPU,
+the allocator model and the oracle's cache write on the CPU; tables and pools
+are compared bit for bit, then the outputs to the bars of the decode tests
+(max|d| <= 1e-2 against the oracle's fp32 result, and within half an ulp of
+the 16-bit format plus 1e-4 of it).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_106_amd as pa
+from oracle.allocator_model import BlockManagerModel
+from workloads import POISON, prefill_workload
+from tests.test_gpu_parity import check_outputs, free_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def dev(a):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).cuda()
+
+
+def build_gpu(w):
+    a = pa.Allocator(w.num_blocks, w.bs, w.initial_free_order)
+    shape = (w.num_blocks, w.bs, w.Hkv, w.D)
+    kc = torch.full(shape, POISON[w.dtype], dtype=torch.int16, device="cuda")
+    vc = torch.full(shape, POISON[w.dtype], dtype=torch.int16, device="cuda")
+    for i in range(w.S):
+        a.allocate(i, int(w.lengths[i]))
+        slots = dev(a.slots(i, 0, int(w.lengths[i])))
+        pa.pa_reshape_and_cache(dev(w.tokens(i, "k")), dev(w.tokens(i, "v")), kc, vc, slots,
+                                w.dtype)
+    bt, lens = a.block_tables(np.arange(w.S), w.max_blocks_per_seq(), pad=0)
+    torch.cuda.synchronize()
+    return kc, vc, dev(bt), dev(lens), dev(w.query_start), bt
+
+
+def build_oracle(w):
+    m = BlockManagerModel(w.num_blocks, w.bs, w.initial_free_order)
+    shape = (w.num_blocks, w.bs, w.Hkv, w.D)
+    kc = np.full(shape, POISON[w.dtype], np.uint16)
+    vc = kc.copy()
+    bt = np.zeros((w.S, w.max_blocks_per_seq()), np.int32)
+    for i in range(w.S):
+        m.allocate(i, int(w.lengths[i]))
+        oracle.cache_write(w.tokens(i, "k"), w.tokens(i, "v"), kc, vc,
+                           np.array(m.slots(i, 0, int(w.lengths[i])), np.int64))
+        t = m.block_table(i)
+        bt[i, : len(t)] = t
+    return kc, vc, bt
+
+
+def run_gpu(w, kc, vc, bt, lens, qs, max_query_len=None):
+    q = dev(w.query())
+    out = torch.full((w.T, w.Hq, w.D), 0x7FFF, dtype=torch.int16, device="cuda")
+    pa.pa_prefill(out, q, kc, vc, bt, lens, qs,
+                  int(w.chunks.max()) if max_query_len is None else max_query_len,
+                  w.scale, w.dtype)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().view(np.uint16)
+
+
+CASES = [
+    dict(),                                                                   # 28q/4kv, D128, bf16
+    dict(num_q_heads=8, num_kv_heads=8, head_dim=64, dtype="f16"),            # MHA, D 64
+    dict(num_q_heads=32, num_kv_heads=8, block_size=32),                      # G = 4, bs 32
+    dict(num_q_heads=8, num_kv_heads=1, dtype="f16"),                         # MQA, G = 8
+    dict(num_q_heads=12, num_kv_heads=2, head_dim=64, contexts=(300, 47, 129, 5),
+         chunks=(300, 46, 64, 5)),                                            # G = 6, whole prompts
+]
+
+
+@pytest.mark.parametrize("over", CASES, ids=[str(i) for i in range(len(CASES))])
+def test_prefill_small(over):
+    w = prefill_workload("small", **over)
+    label = f"prefill Hq{w.Hq} Hkv{w.Hkv} D{w.D} bs{w.bs} {w.dtype}"
+    print(f"\n[{label}] contexts={w.lengths.tolist()} chunks={w.chunks.tolist()}", flush=True)
+    kc, vc, bt, lens, qs, bt_host = build_gpu(w)
+    okc, ovc, obt = build_oracle(w)
+    assert np.array_equal(bt_host, obt)
+    assert np.array_equal(kc.cpu().numpy().view(np.uint16), okc)
+    assert np.array_equal(vc.cpu().numpy().view(np.uint16), ovc)
+    got = run_gpu(w, kc, vc, bt, lens, qs)
+    ref32, refT = oracle.prefill(w.query(), okc, ovc, obt, w.lengths, w.query_start, w.scale,
+                                 w.dtype, nthreads=0)
+    check_outputs(got, ref32, refT, w.dtype, label)
+    # a grid sized for longer chunks changes nothing
+    got2 = run_gpu(w, kc, vc, bt, lens, qs, max_query_len=int(w.chunks.max()) + 200)
+    assert np.array_equal(got2, got)
+    del kc, vc
+    free_gpu()
+
+
+def test_prefill_empty_and_rejects():
+    w = prefill_workload("small")
+    kc, vc, bt, lens, qs, _ = build_gpu(w)
+    out = torch.zeros((1, w.Hq, w.D), dtype=torch.int16, device="cuda")
+    q = torch.zeros_like(out)
+    L = pa.lib()
+    # no query tokens: nothing is launched
+    assert L.pa_prefill(out.data_ptr(), q.data_ptr(), kc.data_ptr(), vc.data_ptr(), bt.data_ptr(),
+                        bt.shape[1], lens.data_ptr(), qs.data_ptr(), w.S, 0, 0, w.Hq, w.Hkv, w.D,
+                        w.bs, w.num_blocks, w.scale, pa.PA_BF16, None, None, None) == 0
+    with pytest.raises(ValueError):
+        pa.pa_prefill(out, q, kc, vc, bt, lens, qs[:-1], 4, w.scale, w.dtype)
+
+
+@pytest.mark.timeout(600)
+def test_prefill_full_size_sampled():
+    """The benchmark's chunked-prefill step (8 x 512-token chunks after up to
+    8192 cached tokens, Qwen2.5-7B-shaped), sampled rows against the oracle:
+    the expected value of a row at position p is the oracle's decode with
+    context length p + 1 over the same table row."""
+    w = prefill_workload("full")
+    label = "prefill full sampled"
+    kc, vc, bt, lens, qs, bt_host = build_gpu(w)
+    got = run_gpu(w, kc, vc, bt, lens, qs)
+    print(f"\n[{label}] GPU done", flush=True)
+    assert np.isfinite(oracle.widen(got, w.dtype)).all()
+    okc, ovc, obt = build_oracle(w)
+    assert np.array_equal(bt_host, obt)
+    del kc, vc
+    free_gpu()
+    rng = np.random.default_rng(5)
+    q = w.query()
+    rows = []
+    for i in range(w.S):
+        n = int(w.chunks[i])
+        rows += [(i, 0), (i, n - 1)] + [(i, int(k)) for k in rng.integers(0, n, 2)]
+    heads = rng.integers(0, w.Hq, len(rows))
+    qd = np.stack([q[w.query_start[i] + k] for i, k in rows])             # [R][Hq][D]
+    cl = np.array([int(w.lengths[i]) - int(w.chunks[i]) + k + 1 for i, k in rows], np.int32)
+    tbl = np.stack([obt[i] for i, _ in rows])
+    pairs = np.array([[r, h] for r, h in enumerate(heads)], np.int32)
+    ref32, refT = oracle.decode_pairs(qd, okc, ovc, tbl, cl, w.scale, w.dtype, pairs, nthreads=0)
+    sub = np.stack([got[w.query_start[i] + k, h] for (i, k), h in zip(rows, heads)])
+    check_outputs(sub, ref32, refT, w.dtype, label)

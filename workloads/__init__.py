@@ -253,3 +253,113 @@ def make_workload(s: Spec) -> Workload:
 
 def workload(cfg_id: int, variant: str = "full", **overrides) -> Workload:
     return make_workload(spec(cfg_id, variant, **overrides))
+
+
+# ---------------------------------------------------------------------------
+# multi-token (chunked-prefill) attention inputs
+# ---------------------------------------------------------------------------
+# Each sequence holds L_i tokens in the cache, the last n_i of which are its
+# query chunk (their K/V written with the rest).  Full variant: a
+# Qwen2.5-7B-shaped layer (28 q / 4 kv heads, D 128, bf16, bs 16) with 8
+# sequences, each running a 512-token prefill chunk after 0 .. 8192 tokens of
+# earlier chunks; small variants keep the head structure at sizes the oracle
+# finishes in seconds, with whole prompts, one-token chunks and ragged tails.
+
+STREAM_PF_Q = 20
+STREAM_PF_K = 21
+STREAM_PF_V = 22
+
+
+@dataclass(frozen=True)
+class PrefillSpec:
+    name: str
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    dtype: str
+    contexts: tuple               # L_i, tokens in the cache including the chunk
+    chunks: tuple                 # n_i <= L_i
+    seed: int = 40
+    pool_factor: float = 1.25
+
+
+PREFILL_SPECS = {
+    "full": PrefillSpec(
+        "Qwen2.5-7B-shaped chunked prefill: 8 seqs x 512-token chunks after 0..8192 cached "
+        "tokens, 28q/4kv heads, D128, bf16, bs16",
+        28, 4, 128, 16, "bf16",
+        contexts=tuple(h + 512 for h in (0, 512, 1024, 2048, 3072, 4096, 6144, 8192)),
+        chunks=(512,) * 8),
+    "small": PrefillSpec(
+        "small chunked prefill, 28q/4kv, D128, bf16, bs16", 28, 4, 128, 16, "bf16",
+        contexts=(1, 17, 100, 530, 64, 33), chunks=(1, 17, 37, 512, 1, 32)),
+}
+
+
+@dataclass
+class PrefillWorkload:
+    spec: PrefillSpec
+    lengths: np.ndarray           # int32 [S]
+    chunks: np.ndarray            # int32 [S]
+    query_start: np.ndarray       # int32 [S + 1]
+    num_blocks: int
+    initial_free_order: np.ndarray
+
+    @property
+    def S(self): return len(self.spec.contexts)
+    @property
+    def Hq(self): return self.spec.num_q_heads
+    @property
+    def Hkv(self): return self.spec.num_kv_heads
+    @property
+    def D(self): return self.spec.head_dim
+    @property
+    def bs(self): return self.spec.block_size
+    @property
+    def dtype(self): return self.spec.dtype
+    @property
+    def T(self): return int(self.query_start[-1])
+    @property
+    def scale(self): return float(np.float32(1.0 / math.sqrt(self.spec.head_dim)))
+
+    def max_blocks_per_seq(self) -> int:
+        return int(-(-int(self.lengths.max()) // self.bs))
+
+    def tokens(self, i: int, which: str) -> np.ndarray:
+        """All L_i cached tokens of sequence i (the chunk last): [L_i][Hkv][D]."""
+        stream = STREAM_PF_K if which == "k" else STREAM_PF_V
+        x = _rng(self.spec.seed, stream, i).standard_normal(
+            (int(self.lengths[i]), self.Hkv, self.D), dtype=np.float32)
+        return to_bits(x, self.dtype)
+
+    def query(self) -> np.ndarray:
+        x = _rng(self.spec.seed, STREAM_PF_Q).standard_normal((self.T, self.Hq, self.D),
+                                                              dtype=np.float32)
+        return to_bits(x, self.dtype)
+
+    def flops(self) -> int:
+        """Causal attention FLOPs: 4 D per (query row, head, visible key)."""
+        keys = sum(int(n) * (int(L) - int(n)) + int(n) * (int(n) + 1) // 2
+                   for L, n in zip(self.lengths, self.chunks))
+        return 4 * self.D * self.Hq * keys
+
+    def kv_bytes(self) -> int:
+        """K+V bytes of the cached tokens the chunks read (each once)."""
+        return int(self.lengths.astype(np.int64).sum()) * 2 * self.Hkv * self.D * 2
+
+
+def prefill_workload(variant: str = "small", **overrides) -> PrefillWorkload:
+    s = PREFILL_SPECS[variant]
+    if overrides:
+        s = replace(s, **overrides)
+    L = np.array(s.contexts, np.int32)
+    n = np.array(s.chunks, np.int32)
+    if L.shape != n.shape or np.any(n < 0) or np.any(n > L):
+        raise ValueError("chunks must satisfy 0 <= n_i <= L_i")
+    blocks = int(sum(-(-int(x) // s.block_size) for x in L))
+    nb = max(int(math.ceil(s.pool_factor * blocks)), 1)
+    perm = _rng(s.seed, STREAM_PERM).permutation(nb).astype(np.int32)
+    qs = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+    return PrefillWorkload(spec=s, lengths=L, chunks=n, query_start=qs, num_blocks=nb,
+                           initial_free_order=perm)
