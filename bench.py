@@ -123,13 +123,16 @@ def run_prefill(args):
     q = dev(w.query())
     out = torch.empty((w.T, w.Hq, w.D), dtype=torch.int16, device="cuda")
     mql = int(w.chunks.max())
+    # longest context first (host-side order, like the decode's work list)
+    order = dev(np.argsort(-w.lengths, kind="stable").astype(np.int32))
     for _ in range(args.warmup):
-        pa_prefill(out, q, kc, vc, bt, lens, qs, mql, w.scale, w.dtype)
+        pa_prefill(out, q, kc, vc, bt, lens, qs, mql, w.scale, w.dtype, seq_order=order)
     torch.cuda.synchronize()
     ev = [(Event(timing=True), Event(timing=True)) for _ in range(args.steps)]
     t0 = time.perf_counter()
     for a, b in ev:
-        pa_prefill(out, q, kc, vc, bt, lens, qs, mql, w.scale, w.dtype, start_event=a, stop_event=b)
+        pa_prefill(out, q, kc, vc, bt, lens, qs, mql, w.scale, w.dtype, seq_order=order,
+                   start_event=a, stop_event=b)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     t = np.array([a.elapsed_time(b) for a, b in ev]) * 1e-3

@@ -280,6 +280,10 @@ pa_status pa_copy_blocks(void* key_cache, void* value_cache,
  *   out[row][h] = sum_{j <= pos} softmax_j(scale * q[row][h] . K[j]) V[j]
  *   query, out     [num_query_tokens][num_q_heads][head_dim] 16-bit
  *   query_start    [num_seqs + 1] int32 device array, query_start[0] = 0
+ *   seq_order      [num_seqs] int32 device array or NULL: the order in which
+ *                  the sequences' work is dispatched (a permutation of
+ *                  0..num_seqs-1; longest context first balances the launch;
+ *                  entries outside [0, num_seqs) are skipped)
  *   max_query_len  >= every n_i (sizes the grid; longer chunks are cut)
  * Other arguments as for pa_decode.  Products run on the matrix cores with
  * fp32 accumulation; the softmax weights enter the P.V product as a 16-bit
@@ -290,7 +294,8 @@ pa_status pa_copy_blocks(void* key_cache, void* value_cache,
 pa_status pa_prefill(void* out, const void* query, const void* key_cache,
                      const void* value_cache, const int32_t* block_tables,
                      int32_t max_blocks_per_seq, const int32_t* context_lens,
-                     const int32_t* query_start, int32_t num_seqs,
+                     const int32_t* query_start, const int32_t* seq_order,
+                     int32_t num_seqs,
                      int32_t num_query_tokens, int32_t max_query_len,
                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                      int32_t block_size, int32_t num_blocks, float scale,

@@ -70,8 +70,8 @@ _DEC8 = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _
          _f32, _i32]
 _sig("pa_decode_int8", _i32, _DEC8 + [_vp, _vp, _vp])
 _sig("pa_decode_partitioned_int8", _i32, _DEC8 + [_i32, _vp, _i32, _vp, _sz, _vp, _vp, _vp])
-_sig("pa_prefill", _i32, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
-                          _i32, _i32, _i32, _f32, _i32, _vp, _vp, _vp])
+_sig("pa_prefill", _i32, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                          _i32, _i32, _i32, _i32, _f32, _i32, _vp, _vp, _vp])
 _sig("pa_copy_blocks_int8", _i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp])
 _sig("pa_alloc_create", _i32, [_i32, _i32, _i32p, ctypes.POINTER(_vp)])
 _sig("pa_alloc_destroy", None, [_vp])
@@ -368,10 +368,12 @@ def pa_copy_blocks_int8(key_cache, value_cache, key_scale, value_scale, block_pa
 
 
 def pa_prefill(out, query, key_cache, value_cache, block_tables, context_lens, query_start,
-               max_query_len, scale, dtype, stream=None, start_event=None, stop_event=None):
+               max_query_len, scale, dtype, seq_order=None, stream=None, start_event=None,
+               stop_event=None):
     """Causal attention of each sequence's query chunk (its last n_i cached
     tokens) over its paged cache.  query/out [T][Hq][D] 16-bit; query_start
-    int32 GPU tensor [S+1]; context_lens int32 [S]; block_tables int32 [S][MB]."""
+    int32 GPU tensor [S+1]; context_lens int32 [S]; block_tables int32 [S][MB];
+    seq_order an optional int32 GPU tensor [S] (dispatch order, longest first)."""
     t, hq, d = query.shape
     nb, bs, hkv, d2 = key_cache.shape
     if d2 != d or tuple(value_cache.shape) != tuple(key_cache.shape):
@@ -385,7 +387,9 @@ def pa_prefill(out, query, key_cache, value_cache, block_tables, context_lens, q
         _dptr(out, "out", 2), _dptr(query, "query", 2), _dptr(key_cache, "key_cache", 2),
         _dptr(value_cache, "value_cache", 2), _dptr(block_tables, "block_tables", 4),
         block_tables.shape[1], _dptr(context_lens, "context_lens", 4),
-        _dptr(query_start, "query_start", 4), s, t, int(max_query_len), hq, hkv, d, bs, nb,
+        _dptr(query_start, "query_start", 4),
+        None if seq_order is None else _dptr(seq_order, "seq_order", 4), s, t,
+        int(max_query_len), hq, hkv, d, bs, nb,
         float(scale), _dtype_code(dtype), _stream(stream), _event(start_event),
         _event(stop_event)))
 

@@ -11,23 +11,28 @@
 // PagedAttention深度解析与工程实践", §二 and §4.1).
 //
 // Rows are (query token, head of the group) pairs of one (sequence, KV head),
-// token-major: row r = k * G + h.  A workgroup of WAVES waves takes
-// 16 * WAVES consecutive rows; wave w's rows are the 16 "n" columns of its
-// matrix products.  The workgroup walks the keys [0, 1 + the largest position
-// among its rows) in tiles of 32: the tile's K rows go to LDS as they are,
-// its V rows transposed ([dim][key]), both read by every wave.  Per tile and
-// wave, in the transposed form that needs no transpose of Q or of the scores:
+// token-major: row r = k * G + h.  A workgroup of 8 waves takes 128
+// consecutive rows; wave w's rows are the 16 "n" columns of its matrix
+// products.  The workgroup walks the keys [0, 1 + the largest position among
+// its rows) in tiles of 64, double-buffered in LDS (the next tile's loads in
+// flight while the current one is computed; block ids one tile further
+// ahead): the K rows as they are, the V rows transposed ([dim][key]), both
+// read by every wave.  Per tile and wave, in the transposed form that needs
+// no transpose of Q or of the scores:
 //   S^T = K Q^T     v_mfma_f32_16x16x32 (A = 16 keys x 32 dims of K from LDS,
 //                   B = 32 dims x 16 rows of Q, resident in registers); the
 //                   result holds, in lane l, keys 4(l/16)+r of row l%16 ...
 //   online softmax  ... so each row's max and sum are a 4-lane exchange
-//                   (row swaps); masked keys (past the row's position) get
-//                   weight 0 by select;
-//   O^T += V^T P^T  v_mfma_f32_16x16x16 (A = 16 dims x 16 keys of V^T from
-//                   LDS, B = P^T straight from the S^T registers, whose
-//                   layout is this instruction's B layout).  P goes in as a
-//                   16-bit high part plus a 16-bit remainder, two products,
-//                   so the weights keep ~17 bits instead of 8.
+//                   (row swaps); keys past the row's position get weight 0
+//                   by select (only tiles that reach that far test it); the
+//                   accumulators are rescaled only when a row's max moved;
+//   O^T += V^T P^T  v_mfma_f32_16x16x32 over 32 keys per product (A = 16 dims
+//                   of V^T from LDS, B = P^T straight from the S^T
+//                   registers: the 32 keys of two S^T tiles are ordered so
+//                   that each lane's 8 k values are its own keys, and V^T is
+//                   read in the same order).  P goes in as a 16-bit part plus
+//                   a 16-bit remainder, two products, so the weights keep
+//                   ~17 bits instead of 8.
 // Products of 16-bit values are exact in the fp32 accumulators; the output
 // is O / l rounded once to the 16-bit type.
 #include <hip/hip_ext.h>
@@ -48,11 +53,15 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWavesP = 8;               // waves per workgroup
 constexpr int kThreadsP = 64 * kWavesP;
 constexpr int kRowsP = 16 * kWavesP;     // (token, head) rows per workgroup
-constexpr int kKeyTile = 32;             // keys per LDS tile
+constexpr int kKeyTile = 64;             // keys per LDS tile
+constexpr int kMT = kKeyTile / 16;       // 16-key tiles of S^T per key tile
 
 // round-to-nearest-even narrowing and exact widening of the 16-bit types
 template <int DT>
@@ -65,10 +74,24 @@ __device__ inline uint16_t narrow16(float x) {
     return static_cast<uint16_t>((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
   }
 }
+// Two weights p0, p1 (finite, >= 0) as a 16-bit pair hi plus the pair of
+// remainders lo = p - hi, so hi + lo carries about 17 significant bits (the
+// remainder p - hi is exact in fp32).
 template <int DT>
-__device__ inline float widen16(uint16_t b) {
-  if constexpr (DT == PA_F16) return static_cast<float>(__builtin_bit_cast(_Float16, b));
-  else return __uint_as_float(static_cast<uint32_t>(b) << 16);
+__device__ inline void split_pair(float p0, float p1, uint32_t& hi, uint32_t& lo) {
+  if constexpr (DT == PA_F16) {
+    const f16x2 h = __builtin_convertvector(f32x2{p0, p1}, f16x2);
+    const f32x2 r = f32x2{p0, p1} - __builtin_convertvector(h, f32x2);
+    hi = __builtin_bit_cast(uint32_t, h);
+    lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, f16x2));
+  } else {
+    const bf16x2 h = __builtin_convertvector(f32x2{p0, p1}, bf16x2);
+    const uint32_t hb = __builtin_bit_cast(uint32_t, h);
+    const float r0 = p0 - __uint_as_float(hb << 16);
+    const float r1 = p1 - __uint_as_float(hb & 0xffff0000u);
+    hi = hb;
+    lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{r0, r1}, bf16x2));
+  }
 }
 
 // 16 keys x 32 dims (A) times 32 dims x 16 rows (B), accumulated in c
@@ -120,6 +143,7 @@ struct PrefillParams {
   const int32_t* block_tables; // [S][mb]
   const int32_t* context_lens; // [S]
   const int32_t* query_start;  // [S + 1]
+  const int32_t* seq_order;    // [S] dispatch order of the sequences, or NULL
   int32_t mb, num_seqs, num_tokens, max_query_len;
   int32_t num_q_heads, num_kv_heads, group, block_size, num_blocks;
   int32_t row_tiles;           // ceil(max_query_len * group / kRowsP)
@@ -133,11 +157,12 @@ struct PrefillLds {
   static constexpr int KROW = D * 2 + 16;          // bytes per K row
   static constexpr int VROW = kKeyTile * 2 + 16;   // bytes per V^T row
   static constexpr int K_BYTES = kKeyTile * KROW;
-  static constexpr int BYTES = K_BYTES + D * VROW;
+  static constexpr int BUF = K_BYTES + D * VROW;   // one tile
+  static constexpr int BYTES = 2 * BUF;            // double buffer
 };
 
 template <int DT, int D>
-__global__ __launch_bounds__(kThreadsP) void prefill_kernel(PrefillParams p) {
+__global__ __launch_bounds__(kThreadsP, 4) void prefill_kernel(PrefillParams p) {
   using L = PrefillLds<D>;
   constexpr int KS = D / 32;          // k-steps of the S^T product
   constexpr int DT_TILES = D / 16;    // 16-dim tiles of O^T
@@ -145,19 +170,21 @@ __global__ __launch_bounds__(kThreadsP) void prefill_kernel(PrefillParams p) {
   constexpr int CHUNKS = kKeyTile * CPK;
   constexpr int LOADS = (CHUNKS + kThreadsP - 1) / kThreadsP;
   __shared__ __attribute__((aligned(16))) char lds[L::BYTES];
-  char* k_lds = lds;
-  char* v_lds = lds + L::K_BYTES;
 
   // blockIdx -> (sequence, KV head, row tile): the tiles of one (sequence,
-  // KV head) share blockIdx.x mod 8, hence an XCD and its L2
+  // KV head) share blockIdx.x mod 8, hence an XCD and its L2; sequences go
+  // in seq_order (the caller's longest-first order keeps the long ones from
+  // being the tail of the launch)
   const int npairs = p.num_seqs * p.num_kv_heads;
   const int id = blockIdx.x;
   const int k8 = id >> 3;
   const int pair = (k8 / p.row_tiles) * 8 + (id & 7);
   const int tile = k8 % p.row_tiles;
   if (pair >= npairs) return;                         // uniform: whole workgroup
-  const int seq = pair / p.num_kv_heads;
-  const int kvh = pair - seq * p.num_kv_heads;
+  const int rank = pair / p.num_kv_heads;
+  const int kvh = pair - rank * p.num_kv_heads;
+  const int seq = p.seq_order ? p.seq_order[rank] : rank;
+  if (static_cast<unsigned>(seq) >= static_cast<unsigned>(p.num_seqs)) return;   // uniform
   const int G = p.group;
 
   const int q0 = p.query_start[seq];
@@ -195,38 +222,44 @@ __global__ __launch_bounds__(kThreadsP) void prefill_kernel(PrefillParams p) {
   const int32_t* bt = p.block_tables + static_cast<int64_t>(seq) * p.mb;
   const uint4* kc = static_cast<const uint4*>(p.k_cache);
   const uint4* vc = static_cast<const uint4*>(p.v_cache);
-  // chunk c of a tile: key c / CPK, dims 8 * (c % CPK) .. +8
-  auto load_tile = [&](int t, uint4 (&kr)[LOADS], uint4 (&vr)[LOADS]) {
+  // Thread tid moves chunks c = tid + j * kThreadsP of each tile: key c / CPK,
+  // dims 8 * (c % CPK) .. +8.  Its block ids run one tile ahead of its loads,
+  // so a tile's K/V loads never wait for a table read.
+  auto block_of = [&](int t, int j) {
+    const int c = tid + j * kThreadsP;
+    const int key = t * kKeyTile + c / CPK;
+    if (c >= CHUNKS || key >= kend) return -1;
+    const int blk = bt[key / p.block_size];
+    return static_cast<unsigned>(blk) < static_cast<unsigned>(p.num_blocks) ? blk : 0;
+  };
+  auto load_tile = [&](int t, const int (&blk)[LOADS], uint4 (&kr)[LOADS], uint4 (&vr)[LOADS]) {
 #pragma unroll
     for (int j = 0; j < LOADS; ++j) {
       const int c = tid + j * kThreadsP;
-      const int key = t * kKeyTile + c / CPK;
-      kr[j] = make_uint4(0, 0, 0, 0);
+      kr[j] = make_uint4(0, 0, 0, 0);       // keys past kend: zeros (their weight is 0)
       vr[j] = make_uint4(0, 0, 0, 0);
-      if (c < CHUNKS && key < kend) {
-        int blk = bt[key / p.block_size];
-        blk = static_cast<unsigned>(blk) < static_cast<unsigned>(p.num_blocks) ? blk : 0;
-        const int64_t at =
-            ((static_cast<int64_t>(blk) * p.block_size + key % p.block_size) * p.num_kv_heads +
-             kvh) * CPK + c % CPK;
+      if (blk[j] >= 0) {
+        const int key = t * kKeyTile + c / CPK;
+        const int64_t at = ((static_cast<int64_t>(blk[j]) * p.block_size + key % p.block_size) *
+                                p.num_kv_heads + kvh) * CPK + c % CPK;
         kr[j] = kc[at];
         vr[j] = vc[at];
       }
     }
   };
-  auto store_tile = [&](const uint4 (&kr)[LOADS], const uint4 (&vr)[LOADS]) {
+  auto store_tile = [&](char* buf, const uint4 (&kr)[LOADS], const uint4 (&vr)[LOADS]) {
 #pragma unroll
     for (int j = 0; j < LOADS; ++j) {
       const int c = tid + j * kThreadsP;
       if (c >= CHUNKS) continue;
       const int key = c / CPK, col = c % CPK;
-      *reinterpret_cast<uint4*>(k_lds + key * L::KROW + col * 16) = kr[j];
+      *reinterpret_cast<uint4*>(buf + key * L::KROW + col * 16) = kr[j];
+      char* vt = buf + L::K_BYTES + key * 2;
       const uint32_t w[4] = {vr[j].x, vr[j].y, vr[j].z, vr[j].w};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint16_t v = static_cast<uint16_t>(w[e / 2] >> (16 * (e & 1)));
-        *reinterpret_cast<uint16_t*>(v_lds + (col * 8 + e) * L::VROW + key * 2) = v;
-      }
+      for (int e = 0; e < 8; ++e)
+        *reinterpret_cast<uint16_t*>(vt + (col * 8 + e) * L::VROW) =
+            static_cast<uint16_t>(w[e / 2] >> (16 * (e & 1)));
     }
   };
 
@@ -235,75 +268,96 @@ __global__ __launch_bounds__(kThreadsP) void prefill_kernel(PrefillParams p) {
   for (int dt = 0; dt < DT_TILES; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -__builtin_inff();
   float l_lane = 0.f;                 // this lane's share of the row's sum
+  // the wave's smallest position: tiles wholly at or below it need no mask
+  const int wave_pos_min = base_pos + min(r0 + wave * 16, nrows - 1) / G;
 
   const int ntiles = (kend + kKeyTile - 1) / kKeyTile;
   uint4 kr[LOADS], vr[LOADS];
-  load_tile(0, kr, vr);
-  for (int t = 0; t < ntiles; ++t) {
-    __syncthreads();                  // the previous tile is no longer read
-    store_tile(kr, vr);
-    __syncthreads();
-    if (t + 1 < ntiles) load_tile(t + 1, kr, vr);   // in flight during this tile
-
-    // S^T for keys t*32 + 16*mt + 4*lg + r of this lane's row
-    f32x4 s[2];
+  int blk[LOADS];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
+  for (int j = 0; j < LOADS; ++j) blk[j] = block_of(0, j);
+  load_tile(0, blk, kr, vr);
+#pragma unroll
+  for (int j = 0; j < LOADS; ++j) blk[j] = block_of(1, j);
+  store_tile(lds, kr, vr);
+  __syncthreads();
+  for (int t = 0; t < ntiles; ++t) {
+    const char* buf = lds + (t & 1) * L::BUF;
+    if (t + 1 < ntiles) {                  // in flight during this tile
+      load_tile(t + 1, blk, kr, vr);
+#pragma unroll
+      for (int j = 0; j < LOADS; ++j) blk[j] = block_of(t + 2, j);
+    }
+
+    // S^T for keys t*KT + 16*mt + 4*lg + r of this lane's row
+    f32x4 s[kMT];
+#pragma unroll
+    for (int mt = 0; mt < kMT; ++mt) {
       s[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const uint4 a = *reinterpret_cast<const uint4*>(k_lds + (16 * mt + lr) * L::KROW +
+        const uint4 a = *reinterpret_cast<const uint4*>(buf + (16 * mt + lr) * L::KROW +
                                                         (8 * lg + 32 * ks) * 2);
         s[mt] = mma_k32<DT>(a, qb[ks], s[mt]);
       }
     }
-    // online softmax of the row (base 2)
-    float x[8];
-    float tmax = -__builtin_inff();
+    // online softmax of the row (base 2); keys past the row's position get
+    // weight 0, tested only on tiles that reach past the wave's first row
+    float x[4 * kMT];
+    const bool masked = t * kKeyTile + kKeyTile - 1 > wave_pos_min;   // uniform
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < kMT; ++mt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int key = t * kKeyTile + 16 * mt + 4 * lg + r;
-        const float v = key <= pos ? s[mt][r] * p.scale_log2 : -__builtin_inff();
-        x[4 * mt + r] = v;
-        tmax = fmaxf(tmax, v);
+        const float v = s[mt][r] * p.scale_log2;
+        x[4 * mt + r] = (masked && t * kKeyTile + 16 * mt + 4 * lg + r > pos)
+                            ? -__builtin_inff() : v;
       }
+    float tmax = x[0];
+#pragma unroll
+    for (int k = 1; k < 4 * kMT; ++k) tmax = fmaxf(tmax, x[k]);
     const float m_new = fmaxf(m_run, row4_max(tmax));
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 while m_run is -inf
-    m_run = m_new;
-    float psum = 0.f;
-    uint2 phi[2], plo[2];
+    // rescale the accumulators only when some row's max moved (uniform test)
+    if (__builtin_amdgcn_ballot_w64(m_new != m_run)) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 while m_run is -inf
+      l_lane *= alpha;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      uint16_t h[4], lo[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float pr = x[4 * mt + r] == -__builtin_inff()
-                             ? 0.f : __builtin_amdgcn_exp2f(x[4 * mt + r] - m_new);
-        psum += pr;
-        h[r] = narrow16<DT>(pr);
-        lo[r] = narrow16<DT>(pr - widen16<DT>(h[r]));
-      }
-      phi[mt] = make_uint2(h[0] | (static_cast<uint32_t>(h[1]) << 16),
-                           h[2] | (static_cast<uint32_t>(h[3]) << 16));
-      plo[mt] = make_uint2(lo[0] | (static_cast<uint32_t>(lo[1]) << 16),
-                           lo[2] | (static_cast<uint32_t>(lo[3]) << 16));
+      for (int dt = 0; dt < DT_TILES; ++dt) acc[dt] *= alpha;
+      m_run = m_new;
     }
-    l_lane = l_lane * alpha + psum;
-    // O^T = alpha O^T + V^T P^T
+    float pr[4 * kMT];
+#pragma unroll
+    for (int k = 0; k < 4 * kMT; ++k) {
+      pr[k] = __builtin_amdgcn_exp2f(x[k] - m_run);   // exp2(-inf) = 0
+      l_lane += pr[k];
+    }
+    // O^T += V^T P^T on 16x16x32 products: k-step ks takes the 32 keys of
+    // S^T tiles 2ks and 2ks + 1, ordered so that lane group lg's 8 k values
+    // are its own keys 4lg + r of both tiles (P^T straight from registers);
+    // the V^T operand follows the same order (two 8-byte reads)
+    uint4 phi[kMT / 2], plo[kMT / 2];
+#pragma unroll
+    for (int ks = 0; ks < kMT / 2; ++ks) {
+      const float* q0p = pr + 8 * ks;
+      split_pair<DT>(q0p[0], q0p[1], phi[ks].x, plo[ks].x);
+      split_pair<DT>(q0p[2], q0p[3], phi[ks].y, plo[ks].y);
+      split_pair<DT>(q0p[4], q0p[5], phi[ks].z, plo[ks].z);
+      split_pair<DT>(q0p[6], q0p[7], phi[ks].w, plo[ks].w);
+    }
 #pragma unroll
     for (int dt = 0; dt < DT_TILES; ++dt) {
-      f32x4 o = acc[dt] * alpha;
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        const uint2 a = *reinterpret_cast<const uint2*>(v_lds + (16 * dt + lr) * L::VROW +
-                                                        (16 * mt + 4 * lg) * 2);
-        o = mma_k16<DT>(a, phi[mt], o);
-        o = mma_k16<DT>(a, plo[mt], o);
+      for (int ks = 0; ks < kMT / 2; ++ks) {
+        const char* vrow = buf + L::K_BYTES + (16 * dt + lr) * L::VROW + (32 * ks + 4 * lg) * 2;
+        const uint2 a0 = *reinterpret_cast<const uint2*>(vrow);
+        const uint2 a1 = *reinterpret_cast<const uint2*>(vrow + 32);   // keys + 16
+        const uint4 a = make_uint4(a0.x, a0.y, a1.x, a1.y);
+        acc[dt] = mma_k32<DT>(a, phi[ks], acc[dt]);
+        acc[dt] = mma_k32<DT>(a, plo[ks], acc[dt]);
       }
-      acc[dt] = o;
     }
+    if (t + 1 < ntiles) store_tile(lds + ((t + 1) & 1) * L::BUF, kr, vr);
+    __syncthreads();   // tile t + 1 is in place; tile t's buffer may be rewritten
   }
 
   // out = O / l, dims 16*dt + 4*lg + r of this lane's row
@@ -330,7 +384,8 @@ bool aligned_p(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(
 extern "C" pa_status pa_prefill(void* out, const void* query, const void* key_cache,
                                 const void* value_cache, const int32_t* block_tables,
                                 int32_t max_blocks_per_seq, const int32_t* context_lens,
-                                const int32_t* query_start, int32_t num_seqs,
+                                const int32_t* query_start, const int32_t* seq_order,
+                                int32_t num_seqs,
                                 int32_t num_query_tokens, int32_t max_query_len,
                                 int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                                 int32_t block_size, int32_t num_blocks, float scale,
@@ -367,7 +422,8 @@ extern "C" pa_status pa_prefill(void* out, const void* query, const void* key_ca
     return fail(PA_ERR_INVALID_ARG, "NULL device pointer");
   if (!pa::aligned_p(out, 16) || !pa::aligned_p(query, 16) || !pa::aligned_p(key_cache, 16) ||
       !pa::aligned_p(value_cache, 16) || !pa::aligned_p(block_tables, 4) ||
-      !pa::aligned_p(context_lens, 4) || !pa::aligned_p(query_start, 4))
+      !pa::aligned_p(context_lens, 4) || !pa::aligned_p(query_start, 4) ||
+      !pa::aligned_p(seq_order, 4))
     return fail(PA_ERR_INVALID_ARG, "device buffers must be 16-byte aligned (metadata 4-byte)");
   pa::PrefillParams p{};
   p.out = out;
@@ -377,6 +433,7 @@ extern "C" pa_status pa_prefill(void* out, const void* query, const void* key_ca
   p.block_tables = block_tables;
   p.context_lens = context_lens;
   p.query_start = query_start;
+  p.seq_order = seq_order;
   p.mb = max_blocks_per_seq;
   p.num_seqs = num_seqs;
   p.num_tokens = num_query_tokens;

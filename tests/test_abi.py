@@ -238,14 +238,15 @@ def test_int8_entry_points_reject_on_host():
 
 def test_prefill_rejects_on_host():
     f = L.pa_prefill
-    ok = [BAD, BAD, BAD, BAD, BAD, 4, BAD, BAD, 2, 10, 8, 8, 2, 128, 16, 10, 0.088, 1]
-    for idx, val, status in [(13, 96, _native.PA_ERR_UNSUPPORTED),     # head_dim
-                             (11, 7, _native.PA_ERR_INVALID_ARG),       # Hq not a multiple of Hkv
+    ok = [BAD, BAD, BAD, BAD, BAD, 4, BAD, BAD, None, 2, 10, 8, 8, 2, 128, 16, 10, 0.088, 1]
+    for idx, val, status in [(14, 96, _native.PA_ERR_UNSUPPORTED),     # head_dim
+                             (12, 7, _native.PA_ERR_INVALID_ARG),       # Hq not a multiple of Hkv
                              (7, None, _native.PA_ERR_INVALID_ARG),     # NULL query_start
+                             (8, MIS, _native.PA_ERR_INVALID_ARG),      # misaligned seq_order
                              (0, MIS, _native.PA_ERR_INVALID_ARG),      # misaligned out
-                             (17, 9, _native.PA_ERR_INVALID_ARG),       # dtype
-                             (16, float("nan"), _native.PA_ERR_INVALID_ARG)]:
+                             (18, 9, _native.PA_ERR_INVALID_ARG),       # dtype
+                             (17, float("nan"), _native.PA_ERR_INVALID_ARG)]:
         bad = list(ok); bad[idx] = val
         assert f(*bad, None, None, None) == status
-    empty = list(ok); empty[9] = 0                                      # no query tokens
+    empty = list(ok); empty[10] = 0                                     # no query tokens
     assert f(*empty, None, None, None) == _native.PA_OK

@@ -57,12 +57,16 @@ def build_oracle(w):
     return kc, vc, bt
 
 
-def run_gpu(w, kc, vc, bt, lens, qs, max_query_len=None):
+def longest_first(w):
+    return dev(np.argsort(-w.lengths, kind="stable").astype(np.int32))
+
+
+def run_gpu(w, kc, vc, bt, lens, qs, max_query_len=None, order=None):
     q = dev(w.query())
     out = torch.full((w.T, w.Hq, w.D), 0x7FFF, dtype=torch.int16, device="cuda")
     pa.pa_prefill(out, q, kc, vc, bt, lens, qs,
                   int(w.chunks.max()) if max_query_len is None else max_query_len,
-                  w.scale, w.dtype)
+                  w.scale, w.dtype, seq_order=order)
     torch.cuda.synchronize()
     return out.cpu().numpy().view(np.uint16)
 
@@ -91,9 +95,11 @@ def test_prefill_small(over):
     ref32, refT = oracle.prefill(w.query(), okc, ovc, obt, w.lengths, w.query_start, w.scale,
                                  w.dtype, nthreads=0)
     check_outputs(got, ref32, refT, w.dtype, label)
-    # a grid sized for longer chunks changes nothing
+    # a grid sized for longer chunks, or another dispatch order, changes nothing
     got2 = run_gpu(w, kc, vc, bt, lens, qs, max_query_len=int(w.chunks.max()) + 200)
     assert np.array_equal(got2, got)
+    got3 = run_gpu(w, kc, vc, bt, lens, qs, order=longest_first(w))
+    assert np.array_equal(got3, got)
     del kc, vc
     free_gpu()
 
@@ -106,7 +112,7 @@ def test_prefill_empty_and_rejects():
     L = pa.lib()
     # no query tokens: nothing is launched
     assert L.pa_prefill(out.data_ptr(), q.data_ptr(), kc.data_ptr(), vc.data_ptr(), bt.data_ptr(),
-                        bt.shape[1], lens.data_ptr(), qs.data_ptr(), w.S, 0, 0, w.Hq, w.Hkv, w.D,
+                        bt.shape[1], lens.data_ptr(), qs.data_ptr(), None, w.S, 0, 0, w.Hq, w.Hkv, w.D,
                         w.bs, w.num_blocks, w.scale, pa.PA_BF16, None, None, None) == 0
     with pytest.raises(ValueError):
         pa.pa_prefill(out, q, kc, vc, bt, lens, qs[:-1], 4, w.scale, w.dtype)
@@ -121,7 +127,7 @@ def test_prefill_full_size_sampled():
     w = prefill_workload("full")
     label = "prefill full sampled"
     kc, vc, bt, lens, qs, bt_host = build_gpu(w)
-    got = run_gpu(w, kc, vc, bt, lens, qs)
+    got = run_gpu(w, kc, vc, bt, lens, qs, order=longest_first(w))
     print(f"\n[{label}] GPU done", flush=True)
     assert np.isfinite(oracle.widen(got, w.dtype)).all()
     okc, ovc, obt = build_oracle(w)
