@@ -222,12 +222,15 @@ __global__ __launch_bounds__(kThreadsP, 4) void prefill_kernel(PrefillParams p) 
   const int32_t* bt = p.block_tables + static_cast<int64_t>(seq) * p.mb;
   const uint4* kc = static_cast<const uint4*>(p.k_cache);
   const uint4* vc = static_cast<const uint4*>(p.v_cache);
-  // Thread tid moves chunks c = tid + j * kThreadsP of each tile: key c / CPK,
-  // dims 8 * (c % CPK) .. +8.  Its block ids run one tile ahead of its loads,
+  // Thread tid moves chunks c = tid + j * kThreadsP of each tile: key
+  // c % kKeyTile, dims 8 * (c / kKeyTile) .. +8, so the 64 lanes of a wave
+  // hold one 8-dim column of all the tile's keys and each 16-bit store of the
+  // transposed V fills 128 contiguous bytes of one V^T row (no bank
+  // conflicts).  Its block ids run one tile ahead of its loads,
   // so a tile's K/V loads never wait for a table read.
   auto block_of = [&](int t, int j) {
     const int c = tid + j * kThreadsP;
-    const int key = t * kKeyTile + c / CPK;
+    const int key = t * kKeyTile + c % kKeyTile;
     if (c >= CHUNKS || key >= kend) return -1;
     const int blk = bt[key / p.block_size];
     return static_cast<unsigned>(blk) < static_cast<unsigned>(p.num_blocks) ? blk : 0;
@@ -239,9 +242,9 @@ __global__ __launch_bounds__(kThreadsP, 4) void prefill_kernel(PrefillParams p) 
       kr[j] = make_uint4(0, 0, 0, 0);       // keys past kend: zeros (their weight is 0)
       vr[j] = make_uint4(0, 0, 0, 0);
       if (blk[j] >= 0) {
-        const int key = t * kKeyTile + c / CPK;
+        const int key = t * kKeyTile + c % kKeyTile;
         const int64_t at = ((static_cast<int64_t>(blk[j]) * p.block_size + key % p.block_size) *
-                                p.num_kv_heads + kvh) * CPK + c % CPK;
+                                p.num_kv_heads + kvh) * CPK + c / kKeyTile;
         kr[j] = kc[at];
         vr[j] = vc[at];
       }
@@ -252,7 +255,7 @@ __global__ __launch_bounds__(kThreadsP, 4) void prefill_kernel(PrefillParams p) 
     for (int j = 0; j < LOADS; ++j) {
       const int c = tid + j * kThreadsP;
       if (c >= CHUNKS) continue;
-      const int key = c / CPK, col = c % CPK;
+      const int key = c % kKeyTile, col = c / kKeyTile;
       *reinterpret_cast<uint4*>(buf + key * L::KROW + col * 16) = kr[j];
       char* vt = buf + L::K_BYTES + key * 2;
       const uint32_t w[4] = {vr[j].x, vr[j].y, vr[j].z, vr[j].w};
