@@ -150,12 +150,21 @@ struct PrefillParams {
   float scale_log2;
 };
 
-// LDS: K tile [kKeyTile][D] with rows padded by 16 bytes (the 16 keys of an
-// A operand fall in different banks), V^T tile [D][kKeyTile] likewise.
+// LDS: K tile [kKeyTile][D] and V^T tile [D][kKeyTile], rows padded so that
+// the 16 rows one operand read touches fall in different banks.
+// Row paddings in bytes, from a sweep on the Qwen-shaped chunk step (K 0 /
+// 16 / 32 / 48, V^T 0 .. 72): unpadded V^T rows ran 3.7x slower, K 32 with
+// V^T 24 fastest.
+#ifndef PA_PF_KPAD
+#define PA_PF_KPAD 32
+#endif
+#ifndef PA_PF_VPAD
+#define PA_PF_VPAD 24
+#endif
 template <int D>
 struct PrefillLds {
-  static constexpr int KROW = D * 2 + 16;          // bytes per K row
-  static constexpr int VROW = kKeyTile * 2 + 16;   // bytes per V^T row
+  static constexpr int KROW = D * 2 + PA_PF_KPAD;          // bytes per K row
+  static constexpr int VROW = kKeyTile * 2 + PA_PF_VPAD;   // bytes per V^T row
   static constexpr int K_BYTES = kKeyTile * KROW;
   static constexpr int BUF = K_BYTES + D * VROW;   // one tile
   static constexpr int BYTES = 2 * BUF;            // double buffer
