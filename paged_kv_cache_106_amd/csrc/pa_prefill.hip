@@ -161,12 +161,18 @@ struct PrefillParams {
 #ifndef PA_PF_VPAD
 #define PA_PF_VPAD 24
 #endif
+// 1: V stays row-major in LDS and the P.V operands come from transposing
+// reads (ds_read_b64_tr_b16); 0: V is stored transposed
+#ifndef PA_PF_VTR
+#define PA_PF_VTR 1
+#endif
+constexpr bool kVTr = PA_PF_VTR;
 template <int D>
 struct PrefillLds {
   static constexpr int KROW = D * 2 + PA_PF_KPAD;          // bytes per K row
-  static constexpr int VROW = kKeyTile * 2 + PA_PF_VPAD;   // bytes per V^T row
+  static constexpr int VROW = kVTr ? KROW : kKeyTile * 2 + PA_PF_VPAD;   // bytes per V (V^T) row
   static constexpr int K_BYTES = kKeyTile * KROW;
-  static constexpr int BUF = K_BYTES + D * VROW;   // one tile
+  static constexpr int BUF = K_BYTES + (kVTr ? kKeyTile : D) * VROW;   // one tile
   static constexpr int BYTES = 2 * BUF;            // double buffer
 };
 
@@ -239,7 +245,7 @@ __global__ __launch_bounds__(kThreadsP, 4) void prefill_kernel(PrefillParams p) 
   // so a tile's K/V loads never wait for a table read.
   auto block_of = [&](int t, int j) {
     const int c = tid + j * kThreadsP;
-    const int key = t * kKeyTile + c % kKeyTile;
+    const int key = t * kKeyTile + (kVTr ? c / CPK : c % kKeyTile);
     if (c >= CHUNKS || key >= kend) return -1;
     const int blk = bt[key / p.block_size];
     return static_cast<unsigned>(blk) < static_cast<unsigned>(p.num_blocks) ? blk : 0;
@@ -251,9 +257,9 @@ __global__ __launch_bounds__(kThreadsP, 4) void prefill_kernel(PrefillParams p) 
       kr[j] = make_uint4(0, 0, 0, 0);       // keys past kend: zeros (their weight is 0)
       vr[j] = make_uint4(0, 0, 0, 0);
       if (blk[j] >= 0) {
-        const int key = t * kKeyTile + c % kKeyTile;
+        const int key = t * kKeyTile + (kVTr ? c / CPK : c % kKeyTile);
         const int64_t at = ((static_cast<int64_t>(blk[j]) * p.block_size + key % p.block_size) *
-                                p.num_kv_heads + kvh) * CPK + c / kKeyTile;
+                                p.num_kv_heads + kvh) * CPK + (kVTr ? c % CPK : c / kKeyTile);
         kr[j] = kc[at];
         vr[j] = vc[at];
       }
@@ -264,14 +270,18 @@ __global__ __launch_bounds__(kThreadsP, 4) void prefill_kernel(PrefillParams p) 
     for (int j = 0; j < LOADS; ++j) {
       const int c = tid + j * kThreadsP;
       if (c >= CHUNKS) continue;
-      const int key = c % kKeyTile, col = c / kKeyTile;
+      const int key = kVTr ? c / CPK : c % kKeyTile, col = kVTr ? c % CPK : c / kKeyTile;
       *reinterpret_cast<uint4*>(buf + key * L::KROW + col * 16) = kr[j];
-      char* vt = buf + L::K_BYTES + key * 2;
-      const uint32_t w[4] = {vr[j].x, vr[j].y, vr[j].z, vr[j].w};
+      if constexpr (kVTr) {
+        *reinterpret_cast<uint4*>(buf + L::K_BYTES + key * L::VROW + col * 16) = vr[j];
+      } else {
+        char* vt = buf + L::K_BYTES + key * 2;
+        const uint32_t w[4] = {vr[j].x, vr[j].y, vr[j].z, vr[j].w};
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        *reinterpret_cast<uint16_t*>(vt + (col * 8 + e) * L::VROW) =
-            static_cast<uint16_t>(w[e / 2] >> (16 * (e & 1)));
+        for (int e = 0; e < 8; ++e)
+          *reinterpret_cast<uint16_t*>(vt + (col * 8 + e) * L::VROW) =
+              static_cast<uint16_t>(w[e / 2] >> (16 * (e & 1)));
+      }
     }
   };
 
@@ -360,10 +370,24 @@ __global__ __launch_bounds__(kThreadsP, 4) void prefill_kernel(PrefillParams p) 
     for (int dt = 0; dt < DT_TILES; ++dt) {
 #pragma unroll
       for (int ks = 0; ks < kMT / 2; ++ks) {
-        const char* vrow = buf + L::K_BYTES + (16 * dt + lr) * L::VROW + (32 * ks + 4 * lg) * 2;
-        const uint2 a0 = *reinterpret_cast<const uint2*>(vrow);
-        const uint2 a1 = *reinterpret_cast<const uint2*>(vrow + 32);   // keys + 16
-        const uint4 a = make_uint4(a0.x, a0.y, a1.x, a1.y);
+        uint4 a;
+        if constexpr (kVTr) {
+          // lane lr of group lg addresses dims 16dt + 4(lr%4) .. +4 of key
+          // 32ks + 4lg + lr/4; the transposing read hands lane lr dim 16dt + lr
+          // of keys 32ks + 4lg + 0..3 (then the same 16 keys further on)
+          const char* vp = buf + L::K_BYTES + (32 * ks + 4 * lg + (lr >> 2)) * L::VROW +
+                           (16 * dt + 4 * (lr & 3)) * 2;
+          typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+          const s16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp));
+          const s16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 16 * L::VROW));
+          const uint2 b0 = __builtin_bit_cast(uint2, a0), b1 = __builtin_bit_cast(uint2, a1);
+          a = make_uint4(b0.x, b0.y, b1.x, b1.y);
+        } else {
+          const char* vrow = buf + L::K_BYTES + (16 * dt + lr) * L::VROW + (32 * ks + 4 * lg) * 2;
+          const uint2 a0 = *reinterpret_cast<const uint2*>(vrow);
+          const uint2 a1 = *reinterpret_cast<const uint2*>(vrow + 32);   // keys + 16
+          a = make_uint4(a0.x, a0.y, a1.x, a1.y);
+        }
         acc[dt] = mma_k32<DT>(a, phi[ks], acc[dt]);
         acc[dt] = mma_k32<DT>(a, plo[ks], acc[dt]);
       }
