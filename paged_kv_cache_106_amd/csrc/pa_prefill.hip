@@ -16,9 +16,8 @@
 // products.  The workgroup walks the keys [0, 1 + the largest position among
 // its rows) in tiles of 64, double-buffered in LDS (the next tile's loads in
 // flight while the current one is computed; block ids one tile further
-// ahead): the K rows as they are, the V rows transposed ([dim][key]), both
-// read by every wave.  Per tile and wave, in the transposed form that needs
-// no transpose of Q or of the scores:
+// ahead), K and V rows as they are, read by every wave.  Per tile and wave,
+// in the transposed form that needs no transpose of Q or of the scores:
 //   S^T = K Q^T     v_mfma_f32_16x16x32 (A = 16 keys x 32 dims of K from LDS,
 //                   B = 32 dims x 16 rows of Q, resident in registers); the
 //                   result holds, in lane l, keys 4(l/16)+r of row l%16 ...
@@ -27,12 +26,13 @@
 //                   by select (only tiles that reach that far test it); the
 //                   accumulators are rescaled only when a row's max moved;
 //   O^T += V^T P^T  v_mfma_f32_16x16x32 over 32 keys per product (A = 16 dims
-//                   of V^T from LDS, B = P^T straight from the S^T
+//                   of V^T, taken from the row-major V tile by the gfx950
+//                   transposing LDS read; B = P^T straight from the S^T
 //                   registers: the 32 keys of two S^T tiles are ordered so
-//                   that each lane's 8 k values are its own keys, and V^T is
-//                   read in the same order).  P goes in as a 16-bit part plus
-//                   a 16-bit remainder, two products, so the weights keep
-//                   ~17 bits instead of 8.
+//                   that each lane's 8 k values are its own keys, and the V^T
+//                   operand is read in the same order).  P goes in as a
+//                   16-bit part plus a 16-bit remainder, two products, so the
+//                   weights keep ~17 bits instead of 8.
 // Products of 16-bit values are exact in the fp32 accumulators; the output
 // is O / l rounded once to the 16-bit type.
 #include <hip/hip_ext.h>
@@ -150,29 +150,18 @@ struct PrefillParams {
   float scale_log2;
 };
 
-// LDS: K tile [kKeyTile][D] and V^T tile [D][kKeyTile], rows padded so that
-// the 16 rows one operand read touches fall in different banks.
-// Row paddings in bytes, from a sweep on the Qwen-shaped chunk step (K 0 /
-// 16 / 32 / 48, V^T 0 .. 72): unpadded V^T rows ran 3.7x slower, K 32 with
-// V^T 24 fastest.
+// LDS: the K and V tiles [kKeyTile][D], both row-major, rows padded by 32
+// bytes (a sweep of 0 .. 96 on the Qwen-shaped chunk step: unpadded rows ran
+// 2.1x slower, 32 fastest) so that the rows one operand read touches fall in
+// different banks.
 #ifndef PA_PF_KPAD
 #define PA_PF_KPAD 32
 #endif
-#ifndef PA_PF_VPAD
-#define PA_PF_VPAD 24
-#endif
-// 1: V stays row-major in LDS and the P.V operands come from transposing
-// reads (ds_read_b64_tr_b16); 0: V is stored transposed
-#ifndef PA_PF_VTR
-#define PA_PF_VTR 1
-#endif
-constexpr bool kVTr = PA_PF_VTR;
 template <int D>
 struct PrefillLds {
-  static constexpr int KROW = D * 2 + PA_PF_KPAD;          // bytes per K row
-  static constexpr int VROW = kVTr ? KROW : kKeyTile * 2 + PA_PF_VPAD;   // bytes per V (V^T) row
-  static constexpr int K_BYTES = kKeyTile * KROW;
-  static constexpr int BUF = K_BYTES + (kVTr ? kKeyTile : D) * VROW;   // one tile
+  static constexpr int ROW = D * 2 + PA_PF_KPAD;   // bytes per K or V row
+  static constexpr int K_BYTES = kKeyTile * ROW;
+  static constexpr int BUF = 2 * K_BYTES;          // one tile: K then V
   static constexpr int BYTES = 2 * BUF;            // double buffer
 };
 
@@ -237,15 +226,13 @@ __global__ __launch_bounds__(kThreadsP, 4) void prefill_kernel(PrefillParams p) 
   const int32_t* bt = p.block_tables + static_cast<int64_t>(seq) * p.mb;
   const uint4* kc = static_cast<const uint4*>(p.k_cache);
   const uint4* vc = static_cast<const uint4*>(p.v_cache);
-  // Thread tid moves chunks c = tid + j * kThreadsP of each tile: key
-  // c % kKeyTile, dims 8 * (c / kKeyTile) .. +8, so the 64 lanes of a wave
-  // hold one 8-dim column of all the tile's keys and each 16-bit store of the
-  // transposed V fills 128 contiguous bytes of one V^T row (no bank
-  // conflicts).  Its block ids run one tile ahead of its loads,
-  // so a tile's K/V loads never wait for a table read.
+  // Thread tid moves chunks c = tid + j * kThreadsP of each tile: key c / CPK,
+  // dims 8 * (c % CPK) .. +8 (a wave reads whole 256-byte rows).  Its block
+  // ids run one tile ahead of its loads, so a tile's K/V loads never wait for
+  // a table read.
   auto block_of = [&](int t, int j) {
     const int c = tid + j * kThreadsP;
-    const int key = t * kKeyTile + (kVTr ? c / CPK : c % kKeyTile);
+    const int key = t * kKeyTile + c / CPK;
     if (c >= CHUNKS || key >= kend) return -1;
     const int blk = bt[key / p.block_size];
     return static_cast<unsigned>(blk) < static_cast<unsigned>(p.num_blocks) ? blk : 0;
@@ -257,9 +244,9 @@ __global__ __launch_bounds__(kThreadsP, 4) void prefill_kernel(PrefillParams p) 
       kr[j] = make_uint4(0, 0, 0, 0);       // keys past kend: zeros (their weight is 0)
       vr[j] = make_uint4(0, 0, 0, 0);
       if (blk[j] >= 0) {
-        const int key = t * kKeyTile + (kVTr ? c / CPK : c % kKeyTile);
+        const int key = t * kKeyTile + c / CPK;
         const int64_t at = ((static_cast<int64_t>(blk[j]) * p.block_size + key % p.block_size) *
-                                p.num_kv_heads + kvh) * CPK + (kVTr ? c % CPK : c / kKeyTile);
+                                p.num_kv_heads + kvh) * CPK + c % CPK;
         kr[j] = kc[at];
         vr[j] = vc[at];
       }
@@ -270,18 +257,9 @@ __global__ __launch_bounds__(kThreadsP, 4) void prefill_kernel(PrefillParams p) 
     for (int j = 0; j < LOADS; ++j) {
       const int c = tid + j * kThreadsP;
       if (c >= CHUNKS) continue;
-      const int key = kVTr ? c / CPK : c % kKeyTile, col = kVTr ? c % CPK : c / kKeyTile;
-      *reinterpret_cast<uint4*>(buf + key * L::KROW + col * 16) = kr[j];
-      if constexpr (kVTr) {
-        *reinterpret_cast<uint4*>(buf + L::K_BYTES + key * L::VROW + col * 16) = vr[j];
-      } else {
-        char* vt = buf + L::K_BYTES + key * 2;
-        const uint32_t w[4] = {vr[j].x, vr[j].y, vr[j].z, vr[j].w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          *reinterpret_cast<uint16_t*>(vt + (col * 8 + e) * L::VROW) =
-              static_cast<uint16_t>(w[e / 2] >> (16 * (e & 1)));
-      }
+      const int key = c / CPK, col = c % CPK;
+      *reinterpret_cast<uint4*>(buf + key * L::ROW + col * 16) = kr[j];
+      *reinterpret_cast<uint4*>(buf + L::K_BYTES + key * L::ROW + col * 16) = vr[j];
     }
   };
 
@@ -318,7 +296,7 @@ __global__ __launch_bounds__(kThreadsP, 4) void prefill_kernel(PrefillParams p) 
       s[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const uint4 a = *reinterpret_cast<const uint4*>(buf + (16 * mt + lr) * L::KROW +
+        const uint4 a = *reinterpret_cast<const uint4*>(buf + (16 * mt + lr) * L::ROW +
                                                         (8 * lg + 32 * ks) * 2);
         s[mt] = mma_k32<DT>(a, qb[ks], s[mt]);
       }
@@ -370,24 +348,18 @@ __global__ __launch_bounds__(kThreadsP, 4) void prefill_kernel(PrefillParams p) 
     for (int dt = 0; dt < DT_TILES; ++dt) {
 #pragma unroll
       for (int ks = 0; ks < kMT / 2; ++ks) {
-        uint4 a;
-        if constexpr (kVTr) {
-          // lane lr of group lg addresses dims 16dt + 4(lr%4) .. +4 of key
-          // 32ks + 4lg + lr/4; the transposing read hands lane lr dim 16dt + lr
-          // of keys 32ks + 4lg + 0..3 (then the same 16 keys further on)
-          const char* vp = buf + L::K_BYTES + (32 * ks + 4 * lg + (lr >> 2)) * L::VROW +
-                           (16 * dt + 4 * (lr & 3)) * 2;
-          typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-          const s16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp));
-          const s16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 16 * L::VROW));
-          const uint2 b0 = __builtin_bit_cast(uint2, a0), b1 = __builtin_bit_cast(uint2, a1);
-          a = make_uint4(b0.x, b0.y, b1.x, b1.y);
-        } else {
-          const char* vrow = buf + L::K_BYTES + (16 * dt + lr) * L::VROW + (32 * ks + 4 * lg) * 2;
-          const uint2 a0 = *reinterpret_cast<const uint2*>(vrow);
-          const uint2 a1 = *reinterpret_cast<const uint2*>(vrow + 32);   // keys + 16
-          a = make_uint4(a0.x, a0.y, a1.x, a1.y);
-        }
+        // lane lr of group lg addresses dims 16dt + 4(lr%4) .. +4 of key
+        // 32ks + 4lg + lr/4; the transposing read (in each 16-lane group, lane
+        // i receives element i%4 of the units that lanes i/4, i/4 + 4, i/4 + 8
+        // and i/4 + 12 address) hands lane lr dim 16dt + lr of keys
+        // 32ks + 4lg + 0..3, and a second read the same 16 keys further on
+        const char* vp = buf + L::K_BYTES + (32 * ks + 4 * lg + (lr >> 2)) * L::ROW +
+                         (16 * dt + 4 * (lr & 3)) * 2;
+        typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+        const s16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp));
+        const s16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 16 * L::ROW));
+        const uint2 b0 = __builtin_bit_cast(uint2, a0), b1 = __builtin_bit_cast(uint2, a1);
+        const uint4 a = make_uint4(b0.x, b0.y, b1.x, b1.y);
         acc[dt] = mma_k32<DT>(a, phi[ks], acc[dt]);
         acc[dt] = mma_k32<DT>(a, plo[ks], acc[dt]);
       }
