@@ -156,7 +156,9 @@ def run_prefill(args):
         "roofline": {"bound": "mfma", "kernel": "pa_prefill: prefill_kernel",
                      "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": None},
+                     "traffic": traffic_from_profile("prefill_qwen25_7b_gqa_8x512_pmc.md",
+                                                     "prefill"),
+                     "traffic_unit": "bytes per call (FETCH_SIZE x2 + WRITE_SIZE, copy-calibrated)"},
     }
     del kc, vc
     torch.cuda.empty_cache()
@@ -166,14 +168,22 @@ def run_prefill(args):
     print(json.dumps(result), flush=True)
 
 
-def kernel_source_sha256():
-    """sha256 over the sources the decode kernels are built and launched from."""
+KERNEL_SOURCES = {
+    # the sources each kernel family is built and launched from
+    "decode": ("pa_attn*", "pa_internal.h", "pa_api.hip"),
+    "prefill": ("pa_prefill.hip", "pa_mfma.h", "pa_internal.h"),
+}
+
+
+def kernel_source_sha256(kind="decode"):
+    """sha256 over the sources one kernel family is built and launched from."""
     import glob
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "paged_kv_cache_106_amd", "csrc")
-    files = glob.glob(os.path.join(csrc, "pa_attn*")) + [
-        os.path.join(csrc, "pa_internal.h"), os.path.join(csrc, "pa_api.hip")]
+    files = set()
+    for pat in KERNEL_SOURCES[kind]:
+        files.update(glob.glob(os.path.join(csrc, pat)))
     for f in sorted(files):
         h.update(os.path.basename(f).encode())
         with open(f, "rb") as fh:
@@ -181,25 +191,27 @@ def kernel_source_sha256():
     return h.hexdigest()
 
 
-def recorded_traffic(config_id, block_size, int8=False):
-    """HBM bytes per decode call from the committed PMC summary of this
-    workload, or None if there is none or the kernel sources changed since."""
-    import glob
+def traffic_from_profile(name, kind):
+    """HBM bytes per call from a committed PMC summary under profiles/, or
+    None if there is none or the kernel sources changed since it was taken."""
     import re
-    names = {(3, False): "decode_qwen25_7b_gqa_64seq_pmc.md",
-             (3, True): "decode_qwen25_7b_gqa_64seq_int8_pmc.md"}
-    name = names.get((config_id, int8)) if block_size in (None, 16) else None
-    if not name:
-        return None
     path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
         return None
     text = open(path).read()
     sha = re.search(r"^kernel_source_sha256: (\w+)", text, re.M)
     tr = re.search(r"^traffic_bytes_per_call: (\d+)", text, re.M)
-    if not sha or not tr or sha.group(1) != kernel_source_sha256():
+    if not sha or not tr or sha.group(1) != kernel_source_sha256(kind):
         return None
     return int(tr.group(1))
+
+
+def recorded_traffic(config_id, block_size, int8=False):
+    """HBM bytes per decode call of a workload from its PMC summary (or None)."""
+    names = {(3, False): "decode_qwen25_7b_gqa_64seq_pmc.md",
+             (3, True): "decode_qwen25_7b_gqa_64seq_int8_pmc.md"}
+    name = names.get((config_id, int8)) if block_size in (None, 16) else None
+    return traffic_from_profile(name, "decode") if name else None
 
 
 def main():

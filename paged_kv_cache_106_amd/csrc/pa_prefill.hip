@@ -44,96 +44,18 @@
 
 #include "pa.h"
 #include "pa_internal.h"
+#include "pa_mfma.h"
 
 namespace pa {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+using namespace mx;
 
 constexpr int kWavesP = 8;               // waves per workgroup
 constexpr int kThreadsP = 64 * kWavesP;
 constexpr int kRowsP = 16 * kWavesP;     // (token, head) rows per workgroup
 constexpr int kKeyTile = 64;             // keys per LDS tile
 constexpr int kMT = kKeyTile / 16;       // 16-key tiles of S^T per key tile
-
-// round-to-nearest-even narrowing and exact widening of the 16-bit types
-template <int DT>
-__device__ inline uint16_t narrow16(float x) {
-  if constexpr (DT == PA_F16) {
-    return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
-  } else {
-    const uint32_t u = __float_as_uint(x);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x0040u);
-    return static_cast<uint16_t>((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
-  }
-}
-// Two weights p0, p1 (finite, >= 0) as a 16-bit pair hi plus the pair of
-// remainders lo = p - hi, so hi + lo carries about 17 significant bits (the
-// remainder p - hi is exact in fp32).
-template <int DT>
-__device__ inline void split_pair(float p0, float p1, uint32_t& hi, uint32_t& lo) {
-  if constexpr (DT == PA_F16) {
-    const f16x2 h = __builtin_convertvector(f32x2{p0, p1}, f16x2);
-    const f32x2 r = f32x2{p0, p1} - __builtin_convertvector(h, f32x2);
-    hi = __builtin_bit_cast(uint32_t, h);
-    lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, f16x2));
-  } else {
-    const bf16x2 h = __builtin_convertvector(f32x2{p0, p1}, bf16x2);
-    const uint32_t hb = __builtin_bit_cast(uint32_t, h);
-    const float r0 = p0 - __uint_as_float(hb << 16);
-    const float r1 = p1 - __uint_as_float(hb & 0xffff0000u);
-    hi = hb;
-    lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{r0, r1}, bf16x2));
-  }
-}
-
-// 16 keys x 32 dims (A) times 32 dims x 16 rows (B), accumulated in c
-template <int DT>
-__device__ inline f32x4 mma_k32(uint4 a, uint4 b, f32x4 c) {
-  if constexpr (DT == PA_F16)
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
-                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-  else
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-}
-// 16 dims x 16 keys (A) times 16 keys x 16 rows (B)
-template <int DT>
-__device__ inline f32x4 mma_k16(uint2 a, uint2 b, f32x4 c) {
-  if constexpr (DT == PA_F16)
-    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
-                                                 __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
-  else
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
-                                                     __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
-}
-
-// max / sum over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four lanes of one row)
-// with the CDNA4 row swaps: v_permlane16_swap(x, x) returns x[l] and
-// x[l ^ 16] in its two results, v_permlane32_swap x[l] and x[l ^ 32].
-__device__ inline float row4_max(float x) {
-  const uint32_t b = __float_as_uint(x);
-  const auto r16 = __builtin_amdgcn_permlane16_swap(b, b, false, false);
-  x = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
-  const uint32_t c = __float_as_uint(x);
-  const auto r32 = __builtin_amdgcn_permlane32_swap(c, c, false, false);
-  return fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
-}
-__device__ inline float row4_sum(float x) {
-  const uint32_t b = __float_as_uint(x);
-  const auto r16 = __builtin_amdgcn_permlane16_swap(b, b, false, false);
-  x = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
-  const uint32_t c = __float_as_uint(x);
-  const auto r32 = __builtin_amdgcn_permlane32_swap(c, c, false, false);
-  return __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
-}
 
 struct PrefillParams {
   void* out;                   // [T][Hq][D] 16-bit
@@ -349,16 +271,12 @@ __global__ __launch_bounds__(kThreadsP, 4) void prefill_kernel(PrefillParams p) 
 #pragma unroll
       for (int ks = 0; ks < kMT / 2; ++ks) {
         // lane lr of group lg addresses dims 16dt + 4(lr%4) .. +4 of key
-        // 32ks + 4lg + lr/4; the transposing read (in each 16-lane group, lane
-        // i receives element i%4 of the units that lanes i/4, i/4 + 4, i/4 + 8
-        // and i/4 + 12 address) hands lane lr dim 16dt + lr of keys
-        // 32ks + 4lg + 0..3, and a second read the same 16 keys further on
+        // 32ks + 4lg + lr/4; the transposing read hands lane lr dim 16dt + lr
+        // of keys 32ks + 4lg + 0..3, and a second read the same 16 keys
+        // further on
         const char* vp = buf + L::K_BYTES + (32 * ks + 4 * lg + (lr >> 2)) * L::ROW +
                          (16 * dt + 4 * (lr & 3)) * 2;
-        typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-        const s16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp));
-        const s16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 16 * L::ROW));
-        const uint2 b0 = __builtin_bit_cast(uint2, a0), b1 = __builtin_bit_cast(uint2, a1);
+        const uint2 b0 = ds_read_tr16(vp), b1 = ds_read_tr16(vp + 16 * L::ROW);
         const uint4 a = make_uint4(b0.x, b0.y, b1.x, b1.y);
         acc[dt] = mma_k32<DT>(a, phi[ks], acc[dt]);
         acc[dt] = mma_k32<DT>(a, plo[ks], acc[dt]);
