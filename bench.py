@@ -156,7 +156,7 @@ def run_prefill(args):
         "roofline": {"bound": "mfma", "kernel": "pa_prefill: prefill_kernel",
                      "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": traffic_from_profile("prefill_qwen25_7b_gqa_8x512_pmc.md",
+                     "traffic": traffic_from_profile("prefill_qwen25_7b_gqa_8x512_profile.md",
                                                      "prefill"),
                      "traffic_unit": "bytes per call (FETCH_SIZE x2 + WRITE_SIZE, copy-calibrated)"},
     }
@@ -217,8 +217,8 @@ def recorded_traffic(config_id, block_size, int8=False):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--block-size", type=int, default=None, choices=[16, 32])
     ap.add_argument("--kv-dtype", default=None, choices=["int8"],
@@ -257,7 +257,10 @@ def main():
     if args.prefill:
         return run_prefill(args)
     overrides = {"block_size": args.block_size} if args.block_size else {}
-    w = workload(args.config, "full", **overrides)
+    # each step appends a token to every sequence: the cache starts short by
+    # the warm-up plus half the timed steps, so the timed steps centre on the
+    # workload's lengths
+    w = workload(args.config, "full", length_shift=args.warmup + args.steps // 2, **overrides)
     log(f"[bench] {w.spec.name}; bs={w.bs}; S={w.S}; KV bytes/step ~{w.kv_bytes()/1e6:.1f} MB")
     t0 = time.perf_counter()
     int8 = args.kv_dtype == "int8"
@@ -268,11 +271,6 @@ def main():
     per_tok = g.cache.kv_bytes_per_token()
     shared = (w.spec.prefix_seqs - 1) * w.spec.prefix_len if w.spec.prefix_seqs > 1 else 0
 
-    for _ in range(args.warmup):
-        step(g.q, g.k_new, g.v_new)
-    torch.cuda.synchronize()
-    log(f"[bench] {args.warmup} warmup steps done")
-
     # HIP events recorded by the decode's launches themselves (hipExtLaunchKernel):
     # start of its first kernel, end of its last, on the step's stream, with no
     # marker packet in the stream (a marker costs a few microseconds of GPU time)
@@ -280,13 +278,18 @@ def main():
     # TIME_EVERY-th step's decode is timed)
     from paged_kv_cache_106_amd._hip import Event
     ev = {k: (Event(timing=True), Event(timing=True)) for k in range(0, args.steps, TIME_EVERY)}
-    kv_bytes = 0
+    kv_bytes, len_sum = 0, 0.0
     host = np.zeros((args.steps, 4))                            # host seconds per phase
-    torch.cuda.synchronize()
+    # the collector is run and paused before the warm-up, so nothing but the
+    # synchronisation separates the warm-up from the timed steps (an idle GPU
+    # between them changes its clocks for the first timed steps)
     gc.collect()
     gc_was_enabled = gc.isenabled()
     if args.no_gc:
         gc.disable()       # a collection pass over this large heap stalls the host for ~30 ms
+    for _ in range(args.warmup):
+        step(g.q, g.k_new, g.v_new)
+    torch.cuda.synchronize()
     t_start = time.perf_counter()
     for k in range(args.steps):
         h0 = time.perf_counter()
@@ -299,11 +302,12 @@ def main():
         step.attend(g.q, *ev.get(k, (None, None)))              # a4 | a5 + a6
         host[k] = (h1 - h0, h2 - h1, h3 - h2, time.perf_counter() - h3)
         kv_bytes += (int(step.host_context_lens.astype(np.int64).sum()) - shared) * per_tok
+        len_sum += float(step.host_context_lens.mean())
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
     if gc_was_enabled:
         gc.enable()
-    log(f"[bench] {args.steps} timed steps done")
+    log(f"[bench] {args.warmup} warmup and {args.steps} timed steps done")
 
     t_decode = np.array([a.elapsed_time(b) for a, b in ev.values()]) * 1e-3   # s
     kv_per_call = kv_bytes / args.steps
@@ -334,7 +338,7 @@ def main():
             "num_seqs": w.S, "num_q_heads": w.Hq, "num_kv_heads": w.Hkv, "head_dim": w.D,
             "block_size": w.bs, "kernel": w.spec.kernel,
             "partition_size": w.spec.partition_size if w.spec.kernel == "partitioned" else None,
-            "mean_context_len": float(step.host_context_lens.mean()),
+            "mean_context_len": round(len_sum / args.steps, 2),      # over the timed steps
             "kv_dtype": "int8 codes + fp32 row scales" if int8 else w.dtype,
             "kv_bytes_per_step": int(kv_per_call),
             "kv_bytes_counting": ("unique (a shared prefix once)" if shared else "logical") +
@@ -366,7 +370,9 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample")
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, int8)
+        # the oracle on the workload's own lengths
+        result["cpu_baseline"] = cpu_baseline(workload(args.config, "full", **overrides),
+                                              args.cpu_seconds, int8)
     print(json.dumps(result), flush=True)
 
 

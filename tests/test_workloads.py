@@ -1,0 +1,54 @@
+"""The seeded input generators (workloads/): every decode and prefill workload
+builds, its lengths follow its spec, and the benchmark's length shift keeps
+the pool and the block order of the drawn workload."""
+import numpy as np
+import pytest
+
+from workloads import SPECS, prefill_workload, workload
+
+
+@pytest.mark.parametrize("cfg", sorted(SPECS))
+@pytest.mark.parametrize("variant", ["small", "full"])
+def test_decode_workloads_build(cfg, variant):
+    w = workload(cfg, variant)
+    s = w.spec
+    assert w.lengths.shape == (s.num_seqs,) and (w.lengths >= 1).all()
+    if s.lengths in ("uniform", "loguniform"):
+        assert (w.lengths >= s.len_lo).all() and (w.lengths <= s.len_hi).all()
+    if s.prefix_seqs:
+        assert (w.lengths[: s.prefix_seqs] > s.prefix_len).all()
+    # the pool is a permutation of its blocks and holds every sequence
+    assert np.array_equal(np.sort(w.initial_free_order), np.arange(w.num_blocks))
+    need = sum(-(-int(x) // w.bs) for x in w.lengths)
+    if s.prefix_seqs > 1:
+        need -= (s.prefix_seqs - 1) * (s.prefix_len // w.bs)
+    assert w.num_blocks >= need
+
+
+@pytest.mark.parametrize("cfg", [3, 4, 5])
+def test_length_shift_keeps_pool_and_order(cfg):
+    w0 = workload(cfg, "full")
+    w = workload(cfg, "full", length_shift=200)
+    assert w.num_blocks == w0.num_blocks
+    assert np.array_equal(w.initial_free_order, w0.initial_free_order)
+    floor = np.ones_like(w0.lengths)
+    floor[: w0.spec.prefix_seqs] = w0.spec.prefix_len + 1
+    assert np.array_equal(w.lengths, np.maximum(w0.lengths - 200, floor))
+    # the steps a benchmark appends fit in the pool the drawn lengths sized
+    grown = sum(-(-(int(x) + 300) // w.bs) for x in w.lengths)
+    if w.spec.prefix_seqs > 1:
+        grown -= (w.spec.prefix_seqs - 1) * (w.spec.prefix_len // w.bs)
+    assert grown <= w.num_blocks
+
+
+@pytest.mark.parametrize("variant", ["small", "full"])
+def test_prefill_workloads_build(variant):
+    w = prefill_workload(variant)
+    assert (w.chunks >= 0).all() and (w.chunks <= w.lengths).all()
+    assert w.query_start[0] == 0 and np.array_equal(np.diff(w.query_start), w.chunks)
+    assert w.T == int(w.chunks.sum())
+    # causal FLOPs: 4 D Hq per (query row, visible key); row k of chunk i sees
+    # L_i - n_i + k + 1 keys
+    keys = sum(int(n) * (int(L) - int(n)) + int(n) * (int(n) + 1) // 2
+               for L, n in zip(w.lengths, w.chunks))
+    assert w.flops() == 4 * w.D * w.Hq * keys

@@ -81,6 +81,11 @@ class Spec:
     num_blocks: int = 0           # 0 -> 1.25x the unique blocks needed
     pool_factor: float = 1.25
     seed: int = 0
+    # Start every sequence this many tokens short of its drawn length (not
+    # below 1, nor below the shared prefix + 1): a decode benchmark that
+    # appends one token per step then spends its timed steps around the drawn
+    # lengths.  The pool size and the block order follow the drawn lengths.
+    length_shift: int = 0
 
 
 SPECS = {
@@ -238,6 +243,10 @@ def make_workload(s: Spec) -> Workload:
     if nb < blocks:
         raise ValueError("pool smaller than the blocks the lengths need")
     perm = _rng(s.seed, STREAM_PERM).permutation(nb).astype(np.int32)
+    if s.length_shift:
+        floor = np.ones_like(L)
+        floor[: s.prefix_seqs] = s.prefix_len + 1
+        L = np.maximum(L - s.length_shift, floor).astype(np.int32)
 
     ops = []
     if s.prefix_seqs:
