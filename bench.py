@@ -261,6 +261,16 @@ def main():
     # the warm-up plus half the timed steps, so the timed steps centre on the
     # workload's lengths
     w = workload(args.config, "full", length_shift=args.warmup + args.steps // 2, **overrides)
+    # a pool the configuration fixes (the tiny workload's 64 blocks) may not
+    # hold the tokens the steps append: it then grows to what they need
+    grown = args.warmup + args.steps + 1
+    need = sum(-(-(int(x) + grown) // w.bs) for x in w.lengths)
+    if w.spec.prefix_seqs > 1:
+        need -= (w.spec.prefix_seqs - 1) * (w.spec.prefix_len // w.bs)
+    pool_grown = need > w.num_blocks
+    if pool_grown:
+        w = workload(args.config, "full", length_shift=args.warmup + args.steps // 2,
+                     num_blocks=need, **overrides)
     log(f"[bench] {w.spec.name}; bs={w.bs}; S={w.S}; KV bytes/step ~{w.kv_bytes()/1e6:.1f} MB")
     t0 = time.perf_counter()
     int8 = args.kv_dtype == "int8"
@@ -339,6 +349,8 @@ def main():
             "block_size": w.bs, "kernel": w.spec.kernel,
             "partition_size": w.spec.partition_size if w.spec.kernel == "partitioned" else None,
             "mean_context_len": round(len_sum / args.steps, 2),      # over the timed steps
+            "num_blocks": w.num_blocks,
+            "pool_grown_for_steps": pool_grown,
             "kv_dtype": "int8 codes + fp32 row scales" if int8 else w.dtype,
             "kv_bytes_per_step": int(kv_per_call),
             "kv_bytes_counting": ("unique (a shared prefix once)" if shared else "logical") +
