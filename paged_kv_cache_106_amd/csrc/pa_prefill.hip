@@ -211,6 +211,10 @@ __global__ __launch_bounds__(kThreadsP, 4) void prefill_kernel(PrefillParams p) 
       for (int j = 0; j < LOADS; ++j) blk[j] = block_of(t + 2, j);
     }
 
+    // the waves of a workgroup run each tile's phases in step (one barrier
+    // per tile); a wave issuing matrix products takes priority, so the
+    // products of some waves overlap the softmax of others (~2 % faster)
+    __builtin_amdgcn_s_setprio(1);
     // S^T for keys t*KT + 16*mt + 4*lg + r of this lane's row
     f32x4 s[kMT];
 #pragma unroll
@@ -223,6 +227,7 @@ __global__ __launch_bounds__(kThreadsP, 4) void prefill_kernel(PrefillParams p) 
         s[mt] = mma_k32<DT>(a, qb[ks], s[mt]);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     // online softmax of the row (base 2); keys past the row's position get
     // weight 0, tested only on tiles that reach past the wave's first row
     float x[4 * kMT];
@@ -253,6 +258,7 @@ __global__ __launch_bounds__(kThreadsP, 4) void prefill_kernel(PrefillParams p) 
       pr[k] = __builtin_amdgcn_exp2f(x[k] - m_run);   // exp2(-inf) = 0
       l_lane += pr[k];
     }
+    __builtin_amdgcn_s_setprio(1);
     // O^T += V^T P^T on 16x16x32 products: k-step ks takes the 32 keys of
     // S^T tiles 2ks and 2ks + 1, ordered so that lane group lg's 8 k values
     // are its own keys 4lg + r of both tiles (P^T straight from registers);
@@ -282,6 +288,7 @@ __global__ __launch_bounds__(kThreadsP, 4) void prefill_kernel(PrefillParams p) 
         acc[dt] = mma_k32<DT>(a, plo[ks], acc[dt]);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     if (t + 1 < ntiles) store_tile(lds + ((t + 1) & 1) * L::BUF, kr, vr);
     __syncthreads();   // tile t + 1 is in place; tile t's buffer may be rewritten
   }
