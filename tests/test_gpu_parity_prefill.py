@@ -78,6 +78,8 @@ CASES = [
     dict(num_q_heads=8, num_kv_heads=1, dtype="f16"),                         # MQA, G = 8
     dict(num_q_heads=12, num_kv_heads=2, head_dim=64, contexts=(300, 47, 129, 5),
          chunks=(300, 46, 64, 5)),                                            # G = 6, whole prompts
+    dict(num_q_heads=16, num_kv_heads=2, head_dim=64, block_size=32, dtype="f16",
+         contexts=(100, 50, 7, 300, 33), chunks=(10, 0, 7, 1, 0)),            # empty chunks, bs 32
 ]
 
 
