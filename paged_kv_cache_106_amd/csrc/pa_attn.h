@@ -12,16 +12,18 @@
 // w, w+4, ...; each wave runs its own softmax over its units, chunk by chunk
 // (the partition for the split kernel), in three phases:
 //
-//  1. logits.  8 lanes per token, each holding 16-byte pieces of the K row
+//  1. logits.  8 lanes per token (16 for groups of 5 or more heads, the
+//     narrow layout), each holding 16-byte pieces of the K row
 //     (buffer_load_dwordx4), take partial dot products with the matching q
 //     elements of every head of the group (v_dot2 on 16-bit pairs, fp32
-//     accumulate); a 3-step DPP sum finishes each dot product and the raw
-//     logits go to the wave's rows of LDS.
+//     accumulate); a 3- or 4-step DPP sum finishes each dot product and the
+//     raw logits go to the wave's rows of LDS.
 //  2. softmax.  The wave scales them into the base-2 domain (scale * log2 e),
 //     takes its max per head, overwrites them with p = 2^(logit - max) and
 //     sums them.
 //  3. P.V.  D/8 lanes per token, each holding 8 consecutive dims of the V
-//     row, accumulate p * V for every head in fp32 registers.
+//     row (D/4 lanes with 4 dims in the narrow layout), accumulate p * V for
+//     every head in fp32 registers.
 //
 // K and V stream through a ring of unit buffers per wave, every refill
 // issued on every path so that the wait counts track the ring.  At the end
@@ -32,7 +34,8 @@
 // ("v2") stores (max, sum, acc) of its partition and the merge kernel
 // combines the partitions.
 //
-// Loads use a wave-uniform block base and per-lane 32-bit offsets.  A wave's
+// Loads use a wave-uniform block base and per-lane 32-bit offsets, with the
+// non-temporal cache policy (each K/V byte is read once).  A wave's
 // block ids arrive in one vector load (lane i: its unit i) and are read back
 // with readlane; tail tokens of the last block are masked by select (the
 // pools' unused slots may hold NaN).
