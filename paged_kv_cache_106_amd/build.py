@@ -38,6 +38,7 @@ SOURCES = [
     "pa_attn_q8_f16_d128.hip",
     "pa_attn_q8_bf16_d64.hip",
     "pa_attn_q8_bf16_d128.hip",
+    "pa_attn_q8_mfma.hip",
     "pa_prefill.hip",
     "pa_allocator.cpp",
 ]

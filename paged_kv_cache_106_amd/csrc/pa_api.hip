@@ -406,7 +406,11 @@ pa_status partitioned(AttnParams& p, bool q8, pa_dtype dtype, int32_t head_dim,
   auto launch = pa::attn_launcher(dtype, head_dim, q8);
   const bool any = work_items ? num_work_items > 0 : parts > 0;
   if (any) {
-    const pa_status s1 = pa::launched(launch(1, p, stream, start_event, nullptr), what);
+    const bool mfma = q8 && p.group >= pa::kQ8MfmaMinGroup;
+    const pa_status s1 = pa::launched(
+        mfma ? pa::launch_attn_q8_mfma_split(dtype, head_dim, p, stream, start_event, nullptr)
+             : launch(1, p, stream, start_event, nullptr),
+        what);
     if (s1 != PA_OK) return s1;
   }
   return pa::launched(launch(2, p, stream, any ? nullptr : start_event, stop_event), what);

@@ -67,6 +67,15 @@ int launch_attn_q8_bf16_d64(int kind, const AttnParams& p, hipStream_t stream, h
                             hipEvent_t stop);
 int launch_attn_q8_bf16_d128(int kind, const AttnParams& p, hipStream_t stream, hipEvent_t start,
                              hipEvent_t stop);
+// Split-context partitions over INT8 pools on the matrix cores (up to 16
+// query heads per workgroup; the launcher sets p.head_chunks and
+// p.heads_per_wg for it); the merge is kind 2 of the launchers above.
+int launch_attn_q8_mfma_split(int dtype, int head_dim, const AttnParams& p, hipStream_t stream,
+                              hipEvent_t start, hipEvent_t stop);
+// Query heads per KV head from which INT8 split-context decodes use it: with
+// fewer, the vector kernel keeps up with the memory stream (measured: 4 heads
+// 4 % slower on the matrix cores, 5 heads 1.25x faster, 7 heads 1.55x).
+constexpr int kQ8MfmaMinGroup = 5;
 int launch_cache_write(const void* key, const void* value, void* k_cache, void* v_cache,
                        const int64_t* slots, int32_t n, int32_t chunks_per_tok,
                        int64_t num_slots, hipStream_t stream);
