@@ -86,14 +86,18 @@ def test_int8_small_workloads(cfg, bs):
 
 
 EDGE = [
-    # Hq, Hkv, D, bs, dtype
+    # Hq, Hkv, D, bs, dtype   (split-context decodes of 5+ heads per KV head
+    # run on the matrix-core kernel, the others on the vector kernel)
     (4, 4, 64, 16, "f16"),        # MHA, D 64
-    (8, 1, 128, 16, "bf16"),      # MQA, G = 8 (narrow lanes)
+    (8, 1, 128, 16, "bf16"),      # MQA, G = 8
     (14, 2, 128, 32, "bf16"),     # G = 7, bs 32
     (6, 2, 64, 16, "f16"),        # G = 3, D 64
-    (10, 2, 128, 16, "f16"),      # G = 5, f16 (narrow lanes)
+    (10, 2, 128, 16, "f16"),      # G = 5, f16
     (8, 2, 128, 16, "bf16"),      # G = 4 (wide lanes)
-    (24, 2, 128, 16, "bf16"),     # G = 12: two head chunks of 6
+    (24, 2, 128, 16, "bf16"),     # G = 12: one head chunk (two of 6 in the single pass)
+    (12, 2, 64, 32, "f16"),       # G = 6, D 64, bs 32
+    (20, 4, 64, 16, "bf16"),      # G = 5, D 64
+    (36, 2, 128, 16, "bf16"),     # G = 18: head chunks of 16 and 2 (three of 6 in the single pass)
 ]
 
 
