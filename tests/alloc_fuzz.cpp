@@ -12,6 +12,8 @@
 //     sequence falls in its table's block at its offset;
 //   * a failed call (OOM or a bad argument) leaves all of the above as it
 //     was.
+// It also runs the host work-list builder (pa_partition_work_items) on random
+// lengths with output buffers of exactly the stated capacity.
 // Usage: alloc_fuzz <seed> <steps>; exit status 0 when every check held.
 #include <algorithm>
 #include <cstdint>
@@ -244,6 +246,42 @@ int main(int argc, char** argv) {
       if (g_failures > 20) break;
     }
     pa_alloc_destroy(a);
+  }
+  // the host work-list builder, with output buffers of exactly the stated
+  // capacity (too small ones included: it must write only `capacity` items)
+  for (int it = 0; it < 300; ++it) {
+    const int32_t ns = uni(0, 40);
+    const int32_t P = std::vector<int32_t>{16, 32, 64, 512, 1024}[uni(0, 4)];
+    const int32_t max_parts = uni(0, 2) ? -1 : uni(1, 8);
+    std::vector<int32_t> lens(ns);
+    int64_t want = 0;
+    for (int32_t i = 0; i < ns; ++i) {
+      lens[i] = uni(0, 5000);
+      int64_t parts = (lens[i] + P - 1) / P;
+      if (max_parts >= 0 && parts > max_parts) parts = max_parts;
+      want += parts;
+    }
+    const int32_t cap = uni(0, 2) ? static_cast<int32_t>(want) : uni(0, static_cast<int>(want) + 2);
+    std::vector<int32_t> items(2 * static_cast<size_t>(cap));
+    int32_t n = -1;
+    const pa_status st = pa_partition_work_items(lens.data(), ns, P, max_parts,
+                                                 cap ? items.data() : nullptr, cap, &n);
+    if (cap >= want) {
+      CHECK(st == PA_OK && n == want, "work list: status %d, %d items of %lld", st, n,
+            static_cast<long long>(want));
+      // every live (sequence, partition) pair once, within max_parts
+      std::map<std::pair<int32_t, int32_t>, int> seen;
+      for (int32_t k = 0; k < n && st == PA_OK; ++k) {
+        const int32_t sq = items[2 * k], pt = items[2 * k + 1];
+        CHECK(sq >= 0 && sq < ns && pt >= 0 && static_cast<int64_t>(pt) * P < lens[sq] &&
+                  (max_parts < 0 || pt < max_parts),
+              "work list item (%d, %d)", sq, pt);
+        CHECK(++seen[{sq, pt}] == 1, "work list item (%d, %d) twice", sq, pt);
+      }
+    } else {
+      CHECK(st != PA_OK, "work list: %lld items into a capacity of %d reported ok",
+            static_cast<long long>(want), cap);
+    }
   }
   if (g_failures) {
     std::fprintf(stderr, "%d checks failed\n", g_failures);
