@@ -276,7 +276,7 @@ int main(int argc, char** argv) {
         CHECK(sq >= 0 && sq < ns && pt >= 0 && static_cast<int64_t>(pt) * P < lens[sq] &&
                   (max_parts < 0 || pt < max_parts),
               "work list item (%d, %d)", sq, pt);
-        CHECK(++seen[{sq, pt}] == 1, "work list item (%d, %d) twice", sq, pt);
+        CHECK(++seen[std::make_pair(sq, pt)] == 1, "work list item (%d, %d) twice", sq, pt);
       }
     } else {
       CHECK(st != PA_OK, "work list: %lld items into a capacity of %d reported ok",
