@@ -169,6 +169,9 @@ size_t pa_decode_partitioned_workspace_size(int32_t num_seqs,
  * l = sum exp(logit - m) and acc = sum exp(logit - m) V; a second kernel
  * merges: out = sum_p e^(m_p - M) acc_p / sum_p e^(m_p - M) l_p with
  * M = max_p m_p.  Result as pa_decode up to fp32 rounding order.
+ * A context_lens[i] above max_context_len breaks the caller's side of the
+ * contract: only its first ceil(max_context_len / P) partitions are read
+ * (every access still stays inside the caller's buffers).
  * start_event / stop_event as for pa_decode: recorded when the first kernel
  * starts and the merge ends.
  * ---------------------------------------------------------------------- */
