@@ -175,6 +175,15 @@ KERNEL_SOURCES = {
 }
 
 
+def input_digests(w):
+    """sha256 (first 16 hex digits) of the workload's small host inputs: the
+    drawn lengths, the initial order of the block pool and the queries, so a
+    run can be matched to its inputs."""
+    import hashlib
+    d = lambda a: hashlib.sha256(np.ascontiguousarray(a).tobytes()).hexdigest()[:16]
+    return {"lengths": d(w.lengths), "free_order": d(w.initial_free_order), "q": d(w.query())}
+
+
 def kernel_source_sha256(kind="decode"):
     """sha256 over the sources one kernel family is built and launched from."""
     import glob
@@ -348,6 +357,8 @@ def main():
             "num_seqs": w.S, "num_q_heads": w.Hq, "num_kv_heads": w.Hkv, "head_dim": w.D,
             "block_size": w.bs, "kernel": w.spec.kernel,
             "partition_size": w.spec.partition_size if w.spec.kernel == "partitioned" else None,
+            "seed": w.spec.seed,
+            "inputs_sha256": input_digests(w),
             "mean_context_len": round(len_sum / args.steps, 2),      # over the timed steps
             "num_blocks": w.num_blocks,
             "pool_grown_for_steps": pool_grown,
@@ -359,6 +370,7 @@ def main():
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "seqs_per_s_per_layer": round(w.S * args.steps / elapsed, 1),
         "decode_us": round(dec_avg * 1e6, 2),
+        "decode_us_p50": round(float(np.median(t_decode)) * 1e6, 2),
         "decode_timed_steps": len(t_decode),
         "decode_us_p10_p90": [round(float(np.percentile(t_decode, 10)) * 1e6, 2),
                               round(float(np.percentile(t_decode, 90)) * 1e6, 2)],
