@@ -105,6 +105,13 @@ struct Fmt<PA_F16> {
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, a),
                                   __builtin_bit_cast(half2v, b), c, false);
   }
+  // dot2(a, b, 0) in the three-operand encoding with an inline 0: the
+  // compiler's two-operand form needs a move to zero its accumulator first
+  __device__ static inline float dot2_first(uint32_t a, uint32_t b) {
+    float r;
+    asm("v_dot2_f32_f16 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+  }
   // round to nearest even (the default rounding mode of v_cvt_f16_f32)
   __device__ static inline uint16_t narrow(float x) {
     return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
@@ -122,6 +129,11 @@ struct Fmt<PA_BF16> {
   __device__ static inline float dot2(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162v, a),
                                            __builtin_bit_cast(bf162v, b), c, false);
+  }
+  __device__ static inline float dot2_first(uint32_t a, uint32_t b) {
+    float r;
+    asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+    return r;
   }
   // round to nearest even: add 0x7fff plus the lowest kept bit, truncate
   __device__ static inline uint16_t narrow(float x) {
@@ -435,8 +447,16 @@ struct WaveAttn {
     const int tid = threadIdx.x;
     wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     lane = tid & 63;
-    krow = lane / QL;
-    kcol = lane % QL;
+    if constexpr (QL == 16) {
+      // a token's 16 lanes: 8 in an even row and the same 8 in the next row
+      // (lanes l and l + 16), so the last step of the dot-product sum is a
+      // row swap that finishes two token groups at once
+      krow = 2 * (lane >> 5) + ((lane >> 3) & 1);
+      kcol = (lane & 7) + 8 * ((lane >> 4) & 1);
+    } else {
+      krow = lane / QL;
+      kcol = lane % QL;
+    }
     vrow = lane / VL;
     vcol = lane % VL;
     kbase = static_cast<const char*>(p.k_cache);
@@ -546,68 +566,108 @@ struct WaveAttn {
 
   // Logits of the wave's unit i (raw q.k; scaled in the softmax), written by
   // the lane holding column 0 of each token.
+  // The lane's part of the raw q.k of its token in load group j, head hh.
+  __device__ __forceinline__ float qk_part(const uint4 (&qv)[GT][KC], const KBuf& kx, int j,
+                                           int hh) const {
+    if constexpr (Q8) {
+      // the lane's codes as exact 16-bit pairs, in dim order: pair m holds
+      // dims 2m, 2m + 1 of the lane's KB
+      constexpr int NW = Words<KVec>::N;
+      uint32_t w[NW], kp[2 * NW];
+      Words<KVec>::get(kx.d[j], w);
+#pragma unroll
+      for (int m = 0; m < NW; ++m) {
+        kp[2 * m] = F::pack_int(code_at<0>(w[m]), code_at<1>(w[m]));
+        kp[2 * m + 1] = F::pack_int(code_at<2>(w[m]), code_at<3>(w[m]));
+      }
+      float a = F::dot2_first(qv[hh][0].x, kp[0]);
+#pragma unroll
+      for (int c = 0; c < KC; ++c) {
+        if (c > 0) a = F::dot2(qv[hh][c].x, kp[4 * c], a);
+        a = F::dot2(qv[hh][c].y, kp[4 * c + 1], a);
+        a = F::dot2(qv[hh][c].z, kp[4 * c + 2], a);
+        a = F::dot2(qv[hh][c].w, kp[4 * c + 3], a);
+      }
+      return a;
+    } else {
+      float a = F::dot2_first(qv[hh][0].x, kx.d[j * KC].x);
+#pragma unroll
+      for (int c = 0; c < KC; ++c) {
+        const uint4 k = kx.d[j * KC + c];
+        if (c > 0) a = F::dot2(qv[hh][c].x, k.x, a);
+        a = F::dot2(qv[hh][c].y, k.y, a);
+        a = F::dot2(qv[hh][c].z, k.z, a);
+        a = F::dot2(qv[hh][c].w, k.w, a);
+      }
+      return a;
+    }
+  }
+
+  // Logits of the wave's unit i (raw q.k; scaled in the softmax), written by
+  // the first lane of each token's lanes.
   __device__ __forceinline__ void qk_unit(const uint4 (&qv)[GT][KC], const KBuf& kx,
                                           int i) const {
     const int u = wave + kWaves * i;
+    if constexpr (QL == 16) {
+      // groups j and j + 1 together: each lane sums its 8-lane half of a
+      // token, then v_permlane16_swap trades rows so that one add leaves
+      // group j's totals in rows 0 and 2 and group j + 1's in rows 1 and 3
+      static_assert(KGROUPS % 2 == 0, "QK groups come in pairs");
+      const int odd = (lane >> 4) & 1;
 #pragma unroll
-    for (int j = 0; j < KGROUPS; ++j) {
-      float sv[GTP];
-      if constexpr (Q8) {
-        // the lane's codes as exact 16-bit pairs, in dim order: pair m holds
-        // dims 2m, 2m + 1 of the lane's KB
-        constexpr int NW = Words<KVec>::N;
-        uint32_t w[NW], kp[2 * NW];
-        Words<KVec>::get(kx.d[j], w);
-#pragma unroll
-        for (int m = 0; m < NW; ++m) {
-          kp[2 * m] = F::pack_int(code_at<0>(w[m]), code_at<1>(w[m]));
-          kp[2 * m + 1] = F::pack_int(code_at<2>(w[m]), code_at<3>(w[m]));
-        }
+      for (int j = 0; j < KGROUPS; j += 2) {
+        float sv[GTP];
 #pragma unroll
         for (int hh = 0; hh < GT; ++hh) {
-          float a = 0.f;
-#pragma unroll
-          for (int c = 0; c < KC; ++c) {
-            a = F::dot2(qv[hh][c].x, kp[4 * c], a);
-            a = F::dot2(qv[hh][c].y, kp[4 * c + 1], a);
-            a = F::dot2(qv[hh][c].z, kp[4 * c + 2], a);
-            a = F::dot2(qv[hh][c].w, kp[4 * c + 3], a);
-          }
-          sv[hh] = group_sum<QL>(a) * kx.sc[j];
+          const float a0 = group_sum<8>(qk_part(qv, kx, j, hh));
+          const float a1 = group_sum<8>(qk_part(qv, kx, j + 1, hh));
+          const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a0),
+                                                          __float_as_uint(a1), false, false);
+          sv[hh] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+          if constexpr (Q8) sv[hh] *= odd ? kx.sc[j + 1] : kx.sc[j];
         }
-      } else {
 #pragma unroll
-        for (int hh = 0; hh < GT; ++hh) {
-          float a = 0.f;
-#pragma unroll
-          for (int c = 0; c < KC; ++c) {
-            const uint4 k = kx.d[j * KC + c];
-            a = F::dot2(qv[hh][c].x, k.x, a);
-            a = F::dot2(qv[hh][c].y, k.y, a);
-            a = F::dot2(qv[hh][c].z, k.z, a);
-            a = F::dot2(qv[hh][c].w, k.w, a);
-          }
-          sv[hh] = group_sum<QL>(a);
-        }
+        for (int hh = GT; hh < GTP; ++hh) sv[hh] = 0.f;
+        if ((lane & 7) == 0) lds_store(s_lds + (u * UNIT + (j + odd) * KTOK + krow) * GTP, sv);
       }
+    } else {
 #pragma unroll
-      for (int hh = GT; hh < GTP; ++hh) sv[hh] = 0.f;
-      if (kcol == 0) lds_store(s_lds + (u * UNIT + j * KTOK + krow) * GTP, sv);
+      for (int j = 0; j < KGROUPS; ++j) {
+        float sv[GTP];
+#pragma unroll
+        for (int hh = 0; hh < GT; ++hh) {
+          sv[hh] = group_sum<QL>(qk_part(qv, kx, j, hh));
+          if constexpr (Q8) sv[hh] *= kx.sc[j];
+        }
+#pragma unroll
+        for (int hh = GT; hh < GTP; ++hh) sv[hh] = 0.f;
+        if (kcol == 0) lds_store(s_lds + (u * UNIT + j * KTOK + krow) * GTP, sv);
+      }
     }
   }
 
   // P.V of the wave's unit i; tokens past n get V = 0 (their p is 0 and their
   // slots may hold NaN).
-  __device__ __forceinline__ void pv_unit(float (&acc)[GT][VW], const VBuf& vx,
+  __device__ __forceinline__ void pv_unit(float (&acc)[GT][VW], VBuf& vx,
                                           const Span& s, int i) const {
     const int u = wave + kWaves * i;
-    const bool tail = (u + 1) * UNIT > s.n;
+    if ((u + 1) * UNIT > s.n) {   // uniform: only the span's last unit
+      asm volatile("");   // keeps this a branch (not selects on every unit)
+#pragma unroll
+      for (int j = 0; j < VLOADS; ++j) {
+        if (u * UNIT + j * VTOK + vrow >= s.n) {
+          if constexpr (Q8)
+            vx.sc[j] = 0.f;
+          else
+            vx.d[j] = VVec{};
+        }
+      }
+    }
     if constexpr (Q8) {
 #pragma unroll
       for (int j = 0; j < VLOADS; ++j) {
         const int t = u * UNIT + j * VTOK + vrow;
-        // a tail token's scale may be NaN: its weight is 0 by select
-        const float vs = (tail && t >= s.n) ? 0.f : vx.sc[j];
+        const float vs = vx.sc[j];   // 0 past the span
         constexpr int NW = Words<VVec>::N;
         uint32_t w[NW];
         Words<VVec>::get(vx.d[j], w);
@@ -638,10 +698,6 @@ struct WaveAttn {
           w[0] = vx.d[j].x; w[1] = vx.d[j].y; w[2] = vx.d[j].z; w[3] = vx.d[j].w;
         } else {
           w[0] = vx.d[j].x; w[1] = vx.d[j].y;
-        }
-        if (tail && t >= s.n) {
-#pragma unroll
-          for (int e = 0; e < VW / 2; ++e) w[e] = 0;
         }
         float pr[GTP];
         lds_load(pr, s_lds + t * GTP);
