@@ -357,6 +357,7 @@ def main():
             "num_seqs": w.S, "num_q_heads": w.Hq, "num_kv_heads": w.Hkv, "head_dim": w.D,
             "block_size": w.bs, "kernel": w.spec.kernel,
             "partition_size": w.spec.partition_size if w.spec.kernel == "partitioned" else None,
+            "partition_grid": g.step.last_grid,
             "seed": w.spec.seed,
             "inputs_sha256": input_digests(w),
             "mean_context_len": round(len_sum / args.steps, 2),      # over the timed steps

@@ -120,16 +120,21 @@ class DecodeStep:
 
     RING = 8            # pinned staging buffers
     EVENT_EVERY = 4     # write launches per recorded event (<= RING)
+    DENSE_RATIO = 3     # "auto": dense grid while it has <= this many times the list's workgroups
 
     def __init__(self, cache, seq_ids, num_q_heads, kernel="partitioned", partition_size=512,
-                 max_context_len=None, scale=None, stream=None):
+                 max_context_len=None, scale=None, stream=None, grid="auto"):
         self.cache = cache
         self.seq_ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
         self.S = int(self.seq_ids.shape[0])
         self.num_q_heads = int(num_q_heads)
         if kernel not in ("partitioned", "single"):
             raise ValueError(kernel)
+        if grid not in ("auto", "list", "dense"):
+            raise ValueError(grid)
         self.kernel = kernel
+        self.grid = grid
+        self.last_grid = None        # the partitioned decode's grid of the last prepared step
         self.partition_size = int(partition_size)
         bs = cache.block_size
         if max_context_len is None:
@@ -260,6 +265,23 @@ class DecodeStep:
         self.stream.synchronize()
         self.host_context_lens[:] = lens
 
+    @staticmethod
+    def dense_grid(grid, max_parts, num_seqs, num_items, ratio):
+        """Whether the partitioned decode runs on its dense grid instead of
+        the work list.  The dense grid, (max_parts | 1) partitions per
+        (sequence, KV head) with empty ones exiting at once, puts partition p
+        of KV head k on XCD (p + 3k) mod 8 for every sequence, so sequences
+        that share prefix blocks read them through one XCD's L2 (~4 % faster
+        on 256 sequences sharing a 1024-token prefix); the work list has no
+        empty workgroups, which matters when one long sequence makes the
+        dense grid mostly empty.  "auto" takes the dense grid while it has at
+        most `ratio` times the list's workgroups."""
+        if grid == "dense":
+            return True
+        if grid == "list" or num_items <= 0:
+            return False
+        return (max_parts | 1) * num_seqs <= ratio * num_items
+
     def prepare(self):
         """a1: one slot per sequence from the host allocator, staged in pinned
         memory with the lengths, copy-on-write pairs and work list.  Returns
@@ -285,8 +307,12 @@ class DecodeStep:
         if self.kernel == "partitioned":
             fn, args = self._items_call
             pa._check(fn(*args))
-            self._num_items[b] = self._nitems.value
-            n = self._offsets()[2] + 8 * self._nitems.value
+            nitems = self._nitems.value
+            if self.dense_grid(self.grid, self.max_parts, self.S, nitems, self.DENSE_RATIO):
+                nitems = 0                          # no list: the decode takes the dense grid
+            self.last_grid = "list" if nitems else "dense"
+            self._num_items[b] = nitems
+            n = self._offsets()[2] + 8 * nitems
         self._host[b].numpy()[:n] = self._stage[:n]
         return b
 
@@ -333,7 +359,11 @@ class DecodeStep:
         args = self._decode_args
         args[1] = self._check_input(q, self._q_shape, "q")
         if self.kernel == "partitioned":
-            args[self._nitems_arg] = self._nitems_dev
+            # a list with no items would mean no live partition: the dense
+            # grid is asked for with a NULL list
+            n = self._nitems_dev
+            args[self._nitems_arg - 1] = self.work_items.data_ptr() if n else None
+            args[self._nitems_arg] = n
         args[-2] = None if start_event is None else start_event.handle
         args[-1] = None if stop_event is None else stop_event.handle
         pa._check(self._decode_fn(*args))

@@ -318,15 +318,18 @@ def test_copy_on_write_blocks():
     free_gpu()
 
 
-def test_decode_steps_across_block_boundaries():
+@pytest.mark.parametrize("grid", ["dense", "list"])
+def test_decode_steps_across_block_boundaries(grid):
     """Twenty whole decode steps (a1..a6) of the engine against the oracle
     replaying the same appends: positions cross block boundaries, and the
     staging ring wraps twice (its buffers are reused only after the write
-    launch that read them has run)."""
+    launch that read them has run).  Both grids of the partitioned decode
+    (the engine asks for the dense one with a NULL work list)."""
     w = workload(3, "small")
     g = gpu_side.build(w, extra_tokens=21)
     o = oracle_side.build(w)
     step = g.step
+    step.grid = grid
     assert 20 > 2 * step.RING
     for k in range(20):
         out = step(g.q, g.k_new, g.v_new)
@@ -341,6 +344,7 @@ def test_decode_steps_across_block_boundaries():
         ref32, refT = oracle.decode(o.q, o.key_cache, o.value_cache, bt, cl, w.scale, w.dtype,
                                     nthreads=0)
         check_outputs(gpu_side.to_host16(out), ref32, refT, w.dtype, f"engine step {k}")
+        assert step.last_grid == grid
     assert np.array_equal(gpu_side.to_host16(g.cache.key_cache), o.key_cache)
     del g
     free_gpu()

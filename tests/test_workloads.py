@@ -52,3 +52,19 @@ def test_prefill_workloads_build(variant):
     keys = sum(int(n) * (int(L) - int(n)) + int(n) * (int(n) + 1) // 2
                for L, n in zip(w.lengths, w.chunks))
     assert w.flops() == 4 * w.D * w.Hq * keys
+
+
+def test_engine_grid_choice():
+    """The engine's choice between the partitioned decode's dense grid and the
+    work list (host logic; the GPU tests cover both grids)."""
+    from paged_kv_cache_106_amd.engine import DecodeStep
+    f = DecodeStep.dense_grid
+    r = DecodeStep.DENSE_RATIO
+    # Qwen-shaped layer (bench lengths): 57 partitions per sequence in the dense grid, 612 live
+    assert not f("auto", 56, 64, 612, r)
+    # long-context layer: every partition live (64 of 65)
+    assert f("auto", 65, 16, 1024, r)
+    # continuous batch: 11 partitions per sequence, 1212 live
+    assert f("auto", 11, 256, 1212, r)
+    assert not f("list", 11, 256, 1212, r) and f("dense", 56, 64, 612, r)
+    assert not f("auto", 11, 256, 0, r)
