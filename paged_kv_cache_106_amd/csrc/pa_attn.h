@@ -204,7 +204,10 @@ __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 // ... of the chunk.
 //  QK: QL lanes per token, each holding KC = D / (8 QL) 16-byte chunks of the
 //      K row (dims c*8*QL + kcol*8 .. +8): a wave load covers KTOK = 64 / QL
-//      tokens, and a log2(QL)-step DPP sum finishes each dot product.
+//      tokens.  With QL = 8 a token's lanes are one aligned 8-lane group and
+//      a 3-step DPP sum finishes each dot product; with QL = 16 they are 8
+//      lanes of an even row plus the same 8 of the next row (WaveAttn's
+//      krow / kcol), summed by 3 DPP steps and one row swap.
 //  PV: VL = D / VW lanes per token, each holding VW consecutive dims (16 or
 //      8 bytes): a wave load covers VTOK = 64 / VL tokens; each lane
 //      accumulates its VW dims for every head of the group.
@@ -564,8 +567,6 @@ struct WaveAttn {
             q + (row0 + min(hh, nact - 1)) * D + (Q8 ? kcol * T8::KB + c * 8 : c * 8 * QL + kcol * 8));
   }
 
-  // Logits of the wave's unit i (raw q.k; scaled in the softmax), written by
-  // the lane holding column 0 of each token.
   // The lane's part of the raw q.k of its token in load group j, head hh.
   __device__ __forceinline__ float qk_part(const uint4 (&qv)[GT][KC], const KBuf& kx, int j,
                                            int hh) const {
