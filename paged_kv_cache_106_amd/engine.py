@@ -116,6 +116,11 @@ class DecodeStep:
     lengths, any copy-on-write pairs and the work list in pinned memory, and
     one pa_write_step launch brings them to the device, records each new
     token's block in the tables and writes the new K/V.
+
+    ``grid`` picks the partitioned decode's grid: "list" (the work list of
+    live partitions), "dense" (every partition slot, empty ones exit at
+    once) or "auto" (see ``dense_grid``); ``last_grid`` names the one the
+    last prepared step used.
     """
 
     RING = 8            # pinned staging buffers
