@@ -396,6 +396,15 @@ def test_full_size_sampled(cfg, bs):
     torch.cuda.synchronize()
     got = gpu_side.to_host16(out)
     print(f"[{label}] GPU done", flush=True)
+    if w.spec.kernel == "partitioned":
+        # the other grid of the partitioned decode runs the same partitions
+        # through the same kernels: the outputs agree bit for bit
+        st = g.step
+        other = "list" if st.last_grid == "dense" else "dense"
+        got2 = run_partitioned(g, w, w.spec.partition_size, max_context_len=st.max_context_len,
+                               listed=other == "list", lens=st.host_context_lens)
+        assert np.array_equal(got2, got), f"{label}: the {st.last_grid} and {other} grids differ"
+        print(f"[{label}] {st.last_grid} grid == {other} grid, bit for bit", flush=True)
     o = oracle_side.build(w)
     check_state(g, o, w, label)
     del g
