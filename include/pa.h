@@ -161,7 +161,10 @@ size_t pa_decode_partitioned_workspace_size(int32_t num_seqs,
  *                     ceil(max_context_len / P) partitions of every sequence
  *                     and the ones past a sequence's end exit at once.
  *                     Pairs out of range are skipped; a missing or repeated
- *                     pair gives unspecified output for that sequence.
+ *                     pair gives unspecified output for that sequence.  A
+ *                     non-NULL list with num_work_items = 0 names no
+ *                     partition: no partition kernel runs, so pass NULL
+ *                     (not an empty list) to get the full grid.
  *   workspace         device buffer of at least
  *                     pa_decode_partitioned_workspace_size(...) bytes,
  *                     16-byte aligned; its contents on entry do not matter.
