@@ -12,7 +12,9 @@ resident in HBM before the timed region.
 Prints one JSON line on stdout.  value = algorithmic K/V bytes read by the
 timed steps' decodes / wall time of the timed steps (GB/s); the decode call
 alone is also timed with HIP events that its own launches record, on the
-step's stream, on every 5th timed step (roofline.achieved).
+step's stream: every timed step's decode up to 20 steps, then every k-th with
+at least 20 timed (roofline.achieved).  Before the warm-up, the decode of the
+prepared state runs back to back for --settle-ms so the clocks have settled.
 """
 import argparse
 import gc
@@ -29,29 +31,40 @@ if ROOT not in sys.path:
 
 METRIC = "paged decode attention KV-read GB/s (% of HBM peak); seqs/s per layer"
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, AMD's published figure
-TIME_EVERY = 5          # the decode of every 5th timed step is timed with HIP events
+MIN_TIMED_DECODES = 20  # decodes timed with HIP events: every step up to this many steps,
+                        # then every k-th step with at least this many timed
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def cpu_baseline(w, budget_s, int8=False):
-    """The oracle as it stands, timed on the host cores over whole sequences of
-    the same workload (in a seeded order, cycling) until about budget_s
-    seconds of work."""
-    import oracle
-    from tests import oracle_side
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
-    o = oracle_side.build_int8(w) if int8 else oracle_side.build(w)
-    threads = len(os.sched_getaffinity(0))
+
+def _oracle_rate(o, w, budget_s, threads, int8):
+    """Oracle decodes of whole sequences (all q heads; a seeded order, cycling)
+    on `threads` host threads until about budget_s seconds of work: (bytes/s,
+    sequences/s, sequences, tokens, seconds)."""
+    import oracle
+
     per_tok = 2 * w.Hkv * (w.D + 4) if int8 else 2 * w.Hkv * w.D * w.elem_bytes
     spent, done_bytes, nseq, ntok = 0.0, 0, 0, 0
     order = np.random.default_rng(1234).permutation(w.S)
     k = 0
+    batch_n = 4 if threads > 1 else 1
     while spent < budget_s:
-        batch = [int(order[(k + j) % w.S]) for j in range(4)]
-        k += 4
+        batch = [int(order[(k + j) % w.S]) for j in range(batch_n)]
+        k += batch_n
         pairs = np.array([[i, h] for i in batch for h in range(w.Hq)], np.int32)
         t0 = time.perf_counter()
         if int8:
@@ -66,16 +79,34 @@ def cpu_baseline(w, budget_s, int8=False):
         done_bytes += toks * per_tok
         ntok += toks
         nseq += len(batch)
+    return done_bytes / spent, nseq / spent, nseq, ntok, spent
+
+
+def cpu_baseline(w, budget_s, int8=False):
+    """The oracle as it stands, timed on the host cores over whole sequences of
+    the same workload: on every core the process may use (about budget_s
+    seconds of work), then on one thread (about half that)."""
+    from tests import oracle_side
+
+    o = oracle_side.build_int8(w) if int8 else oracle_side.build(w)
+    threads = len(os.sched_getaffinity(0))
+    bps, sps, nseq, ntok, spent = _oracle_rate(o, w, budget_s, threads, int8)
+    bps1, sps1, nseq1, ntok1, spent1 = _oracle_rate(o, w, budget_s / 2, 1, int8)
+    what = "stored K/V bytes (codes + scales)" if int8 else "logical K/V bytes"
     return {
-        "value": done_bytes / spent / 1e9,
+        "value": bps / 1e9,
         "unit": "GB/s",
         "cores": threads,
         "kind": "oracle",
         "sample": (f"{nseq} sequence decodes drawn cyclically from the workload's {w.S} "
-                   f"(all {w.Hq} q heads each, {ntok} tokens), {spent:.1f} s of oracle time; "
-                   + ("stored K/V bytes (codes + scales)" if int8 else "logical K/V bytes")
-                   + " of the sample / oracle decode time"),
-        "seqs_per_s": nseq / spent,
+                   f"(all {w.Hq} q heads each, {ntok} tokens) on {threads} threads, "
+                   f"{spent:.1f} s of oracle time; {what} of the sample / oracle decode time"),
+        "seqs_per_s": sps,
+        "single_thread": {
+            "value": bps1 / 1e9, "unit": "GB/s", "cores": 1, "seqs_per_s": sps1,
+            "sample": f"{nseq1} sequence decodes ({ntok1} tokens), {spent1:.1f} s on one thread"},
+        "cpu_model": cpu_model(),
+        "nproc": os.cpu_count(),
     }
 
 
@@ -237,6 +268,10 @@ def main():
     ap.add_argument("--prefill", action="store_true",
                     help="time the chunked-prefill attention (pa_prefill) instead of a decode step")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="before the warm-up, decode calls back to back (the same inputs, "
+                         "no step state changes) for this long, so the GPU clocks have "
+                         "settled when the steps start")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--gc", dest="no_gc", action="store_false",
                     help="keep Python's garbage collector on during the timed steps")
@@ -295,10 +330,12 @@ def main():
     # HIP events recorded by the decode's launches themselves (hipExtLaunchKernel):
     # start of its first kernel, end of its last, on the step's stream, with no
     # marker packet in the stream (a marker costs a few microseconds of GPU time)
-    # (each event still costs the stream a few microseconds, so only every
-    # TIME_EVERY-th step's decode is timed)
+    # (each event still costs the stream a few microseconds: every step's decode
+    # is timed up to MIN_TIMED_DECODES steps, then every k-th with at least
+    # MIN_TIMED_DECODES of them)
     from paged_kv_cache_106_amd._hip import Event
-    ev = {k: (Event(timing=True), Event(timing=True)) for k in range(0, args.steps, TIME_EVERY)}
+    time_every = max(1, args.steps // MIN_TIMED_DECODES)
+    ev = {k: (Event(timing=True), Event(timing=True)) for k in range(0, args.steps, time_every)}
     kv_bytes, len_sum = 0, 0.0
     host = np.zeros((args.steps, 4))                            # host seconds per phase
     # the collector is run and paused before the warm-up, so nothing but the
@@ -308,6 +345,15 @@ def main():
     gc_was_enabled = gc.isenabled()
     if args.no_gc:
         gc.disable()       # a collection pass over this large heap stalls the host for ~30 ms
+    settle_calls = 0
+    if args.settle_ms > 0:
+        # the decode of the current state, repeated: no token is appended
+        t_settle = time.perf_counter()
+        while (time.perf_counter() - t_settle) * 1e3 < args.settle_ms:
+            for _ in range(10):
+                step.attend(g.q)
+            settle_calls += 10
+            torch.cuda.synchronize()
     for _ in range(args.warmup):
         step(g.q, g.k_new, g.v_new)
     torch.cuda.synchronize()
@@ -375,6 +421,8 @@ def main():
         "decode_us": round(dec_avg * 1e6, 2),
         "decode_us_p50": round(float(np.median(t_decode)) * 1e6, 2),
         "decode_timed_steps": len(t_decode),
+        "decode_timed_every": time_every,
+        "clock_settle_decodes": settle_calls,
         "decode_us_p10_p90": [round(float(np.percentile(t_decode, 10)) * 1e6, 2),
                               round(float(np.percentile(t_decode, 90)) * 1e6, 2)],
         "decode_seqs_per_s": round(w.S / dec_avg, 1),

@@ -162,9 +162,9 @@ size_t pa_decode_partitioned_workspace_size(int32_t num_seqs,
  *                     and the ones past a sequence's end exit at once.
  *                     Pairs out of range are skipped; a missing or repeated
  *                     pair gives unspecified output for that sequence.  A
- *                     non-NULL list with num_work_items = 0 names no
- *                     partition: no partition kernel runs, so pass NULL
- *                     (not an empty list) to get the full grid.
+ *                     non-NULL list with num_work_items = 0 (and
+ *                     num_seqs > 0) is rejected with PA_ERR_INVALID_ARG:
+ *                     pass NULL for the full grid.
  *   workspace         device buffer of at least
  *                     pa_decode_partitioned_workspace_size(...) bytes,
  *                     16-byte aligned; its contents on entry do not matter.
@@ -290,12 +290,15 @@ pa_status pa_copy_blocks(void* key_cache, void* value_cache,
  *                  the sequences' work is dispatched (a permutation of
  *                  0..num_seqs-1; longest context first balances the launch;
  *                  entries outside [0, num_seqs) are skipped)
- *   max_query_len  >= every n_i (sizes the grid; longer chunks are cut)
+ *   max_query_len  >= every n_i (sizes the grid); a longer chunk is cut:
+ *                  its first max_query_len rows are computed at their true
+ *                  positions, the rest are left unwritten
  * Other arguments as for pa_decode.  Products run on the matrix cores with
  * fp32 accumulation; the softmax weights enter the P.V product as a 16-bit
  * part plus a 16-bit remainder (about 17 significant bits).  A chunk longer
- * than its context, or rows outside [0, num_query_tokens), are skipped on
- * the device (their outputs are left unwritten).
+ * than its context (n_i > context_lens[i]), or one whose rows fall outside
+ * [0, num_query_tokens), is skipped whole on the device (its outputs are
+ * left unwritten).
  * ---------------------------------------------------------------------- */
 pa_status pa_prefill(void* out, const void* query, const void* key_cache,
                      const void* value_cache, const int32_t* block_tables,

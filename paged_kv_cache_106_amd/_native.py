@@ -228,6 +228,19 @@ def pa_decode(out, query, key_cache, value_cache, block_tables, context_lens, ma
     _check(_lib.pa_decode(*args, _stream(stream), _event(start_event), _event(stop_event)))
 
 
+def _work_list(work_items):
+    """(pointer, count) of an optional [n][2] int32 work list.  An empty list
+    would name no partition (the C call rejects it): None asks for the full
+    grid."""
+    if work_items is None:
+        return None, 0
+    if work_items.dim() != 2 or work_items.shape[1] != 2:
+        raise ValueError("work_items must be [n][2]")
+    if work_items.shape[0] == 0:
+        raise ValueError("an empty work list names no partition: pass None for the full grid")
+    return _dptr(work_items, "work_items", 4), work_items.shape[0]
+
+
 def pa_decode_partitioned_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len,
                                          partition_size):
     return int(_lib.pa_decode_partitioned_workspace_size(num_seqs, num_q_heads, head_dim,
@@ -240,14 +253,9 @@ def pa_decode_partitioned(out, query, key_cache, value_cache, block_tables, cont
     """Split-context paged decode + merge; workspace is a uint8 GPU tensor;
     work_items an optional int32 GPU tensor [n][2] of (sequence, partition);
     start/stop events as for pa_decode."""
+    wi, nwi = _work_list(work_items)
     args = _decode_args(out, query, key_cache, value_cache, block_tables, context_lens,
                         max_context_len, scale, dtype)
-    if work_items is None:
-        wi, nwi = None, 0
-    else:
-        if work_items.dim() != 2 or work_items.shape[1] != 2:
-            raise ValueError("work_items must be [n][2]")
-        wi, nwi = (_dptr(work_items, "work_items", 4) if work_items.shape[0] else None), work_items.shape[0]
     _check(_lib.pa_decode_partitioned(*args, int(partition_size), wi, int(nwi),
                                       _dptr(workspace, "workspace"),
                                       workspace.numel() * workspace.element_size(),
@@ -343,14 +351,9 @@ def pa_decode_partitioned_int8(out, query, key_cache, value_cache, key_scale, va
                                start_event=None, stop_event=None):
     """Split-context paged decode + merge over INT8 pools (workspace as for
     pa_decode_partitioned)."""
+    wi, nwi = _work_list(work_items)
     args = _decode_int8_args(out, query, key_cache, value_cache, key_scale, value_scale,
                              block_tables, context_lens, max_context_len, scale, dtype)
-    if work_items is None:
-        wi, nwi = None, 0
-    else:
-        if work_items.dim() != 2 or work_items.shape[1] != 2:
-            raise ValueError("work_items must be [n][2]")
-        wi, nwi = (_dptr(work_items, "work_items", 4) if work_items.shape[0] else None), work_items.shape[0]
     _check(_lib.pa_decode_partitioned_int8(*args, int(partition_size), wi, int(nwi),
                                            _dptr(workspace, "workspace"),
                                            workspace.numel() * workspace.element_size(),

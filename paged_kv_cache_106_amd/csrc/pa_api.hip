@@ -385,6 +385,11 @@ pa_status partitioned(AttnParams& p, bool q8, pa_dtype dtype, int32_t head_dim,
   if (num_work_items < 0 || (num_work_items > 0 && !work_items) ||
       (work_items && !pa::aligned(work_items, 4)))
     return fail(PA_ERR_INVALID_ARG, "work_items must be NULL or a 4-byte aligned device array");
+  // a list names every partition to compute; an empty one would leave every
+  // sequence's partials unwritten before the merge reads them
+  if (work_items && num_work_items == 0 && num_seqs > 0)
+    return fail(PA_ERR_INVALID_ARG,
+                "an empty work list names no partition: pass NULL for the full grid");
   if ((static_cast<int64_t>(num_work_items) + 7) * p.num_kv_heads * p.head_chunks > INT32_MAX)
     return fail(PA_ERR_UNSUPPORTED, "num_work_items * num_kv_heads * head chunks overflows int32");
   if (num_seqs == 0) return pa::mark_events(start_event, stop_event, stream, what);
@@ -404,7 +409,7 @@ pa_status partitioned(AttnParams& p, bool q8, pa_dtype dtype, int32_t head_dim,
   p.work_items = num_work_items > 0 ? work_items : nullptr;
   p.num_work_items = num_work_items;
   auto launch = pa::attn_launcher(dtype, head_dim, q8);
-  const bool any = work_items ? num_work_items > 0 : parts > 0;
+  const bool any = work_items ? true : parts > 0;
   if (any) {
     const bool mfma = q8 && p.group >= pa::kQ8MfmaMinGroup;
     const pa_status s1 = pa::launched(

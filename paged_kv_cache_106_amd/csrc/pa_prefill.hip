@@ -116,13 +116,19 @@ __global__ __launch_bounds__(kThreadsP, 4) void prefill_kernel(PrefillParams p) 
   const int q0 = p.query_start[seq];
   int L_ctx = p.context_lens[seq];
   L_ctx = max(0, min(L_ctx, p.mb * p.block_size));
-  int n = p.query_start[seq + 1] - q0;
-  n = max(0, min(n, min(L_ctx, p.max_query_len)));
-  if (q0 < 0 || q0 + n > p.num_tokens) n = 0;
+  // the chunk's tokens are the last n_all of the context; a chunk longer than
+  // its context, or one whose rows leave [0, num_tokens), is skipped whole; a
+  // chunk longer than max_query_len keeps its positions and loses its rows
+  // past that count
+  const int64_t n_all64 = static_cast<int64_t>(p.query_start[seq + 1]) - q0;
+  const bool chunk_ok = q0 >= 0 && n_all64 >= 0 && n_all64 <= L_ctx &&
+                        static_cast<int64_t>(q0) + n_all64 <= p.num_tokens;
+  const int n_all = chunk_ok ? static_cast<int>(n_all64) : 0;
+  const int n = min(n_all, p.max_query_len);
   const int nrows = n * G;
   const int r0 = tile * kRowsP;
   if (r0 >= nrows) return;                            // uniform: whole workgroup
-  const int base_pos = L_ctx - n;                     // position of query token 0
+  const int base_pos = L_ctx - n_all;                 // position of query token 0
   const int last_row = min(r0 + kRowsP, nrows) - 1;
   const int kend = base_pos + last_row / G + 1;       // keys this workgroup needs
 

@@ -250,3 +250,21 @@ def test_prefill_rejects_on_host():
         assert f(*bad, None, None, None) == status
     empty = list(ok); empty[10] = 0                                     # no query tokens
     assert f(*empty, None, None, None) == _native.PA_OK
+
+
+def test_partitioned_rejects_an_empty_work_list():
+    """A non-NULL list with no items names no partition: the C call refuses it
+    (the merge would read partials nobody wrote) and the binding refuses an
+    empty tensor before calling; NULL still means the full grid."""
+    assert decode_part(items=BAD, nitems=0) == _native.PA_ERR_INVALID_ARG
+    assert "pass NULL" in L.pa_last_error().decode()
+    # with no sequences there is nothing to name: a no-op
+    assert decode_part(items=BAD, nitems=0, S=0) == _native.PA_OK
+    import torch
+    empty = torch.empty((0, 2), dtype=torch.int32)
+    with pytest.raises(ValueError, match="pass None"):
+        pa.pa_decode_partitioned(None, None, None, None, None, None, 64, 0.1, "bf16", 512,
+                                 None, work_items=empty)
+    with pytest.raises(ValueError, match="pass None"):
+        pa.pa_decode_partitioned_int8(None, None, None, None, None, None, None, None, 64, 0.1,
+                                      "bf16", 512, None, work_items=empty)

@@ -8,6 +8,7 @@ place of the 16-bit format (plus 1e-4 of fp32 summation noise) of it.
 """
 import gc
 import math
+import os
 
 import numpy as np
 import pytest
@@ -38,6 +39,8 @@ def half_ulp(x, dtype):
 
 
 FP32_NOISE = 1e-4   # allowance for fp32 summation-order differences (outputs are O(1))
+# host threads for the oracle's full-size decodes (the GPU machine's CPU share is 16)
+ORACLE_THREADS = min(16, len(os.sched_getaffinity(0)))
 
 
 def check_outputs(got_bits, ref32, ref_bits, dtype, label):
@@ -118,7 +121,7 @@ def test_small_workloads(cfg, bs):
     o = oracle_side.build(w)
     check_state(g, o, w, label)
     ref32, refT = oracle.decode(o.q, o.key_cache, o.value_cache, o.block_tables, o.context_lens,
-                                w.scale, w.dtype, nthreads=0)
+                                w.scale, w.dtype, nthreads=ORACLE_THREADS)
     check_outputs(run_single(g, w), ref32, refT, w.dtype, label + " single")
     for P in sorted({w.bs, 3 * w.bs, 512}):
         check_outputs(run_partitioned(g, w, P), ref32, refT, w.dtype, label + f" P={P}")
@@ -160,7 +163,7 @@ def test_edge_lengths(Hq, Hkv, D, bs, dtype):
     o = oracle_side.build(w)
     check_state(g, o, w, label)
     ref32, refT = oracle.decode(o.q, o.key_cache, o.value_cache, o.block_tables, o.context_lens,
-                                w.scale, w.dtype, nthreads=0)
+                                w.scale, w.dtype, nthreads=ORACLE_THREADS)
     check_outputs(run_single(g, w), ref32, refT, dtype, label + " single")
     for PP in (bs, P, 1024):
         check_outputs(run_partitioned(g, w, PP), ref32, refT, dtype, label + f" P={PP}")
@@ -175,7 +178,7 @@ def test_zero_length_and_empty_batch():
     g = gpu_side.build(w)
     o = oracle_side.build(w)
     ref32, refT = oracle.decode(o.q, o.key_cache, o.value_cache, o.block_tables, o.context_lens,
-                                w.scale, w.dtype, nthreads=0)
+                                w.scale, w.dtype, nthreads=ORACLE_THREADS)
     # sequence 2 reports no tokens: its rows become zeros, the others are unchanged
     g.step.context_lens[2] = 0
     torch.cuda.synchronize()
@@ -342,7 +345,7 @@ def test_decode_steps_across_block_boundaries(grid):
         assert np.array_equal(step.block_tables.cpu().numpy(), bt)
         assert np.array_equal(step.context_lens.cpu().numpy(), cl)
         ref32, refT = oracle.decode(o.q, o.key_cache, o.value_cache, bt, cl, w.scale, w.dtype,
-                                    nthreads=0)
+                                    nthreads=ORACLE_THREADS)
         check_outputs(gpu_side.to_host16(out), ref32, refT, w.dtype, f"engine step {k}")
         assert step.last_grid == grid
     assert np.array_equal(gpu_side.to_host16(g.cache.key_cache), o.key_cache)
@@ -372,14 +375,14 @@ def test_engine_steps_back_to_back():
     assert np.array_equal(gpu_side.to_host16(g.cache.key_cache), o.key_cache)
     assert np.array_equal(gpu_side.to_host16(g.cache.value_cache), o.value_cache)
     ref32, refT = oracle.decode(o.q, o.key_cache, o.value_cache, bt, cl, w.scale, w.dtype,
-                                nthreads=0)
+                                nthreads=ORACLE_THREADS)
     check_outputs(gpu_side.to_host16(out), ref32, refT, w.dtype, "engine, 20 steps back to back")
     del g
     free_gpu()
 
 
 # ---------------------------------------------------------------------------
-# full-size workloads in the benchmark's launch configuration: sampled outputs
+# full-size workloads in the benchmark's launch configuration: every output
 # ---------------------------------------------------------------------------
 
 FULL = [(2, None), (3, None), (4, None), (5, 16), (5, 32)]
@@ -387,7 +390,7 @@ FULL = [(2, None), (3, None), (4, None), (5, 16), (5, 32)]
 
 @pytest.mark.timeout(600)
 @pytest.mark.parametrize("cfg,bs", FULL, ids=[f"cfg{c}-bs{b or 16}" for c, b in FULL])
-def test_full_size_sampled(cfg, bs):
+def test_full_size_every_output(cfg, bs):
     w = workload(cfg, "full", **({"block_size": bs} if bs else {}))
     label = f"cfg{cfg} full bs{w.bs}"
     print(f"\n[{label}] S={w.S} KV bytes={w.kv_bytes()} blocks={w.num_blocks}", flush=True)
@@ -409,19 +412,9 @@ def test_full_size_sampled(cfg, bs):
     check_state(g, o, w, label)
     del g
     free_gpu()
-    rng = np.random.default_rng(cfg)
-    order = np.argsort(w.lengths)
-    seqs = sorted(set([int(order[0]), int(order[-1]), int(order[len(order) // 2])] +
-                      [int(x) for x in rng.choice(w.S, min(5, w.S), replace=False)]))
-    pairs = np.array([[i, h] for i in seqs for h in rng.choice(w.Hq, 3, replace=False)], np.int32)
-    ref32, refT = oracle.decode_pairs(o.q, o.key_cache, o.value_cache, o.block_tables,
-                                      o.context_lens, w.scale, w.dtype, pairs, nthreads=0)
-    sub = np.stack([got[i, h] for i, h in pairs])
-    check_outputs(sub, ref32, refT, w.dtype, label + " sampled")
-    # properties at any size: every output finite and within the range of V
-    allv = oracle.widen(got, w.dtype)
-    assert np.isfinite(allv).all()
-    assert np.abs(allv).max() <= 8.0          # convex combinations of N(0,1) samples
+    ref32, refT = oracle.decode(o.q, o.key_cache, o.value_cache, o.block_tables, o.context_lens,
+                                w.scale, w.dtype, nthreads=ORACLE_THREADS)
+    check_outputs(got, ref32, refT, w.dtype, label + f" all {got.shape[0] * got.shape[1]} outputs")
 
 
 def test_engine_step_with_copy_on_write():

@@ -15,7 +15,7 @@ import oracle
 import paged_kv_cache_106_amd as pa
 from oracle.allocator_model import BlockManagerModel
 from workloads import POISON, prefill_workload
-from tests.test_gpu_parity import check_outputs, free_gpu
+from tests.test_gpu_parity import ORACLE_THREADS, check_outputs, free_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -95,7 +95,7 @@ def test_prefill_small(over):
     assert np.array_equal(vc.cpu().numpy().view(np.uint16), ovc)
     got = run_gpu(w, kc, vc, bt, lens, qs)
     ref32, refT = oracle.prefill(w.query(), okc, ovc, obt, w.lengths, w.query_start, w.scale,
-                                 w.dtype, nthreads=0)
+                                 w.dtype, nthreads=ORACLE_THREADS)
     check_outputs(got, ref32, refT, w.dtype, label)
     # a grid sized for longer chunks, or another dispatch order, changes nothing
     got2 = run_gpu(w, kc, vc, bt, lens, qs, max_query_len=int(w.chunks.max()) + 200)
@@ -120,14 +120,45 @@ def test_prefill_empty_and_rejects():
         pa.pa_prefill(out, q, kc, vc, bt, lens, qs[:-1], 4, w.scale, w.dtype)
 
 
+def test_prefill_cut_and_overlong_chunks():
+    """A chunk cut by max_query_len keeps its true positions: its first
+    max_query_len rows equal the oracle's, the rest stay unwritten.  A chunk
+    longer than its context is skipped whole (its rows stay unwritten) and
+    leaves the other sequences' rows unchanged."""
+    w = prefill_workload("small")              # chunks (1, 17, 37, 512, 1, 32)
+    kc, vc, bt, lens, qs, _ = build_gpu(w)
+    okc, ovc, obt = build_oracle(w)
+    ref32, refT = oracle.prefill(w.query(), okc, ovc, obt, w.lengths, w.query_start, w.scale,
+                                 w.dtype, nthreads=ORACLE_THREADS)
+    cut = 20
+    got = run_gpu(w, kc, vc, bt, lens, qs, max_query_len=cut)
+    keep = np.concatenate([np.arange(w.query_start[i], w.query_start[i] + min(int(w.chunks[i]), cut))
+                           for i in range(w.S)])
+    dropped = np.setdiff1d(np.arange(w.T), keep)
+    assert dropped.size > 0
+    check_outputs(got[keep], ref32[keep], refT[keep], w.dtype, "prefill cut at 20 rows")
+    assert (got[dropped] == 0x7FFF).all(), "rows past max_query_len were written"
+    # sequence 2 reports fewer cached tokens than its chunk holds: skipped
+    short = w.lengths.copy()
+    short[2] = int(w.chunks[2]) - 1
+    got2 = run_gpu(w, kc, vc, bt, dev(short), qs)
+    rows2 = np.arange(w.query_start[2], w.query_start[3])
+    others = np.setdiff1d(np.arange(w.T), rows2)
+    assert (got2[rows2] == 0x7FFF).all(), "an over-long chunk was computed"
+    check_outputs(got2[others], ref32[others], refT[others], w.dtype, "prefill, one chunk skipped")
+    del kc, vc
+    free_gpu()
+
+
 @pytest.mark.timeout(600)
-def test_prefill_full_size_sampled():
+def test_prefill_full_size_whole_chunks():
     """The benchmark's chunked-prefill step (8 x 512-token chunks after up to
-    8192 cached tokens, Qwen2.5-7B-shaped), sampled rows against the oracle:
-    the expected value of a row at position p is the oracle's decode with
-    context length p + 1 over the same table row."""
+    8192 cached tokens, Qwen2.5-7B-shaped) in its launch configuration: every
+    row and head of three whole chunks (the two with the fewest cached tokens
+    and the one with the most) against the oracle's prefill over the same
+    tables, the other chunks given no rows on the oracle's side."""
     w = prefill_workload("full")
-    label = "prefill full sampled"
+    label = "prefill full"
     kc, vc, bt, lens, qs, bt_host = build_gpu(w)
     got = run_gpu(w, kc, vc, bt, lens, qs, order=longest_first(w))
     print(f"\n[{label}] GPU done", flush=True)
@@ -136,17 +167,13 @@ def test_prefill_full_size_sampled():
     assert np.array_equal(bt_host, obt)
     del kc, vc
     free_gpu()
-    rng = np.random.default_rng(5)
+    order = np.argsort(w.lengths, kind="stable")
+    pick = sorted({int(order[0]), int(order[1]), int(order[-1])})
+    n = np.where(np.isin(np.arange(w.S), pick), w.chunks, 0).astype(np.int32)
+    qs_sub = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+    rows = np.concatenate([np.arange(w.query_start[i], w.query_start[i + 1]) for i in pick])
     q = w.query()
-    rows = []
-    for i in range(w.S):
-        n = int(w.chunks[i])
-        rows += [(i, 0), (i, n - 1)] + [(i, int(k)) for k in rng.integers(0, n, 2)]
-    heads = rng.integers(0, w.Hq, len(rows))
-    qd = np.stack([q[w.query_start[i] + k] for i, k in rows])             # [R][Hq][D]
-    cl = np.array([int(w.lengths[i]) - int(w.chunks[i]) + k + 1 for i, k in rows], np.int32)
-    tbl = np.stack([obt[i] for i, _ in rows])
-    pairs = np.array([[r, h] for r, h in enumerate(heads)], np.int32)
-    ref32, refT = oracle.decode_pairs(qd, okc, ovc, tbl, cl, w.scale, w.dtype, pairs, nthreads=0)
-    sub = np.stack([got[w.query_start[i] + k, h] for (i, k), h in zip(rows, heads)])
-    check_outputs(sub, ref32, refT, w.dtype, label)
+    ref32, refT = oracle.prefill(np.ascontiguousarray(q[rows]), okc, ovc, obt, w.lengths, qs_sub,
+                                 w.scale, w.dtype, nthreads=ORACLE_THREADS)
+    check_outputs(got[rows], ref32, refT, w.dtype,
+                  label + f" chunks {pick}: all {rows.size * w.Hq} rows x heads")

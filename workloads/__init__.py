@@ -372,3 +372,49 @@ def prefill_workload(variant: str = "small", **overrides) -> PrefillWorkload:
     qs = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
     return PrefillWorkload(spec=s, lengths=L, chunks=n, query_start=qs, num_blocks=nb,
                            initial_free_order=perm)
+
+
+# -- prompts for the prefix cache -------------------------------------------------------
+# A token's K/V depends on every token before it in a real model, so the rows
+# drawn here for position j of a prompt come from a generator seeded by a
+# digest of the prompt's tokens 0..j: two prompts get bit-identical rows
+# exactly where they share a prefix, and different rows after the first token
+# where they differ.  (Input preparation only; the digest is blake2b.)
+
+STREAM_PC_K = 30
+STREAM_PC_V = 31
+STREAM_PC_Q = 32
+STREAM_PC_TOKENS = 33
+
+
+def prompt_tokens(seed: int, index: int, n: int, vocab: int = 32000) -> np.ndarray:
+    """n seeded token ids in [0, vocab) (int32)."""
+    return _rng(seed, STREAM_PC_TOKENS, index).integers(0, vocab, n).astype(np.int32)
+
+
+def prefix_keyed_kv(seed: int, tokens, num_kv_heads: int, head_dim: int, dtype: str):
+    """(keys, values), each [n][num_kv_heads][head_dim] 16-bit patterns, row j
+    drawn from N(0,1) with a generator keyed by (seed, digest of tokens[:j+1])."""
+    import hashlib
+    toks = np.ascontiguousarray(tokens, dtype=np.int32).reshape(-1)
+    n = toks.shape[0]
+    k = np.empty((n, num_kv_heads, head_dim), np.float32)
+    v = np.empty_like(k)
+    h = hashlib.blake2b(digest_size=16)
+    for j in range(n):
+        h.update(toks[j:j + 1].tobytes())
+        d = np.frombuffer(h.digest(), np.uint32)
+        key = [seed] + [int(x) for x in d]
+        k[j] = np.random.default_rng([STREAM_PC_K] + key).standard_normal(
+            (num_kv_heads, head_dim), dtype=np.float32)
+        v[j] = np.random.default_rng([STREAM_PC_V] + key).standard_normal(
+            (num_kv_heads, head_dim), dtype=np.float32)
+    return to_bits(k, dtype), to_bits(v, dtype)
+
+
+def prompt_queries(seed: int, num_seqs: int, num_q_heads: int, head_dim: int,
+                   dtype: str) -> np.ndarray:
+    """[num_seqs][num_q_heads][head_dim] N(0,1) queries, 16-bit patterns."""
+    x = _rng(seed, STREAM_PC_Q).standard_normal((num_seqs, num_q_heads, head_dim),
+                                                dtype=np.float32)
+    return to_bits(x, dtype)
