@@ -194,6 +194,48 @@ pa_status pa_decode_partitioned(void* out, const void* query,
                                 hipEvent_t start_event, hipEvent_t stop_event);
 
 /* ------------------------------------------------------------------------
+ * pa_decode_partitioned without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  It computes exactly what
+ * pa_decode_partitioned computes, with the same kernels; the split
+ * workspace is a file-scope device array inside libpa of
+ * pa_decode_partitioned_noalloc_max_workspace() bytes (64 MiB), one copy per
+ * GPU, created when libpa's code is loaded on that GPU and held until the
+ * process ends.  The call allocates nothing (no hipMalloc, no hipFree).
+ *   Arguments as pa_decode_partitioned, without workspace / workspace_bytes.
+ *   A call whose workspace (pa_decode_partitioned_workspace_size of the same
+ *   sizes) exceeds the array is rejected with PA_ERR_INVALID_ARG before
+ *   anything is enqueued.
+ *   The array of the CURRENT device is used; a non-NULL stream must belong
+ *   to it (PA_ERR_INVALID_ARG otherwise).  The first call on a device looks
+ *   the array's address up (hipGetSymbolAddress, with that device current);
+ *   a failure there returns PA_ERR_HIP.
+ * Every call on one GPU shares that GPU's array and leaves its partials in
+ * it: calls that overlap on one GPU (other streams, other threads) race and
+ * give unspecified outputs; calls ordered on one stream are safe.  Nothing
+ * in the array needs to start at zero (the merge reads only partials the
+ * same call wrote).
+ * ---------------------------------------------------------------------- */
+size_t pa_decode_partitioned_noalloc_max_workspace(void);
+
+pa_status pa_decode_partitioned_noalloc(void* out, const void* query,
+                                        const void* key_cache,
+                                        const void* value_cache,
+                                        const int32_t* block_tables,
+                                        int32_t max_blocks_per_seq,
+                                        const int32_t* context_lens,
+                                        int32_t num_seqs, int32_t num_q_heads,
+                                        int32_t num_kv_heads, int32_t head_dim,
+                                        int32_t block_size, int32_t num_blocks,
+                                        int32_t max_context_len, float scale,
+                                        pa_dtype dtype, int32_t partition_size,
+                                        const int32_t* work_items,
+                                        int32_t num_work_items,
+                                        hipStream_t stream,
+                                        hipEvent_t start_event,
+                                        hipEvent_t stop_event);
+
+/* ------------------------------------------------------------------------
  * Decode-step update of device-resident block tables.
  * Follows: append_slot puts the new token into the sequence's current block
  * or a fresh one ("vLLM 深度拆解：当大模型推理学会「分页注意力」", §3.3), and

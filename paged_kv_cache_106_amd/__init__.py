@@ -20,6 +20,8 @@ from ._native import (  # noqa: F401
     pa_decode_int8,
     pa_decode_partitioned,
     pa_decode_partitioned_int8,
+    pa_decode_partitioned_noalloc,
+    pa_decode_partitioned_noalloc_max_workspace,
     pa_decode_partitioned_workspace_size,
     pa_prefill,
     pa_reshape_and_cache,
@@ -33,7 +35,9 @@ from ._native import (  # noqa: F401
 __all__ = [
     "Allocator", "PaError", "PaOOM", "PA_F16", "PA_BF16", "lib", "pa_copy_blocks",
     "pa_copy_blocks_int8", "pa_decode", "pa_decode_int8", "pa_decode_partitioned",
-    "pa_decode_partitioned_int8", "pa_decode_partitioned_workspace_size", "pa_prefill",
+    "pa_decode_partitioned_int8", "pa_decode_partitioned_noalloc",
+    "pa_decode_partitioned_noalloc_max_workspace", "pa_decode_partitioned_workspace_size",
+    "pa_prefill",
     "pa_reshape_and_cache",
     "pa_reshape_and_cache_int8", "pa_update_block_tables", "pa_write_step",
     "pa_write_step_int8", "partition_work_items",

@@ -61,6 +61,8 @@ _DEC = [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32, 
 _sig("pa_decode", _i32, _DEC + [_vp, _vp, _vp])
 _sig("pa_decode_partitioned_workspace_size", _sz, [_i32, _i32, _i32, _i32, _i32])
 _sig("pa_decode_partitioned", _i32, _DEC + [_i32, _vp, _i32, _vp, _sz, _vp, _vp, _vp])
+_sig("pa_decode_partitioned_noalloc", _i32, _DEC + [_i32, _vp, _i32, _vp, _vp, _vp])
+_sig("pa_decode_partitioned_noalloc_max_workspace", _sz, [])
 _sig("pa_copy_blocks", _i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp])
 _sig("pa_reshape_and_cache_int8", _i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                          _i32, _i32, _vp])
@@ -260,6 +262,25 @@ def pa_decode_partitioned(out, query, key_cache, value_cache, block_tables, cont
                                       _dptr(workspace, "workspace"),
                                       workspace.numel() * workspace.element_size(),
                                       _stream(stream), _event(start_event), _event(stop_event)))
+
+
+def pa_decode_partitioned_noalloc(out, query, key_cache, value_cache, block_tables,
+                                  context_lens, max_context_len, scale, dtype, partition_size,
+                                  work_items=None, stream=None, start_event=None,
+                                  stop_event=None):
+    """pa_decode_partitioned with its split workspace in libpa's per-GPU
+    scratch array (no allocation by the call; workspaces above
+    pa_decode_partitioned_noalloc_max_workspace() bytes are refused)."""
+    wi, nwi = _work_list(work_items)
+    args = _decode_args(out, query, key_cache, value_cache, block_tables, context_lens,
+                        max_context_len, scale, dtype)
+    _check(_lib.pa_decode_partitioned_noalloc(*args, int(partition_size), wi, int(nwi),
+                                              _stream(stream), _event(start_event),
+                                              _event(stop_event)))
+
+
+def pa_decode_partitioned_noalloc_max_workspace():
+    return int(_lib.pa_decode_partitioned_noalloc_max_workspace())
 
 
 # -- INT8 pools: codes int8 [NB][bs][Hkv][D], scales float32 [NB][Hkv][bs] ---------------

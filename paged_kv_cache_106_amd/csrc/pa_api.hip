@@ -5,6 +5,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 #include <string>
 
 #include "pa.h"
@@ -366,6 +367,94 @@ pa_status pa_decode_partitioned_int8(
   return pa::partitioned(p, true, dtype, head_dim, block_size, max_context_len, partition_size,
                          work_items, num_work_items, workspace, workspace_bytes, stream,
                          start_event, stop_event, "pa_decode_partitioned_int8");
+}
+
+}  // extern "C"
+
+// ---- the split-context decode with no allocation anywhere ------------------
+// Its workspace is this file-scope array: one copy per GPU, created when the
+// code object is loaded on that GPU and held until the process ends.  In
+// host code `scratch` names a host-side stand-in; the array's device address
+// comes from hipGetSymbolAddress, once per device, with that device current.
+namespace {
+constexpr size_t kScratchBytes = size_t(64) << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) char scratch[kScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch array's device address on the current device; NULL with the
+// error set when it cannot be found.
+void* scratch_of_current_device(const char* what) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    pa::g_last_error = std::string(what) + ": no usable current device";
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      (void)hipGetLastError();
+      pa::g_last_error = std::string(what) + ": hipGetSymbolAddress(scratch) failed: " +
+                         hipGetErrorString(e);
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+}  // namespace
+
+extern "C" {
+
+size_t pa_decode_partitioned_noalloc_max_workspace(void) { return kScratchBytes; }
+
+pa_status pa_decode_partitioned_noalloc(void* out, const void* query, const void* key_cache,
+                                        const void* value_cache, const int32_t* block_tables,
+                                        int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                        int32_t num_seqs, int32_t num_q_heads,
+                                        int32_t num_kv_heads, int32_t head_dim,
+                                        int32_t block_size, int32_t num_blocks,
+                                        int32_t max_context_len, float scale, pa_dtype dtype,
+                                        int32_t partition_size, const int32_t* work_items,
+                                        int32_t num_work_items, hipStream_t stream,
+                                        hipEvent_t start_event, hipEvent_t stop_event) {
+  pa::clear_error();
+  const char* what = "pa_decode_partitioned_noalloc";
+  pa::AttnParams p;
+  const pa_status st = pa::check_decode(out, query, key_cache, value_cache, block_tables,
+                                        max_blocks_per_seq, context_lens, num_seqs, num_q_heads,
+                                        num_kv_heads, head_dim, block_size, num_blocks,
+                                        max_context_len, scale, dtype, &p);
+  if (st != PA_OK) return st;
+  if (num_seqs > 0 && partition_size > 0) {
+    const size_t need = pa_decode_partitioned_workspace_size(
+        num_seqs, num_q_heads, head_dim, max_context_len, partition_size);
+    if (need > kScratchBytes)
+      return fail(PA_ERR_INVALID_ARG,
+                  "pa_decode_partitioned_noalloc: the split workspace this call needs "
+                  "(num_seqs x num_q_heads x ceil(max_context_len / partition_size) x "
+                  "(head_dim + 2) x 4 bytes, each part 256-byte aligned) exceeds the 64 MiB "
+                  "scratch array; use pa_decode_partitioned with a caller workspace");
+  }
+  void* ws = nullptr;
+  if (num_seqs > 0) {
+    int sdev = -1, cur = -1;
+    if (stream && (hipStreamGetDevice(stream, &sdev) != hipSuccess ||
+                   hipGetDevice(&cur) != hipSuccess || sdev != cur)) {
+      (void)hipGetLastError();
+      return fail(PA_ERR_INVALID_ARG,
+                  "pa_decode_partitioned_noalloc: the stream must belong to the current device");
+    }
+    ws = scratch_of_current_device(what);
+    if (!ws) return PA_ERR_HIP;
+  }
+  return pa::partitioned(p, false, dtype, head_dim, block_size, max_context_len, partition_size,
+                         work_items, num_work_items, ws, kScratchBytes, stream, start_event,
+                         stop_event, what);
 }
 
 }  // extern "C"

@@ -268,3 +268,25 @@ def test_partitioned_rejects_an_empty_work_list():
     with pytest.raises(ValueError, match="pass None"):
         pa.pa_decode_partitioned_int8(None, None, None, None, None, None, None, None, 64, 0.1,
                                       "bf16", 512, None, work_items=empty)
+
+
+def test_noalloc_decode_rejects_oversized_workspaces_on_host():
+    """The no-allocation decode serves workspaces up to its scratch array's
+    size; a larger request is refused before any device call."""
+    cap = pa.pa_decode_partitioned_noalloc_max_workspace()
+    assert cap == 64 << 20
+    # 64 seqs x 28 heads x 2048 partitions of 16 tokens x 520 bytes: far above 64 MiB
+    need = pa.pa_decode_partitioned_workspace_size(64, 28, 128, 32768, 16)
+    assert need > cap
+    st = L.pa_decode_partitioned_noalloc(BAD, BAD, BAD, BAD, BAD, 2048, BAD, 64, 28, 4, 128, 16,
+                                         1 << 20, 32768, 0.088, 1, 16, None, 0, None, None, None)
+    assert st == _native.PA_ERR_INVALID_ARG
+    assert "64 MiB" in L.pa_last_error().decode()
+    # argument errors come first, exactly as for pa_decode_partitioned
+    st = L.pa_decode_partitioned_noalloc(BAD, BAD, BAD, BAD, BAD, 64, BAD, 2, 7, 2, 128, 16, 10,
+                                         1024, 0.088, 1, 512, None, 0, None, None, None)
+    assert st == _native.PA_ERR_INVALID_ARG
+    assert decode_part(S=0) == _native.PA_OK
+    assert L.pa_decode_partitioned_noalloc(None, None, None, None, None, 4, None, 0, 8, 2, 128, 16,
+                                           10, 64, 0.088, 1, 512, None, 0, None, None,
+                                           None) == _native.PA_OK
