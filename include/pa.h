@@ -172,6 +172,7 @@ size_t pa_decode_partitioned_workspace_size(int32_t num_seqs,
  * l = sum exp(logit - m) and acc = sum exp(logit - m) V; a second kernel
  * merges: out = sum_p e^(m_p - M) acc_p / sum_p e^(m_p - M) l_p with
  * M = max_p m_p.  Result as pa_decode up to fp32 rounding order.
+ * num_q_heads * head_dim must stay below 2^23 (PA_ERR_UNSUPPORTED beyond).
  * A context_lens[i] above max_context_len breaks the caller's side of the
  * contract: only its first ceil(max_context_len / P) partitions are read
  * (every access still stays inside the caller's buffers).

@@ -479,6 +479,10 @@ pa_status partitioned(AttnParams& p, bool q8, pa_dtype dtype, int32_t head_dim,
   if (work_items && num_work_items == 0 && num_seqs > 0)
     return fail(PA_ERR_INVALID_ARG,
                 "an empty work list names no partition: pass NULL for the full grid");
+  // the merge reads 64 partitions of one (sequence, head) through one buffer
+  // resource of 64 workspace rows of num_q_heads * head_dim floats
+  if (static_cast<int64_t>(num_q_heads) * head_dim * 4 * 64 > INT32_MAX)
+    return fail(PA_ERR_UNSUPPORTED, "num_q_heads * head_dim must stay below 2^23 for the merge");
   if ((static_cast<int64_t>(num_work_items) + 7) * p.num_kv_heads * p.head_chunks > INT32_MAX)
     return fail(PA_ERR_UNSUPPORTED, "num_work_items * num_kv_heads * head chunks overflows int32");
   if (num_seqs == 0) return pa::mark_events(start_event, stop_event, stream, what);

@@ -431,6 +431,9 @@ struct WaveAttn {
   };
 
   int wave, lane, krow, kcol, vrow, vcol;
+  // QK: the head whose dot product this lane holds after the sum over its
+  // aligned 8-lane group (qk_sum); lanes with (lane & 7) < GTP write it
+  int qhead;
   const char* kbase;
   const char* vbase;
   const uint16_t* q;
@@ -462,6 +465,10 @@ struct WaveAttn {
     }
     vrow = lane / VL;
     vcol = lane % VL;
+    {
+      const int b = lane & 7;
+      qhead = GTP == 8 ? b : ((b & (GTP - 1)) ^ ((b & 4) ? GTP - 1 : 0));
+    }
     kbase = static_cast<const char*>(p.k_cache);
     vbase = static_cast<const char*>(p.v_cache);
     q = static_cast<const uint16_t*>(p.q);
@@ -554,21 +561,24 @@ struct WaveAttn {
     }
   }
 
-  // q slices for the QK layout: chunk c of head hh = dims c*8*QL + kcol*8 .. +8
-  // (INT8: dims kcol*KB + c*8 .. +8, the lane's codes).
-  // Heads past nact reread the last active head (their results are never
-  // stored): loads on every path keep the wait counts exact.
-  __device__ __forceinline__ void load_q(uint4 (&qv)[GT][KC], int64_t row0, int nact) const {
+  // q slices for the QK layout: chunk c = dims c*8*QL + kcol*8 .. +8 (INT8:
+  // dims kcol*KB + c*8 .. +8, the lane's codes) of the head in slot r, which
+  // is head r ^ qhead (the slot order qk_sum's reduce-scatter needs).
+  // Heads past nact (and slots past the group) reread the last active head:
+  // their results are never used, and loads on every path keep the wait
+  // counts exact.
+  __device__ __forceinline__ void load_q(uint4 (&qv)[GTP][KC], int64_t row0, int nact) const {
 #pragma unroll
-    for (int hh = 0; hh < GT; ++hh)
+    for (int r = 0; r < GTP; ++r)
 #pragma unroll
       for (int c = 0; c < KC; ++c)
-        qv[hh][c] = *reinterpret_cast<const uint4*>(
-            q + (row0 + min(hh, nact - 1)) * D + (Q8 ? kcol * T8::KB + c * 8 : c * 8 * QL + kcol * 8));
+        qv[r][c] = *reinterpret_cast<const uint4*>(
+            q + (row0 + min(r ^ qhead, nact - 1)) * D +
+            (Q8 ? kcol * T8::KB + c * 8 : c * 8 * QL + kcol * 8));
   }
 
-  // The lane's part of the raw q.k of its token in load group j, head hh.
-  __device__ __forceinline__ float qk_part(const uint4 (&qv)[GT][KC], const KBuf& kx, int j,
+  // The lane's part of the raw q.k of its token in load group j, q slot hh.
+  __device__ __forceinline__ float qk_part(const uint4 (&qv)[GTP][KC], const KBuf& kx, int j,
                                            int hh) const {
     if constexpr (Q8) {
       // the lane's codes as exact 16-bit pairs, in dim order: pair m holds
@@ -604,45 +614,81 @@ struct WaveAttn {
     }
   }
 
-  // Logits of the wave's unit i (raw q.k; scaled in the softmax), written by
-  // the first lane of each token's lanes.
-  __device__ __forceinline__ void qk_unit(const uint4 (&qv)[GT][KC], const KBuf& kx,
-                                          int i) const {
+  // Sum over the lane's aligned 8-lane group of the products of every q
+  // slot, as a reduce-scatter: slot r of lane b holds head r ^ qhead(b), so
+  // each step adds half of a lane's slots to the partner lane's matching
+  // slots (lane ^ 7: row_half_mirror; lane ^ 2, lane ^ 1: quad permutes) and
+  // keeps the other half, and the lane ends with the group's total for its
+  // own head qhead.  8 heads take 4 + 2 + 1 DPP adds instead of 3 per head;
+  // with fewer slots the remaining steps are plain sums (qhead is chosen so
+  // that a lane and its lane ^ 7 partner hold the same head).
+  __device__ __forceinline__ float qk_sum(const float (&a)[GTP]) const {
+    if constexpr (GTP == 8) {
+      const float t0 = a[0] + dpp<0x141>(a[7]), t1 = a[1] + dpp<0x141>(a[6]);
+      const float t2 = a[2] + dpp<0x141>(a[5]), t3 = a[3] + dpp<0x141>(a[4]);
+      const float u0 = t0 + dpp<0x4E>(t2), u1 = t1 + dpp<0x4E>(t3);
+      return u0 + dpp<0xB1>(u1);
+    } else if constexpr (GTP == 4) {
+      const float u0 = a[0] + dpp<0x4E>(a[2]), u1 = a[1] + dpp<0x4E>(a[3]);
+      const float v = u0 + dpp<0xB1>(u1);
+      return v + dpp<0x141>(v);
+    } else if constexpr (GTP == 2) {
+      float v = a[0] + dpp<0xB1>(a[1]);
+      v += dpp<0x4E>(v);
+      return v + dpp<0x141>(v);
+    } else {
+      return group_sum<8>(a[0]);
+    }
+  }
+
+  // Logits of the wave's unit i in the base-2 domain (scale * log2 e * q.k),
+  // one per (token, head) from the lanes that hold a head of their own
+  // ((lane & 7) < GTP); tokens past the span get -inf (their slots may hold
+  // NaN).  qmax gathers the lane's largest logit (of head qhead).
+  __device__ __forceinline__ void qk_unit(const uint4 (&qv)[GTP][KC], const KBuf& kx, int i,
+                                          const Span& s, float& qmax) const {
     const int u = wave + kWaves * i;
+    const bool tail = (u + 1) * UNIT > s.n;     // uniform: only the span's last unit
+    const bool writer = (lane & 7) < GTP;
+    auto finish = [&](float v, int tok) {
+      v *= scale_log2;
+      if (tail) v = tok < s.n ? v : -__builtin_inff();
+      qmax = fmaxf(qmax, v);
+      if (writer) s_lds[tok * GTP + qhead] = v;
+    };
     if constexpr (QL == 16) {
-      // groups j and j + 1 together: each lane sums its 8-lane half of a
+      // groups j and j + 1 together: each lane's 8-lane sum covers half of a
       // token, then v_permlane16_swap trades rows so that one add leaves
       // group j's totals in rows 0 and 2 and group j + 1's in rows 1 and 3
       static_assert(KGROUPS % 2 == 0, "QK groups come in pairs");
       const int odd = (lane >> 4) & 1;
 #pragma unroll
       for (int j = 0; j < KGROUPS; j += 2) {
-        float sv[GTP];
+        // one group at a time: all GTP partial sums of a group are live
+        // until its reduce-scatter
+        float a[GTP];
 #pragma unroll
-        for (int hh = 0; hh < GT; ++hh) {
-          const float a0 = group_sum<8>(qk_part(qv, kx, j, hh));
-          const float a1 = group_sum<8>(qk_part(qv, kx, j + 1, hh));
-          const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a0),
-                                                          __float_as_uint(a1), false, false);
-          sv[hh] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-          if constexpr (Q8) sv[hh] *= odd ? kx.sc[j + 1] : kx.sc[j];
-        }
+        for (int r = 0; r < GTP; ++r) a[r] = qk_part(qv, kx, j, r);
+        const float v0 = qk_sum(a);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int hh = GT; hh < GTP; ++hh) sv[hh] = 0.f;
-        if ((lane & 7) == 0) lds_store(s_lds + (u * UNIT + (j + odd) * KTOK + krow) * GTP, sv);
+        for (int r = 0; r < GTP; ++r) a[r] = qk_part(qv, kx, j + 1, r);
+        const float v1 = qk_sum(a);
+        const auto rr = __builtin_amdgcn_permlane16_swap(__float_as_uint(v0),
+                                                         __float_as_uint(v1), false, false);
+        float v = __uint_as_float(rr[0]) + __uint_as_float(rr[1]);
+        if constexpr (Q8) v *= odd ? kx.sc[j + 1] : kx.sc[j];
+        finish(v, u * UNIT + (j + odd) * KTOK + krow);
       }
     } else {
 #pragma unroll
       for (int j = 0; j < KGROUPS; ++j) {
-        float sv[GTP];
+        float a[GTP];
 #pragma unroll
-        for (int hh = 0; hh < GT; ++hh) {
-          sv[hh] = group_sum<QL>(qk_part(qv, kx, j, hh));
-          if constexpr (Q8) sv[hh] *= kx.sc[j];
-        }
-#pragma unroll
-        for (int hh = GT; hh < GTP; ++hh) sv[hh] = 0.f;
-        if (kcol == 0) lds_store(s_lds + (u * UNIT + j * KTOK + krow) * GTP, sv);
+        for (int r = 0; r < GTP; ++r) a[r] = qk_part(qv, kx, j, r);
+        float v = qk_sum(a);
+        if constexpr (Q8) v *= kx.sc[j];
+        finish(v, u * UNIT + j * KTOK + krow);
       }
     }
   }
@@ -725,44 +771,43 @@ struct WaveAttn {
   // every path the compiler's wait counts see the ring in issue order and
   // wait for one unit at a time (a skipped refill would make it wait for all).
   template <int DEPTH>
-  __device__ __forceinline__ void logits(const uint4 (&qv)[GT][KC], KBuf (&kb)[DEPTH],
-                                         const Span& s) const {
+  __device__ __forceinline__ void logits(const uint4 (&qv)[GTP][KC], KBuf (&kb)[DEPTH],
+                                         const Span& s, float& qmax) const {
     for (int i = 0; i < s.cnt; i += DEPTH) {
 #pragma unroll
       for (int b = 0; b < DEPTH; ++b) {
-        if (b == 0 || i + b < s.cnt) qk_unit(qv, kb[b], i + b);   // uniform
+        if (b == 0 || i + b < s.cnt) qk_unit(qv, kb[b], i + b, s, qmax);   // uniform
         load_k(kb[b], s, i + b + DEPTH);
       }
     }
   }
 
-  // The wave's softmax over its tokens of the span (lane l takes the wave's
-  // tokens l, l + 64, ...): scales the logits into the base-2 domain, folds
-  // their max into m_run, overwrites them with p = 2^(logit - m_run), and
-  // sets l_run = alpha * l_run + sum p with alpha = 2^(old m_run - new m_run),
-  // which it returns for the caller's accumulator.
-  __device__ __forceinline__ void softmax(const Span& s, float (&m_run)[GT], float (&l_run)[GT],
-                                          float (&alpha)[GT]) const {
+  // The wave's softmax over its tokens of the span, from the logits qk_unit
+  // left in LDS (base-2 domain, -inf past the span) and each lane's qmax:
+  // folds the wave's max per head into m_run, overwrites the logits with
+  // p = 2^(logit - m_run) (lane l takes the wave's tokens l, l + 64, ...), and
+  // sets l_run = alpha * l_run + sum p with alpha = 2^(old m_run - new
+  // m_run), which it returns for the caller's accumulator.
+  __device__ __forceinline__ void softmax(const Span& s, float qmax, float (&m_run)[GT],
+                                          float (&l_run)[GT], float (&alpha)[GT]) const {
     const int wtok = s.cnt * UNIT;
     auto tok_of = [&](int r) { return (wave + kWaves * (r / UNIT)) * UNIT + (r % UNIT); };
-    float mloc[GT];
-#pragma unroll
-    for (int hh = 0; hh < GT; ++hh) mloc[hh] = -__builtin_inff();
-    for (int r = lane; r < wtok; r += 64) {
-      const int t = tok_of(r);
-      float v[GTP];
-      lds_load(v, s_lds + t * GTP);
-#pragma unroll
-      for (int hh = 0; hh < GT; ++hh) {
-        v[hh] *= scale_log2;
-        if (t < s.n) mloc[hh] = v[hh] > mloc[hh] ? v[hh] : mloc[hh];
-      }
-      lds_store(s_lds + t * GTP, v);
+    // lanes l, l ^ 8, ..., l ^ 56 hold the same head: the wave's max per head
+    float mx = fmaxf(qmax, dpp<0x128>(qmax));   // row_ror:8
+    {
+      const uint32_t b = __float_as_uint(mx);
+      const auto r16 = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+      mx = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+      const uint32_t c = __float_as_uint(mx);
+      const auto r32 = __builtin_amdgcn_permlane32_swap(c, c, false, false);
+      mx = fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
     }
     float m_new[GT];
 #pragma unroll
     for (int hh = 0; hh < GT; ++hh) {
-      m_new[hh] = fmaxf(m_run[hh], wave_max_all(mloc[hh]));
+      // lane hh (< 8) holds head hh
+      const float mh = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mx), hh));
+      m_new[hh] = fmaxf(m_run[hh], mh);
       alpha[hh] = fast_exp2(m_run[hh] - m_new[hh]);   // 0 while m_run is -inf
       m_run[hh] = m_new[hh];
     }
@@ -775,7 +820,7 @@ struct WaveAttn {
       lds_load(v, s_lds + t * GTP);
 #pragma unroll
       for (int hh = 0; hh < GT; ++hh) {
-        const float pr = t < s.n ? fast_exp2(v[hh] - m_new[hh]) : 0.f;
+        const float pr = fast_exp2(v[hh] - m_new[hh]);   // 0 past the span (-inf)
         v[hh] = pr;
         lsum[hh] += pr;
       }
@@ -923,20 +968,21 @@ __global__ __launch_bounds__(kThreads) void single_kernel(AttnParams p) {
   for (int c0 = 0; c0 < L; c0 += p.chunk) {
     const typename W::Span s = w.span(bt, c0, min(p.chunk, L - c0));
     if (s.cnt == 0) continue;                      // uniform: this wave has no tokens
+    float qmax = -__builtin_inff();
     {
-      uint4 qv[GT][W::KC];
+      uint4 qv[W::GTP][W::KC];
       w.load_q(qv, row0, nact);                    // first: waiting for q must not wait for K
       typename W::KBuf kb[kDepthSingle];
 #pragma unroll
       for (int b = 0; b < kDepthSingle; ++b) w.load_k(kb[b], s, b);
-      w.template logits<kDepthSingle>(qv, kb, s);
+      w.template logits<kDepthSingle>(qv, kb, s, qmax);
     }
     typename W::VBuf vb[kDepthSingle];             // streams in during the softmax
 #pragma unroll
     for (int b = 0; b < kDepthSingle; ++b) w.load_v(vb[b], s, b);
     wave_lds_sync();
     float alpha[GT];
-    w.softmax(s, m_run, l_run, alpha);
+    w.softmax(s, qmax, m_run, l_run, alpha);
 #pragma unroll
     for (int hh = 0; hh < GT; ++hh)
 #pragma unroll
@@ -949,13 +995,36 @@ __global__ __launch_bounds__(kThreads) void single_kernel(AttnParams p) {
                                   row0, nact, 0);
 }
 
+// Work-list grid: linear workgroup id -> (work item, KV head x chunk).  Ids
+// come in groups of 8 * nkv: 8 consecutive items x the nkv KV heads (x head
+// chunks), the KV heads of an item 8 ids apart, so that they share an XCD
+// (workgroups go to the 8 XCDs round-robin by id) and read the same token
+// rows.  Inside an XCD the dispatcher deals consecutive workgroups to its
+// shader engines in turn (four of them on this part, measured), so a KV head
+// fixed by the id's place in its group would put every workgroup of one head
+// on the same shader engine: each engine then streams one head's slices
+// only, at a fixed byte offset inside every token row.  One offset class of
+// the K pool streams slower; the engine holding it became the end of the
+// launch (its workgroups ~20 % longer, the last ~10 us of the launch spent on
+// them).  So the KV head rotates with the group: every engine serves every
+// head (Qwen2.5-7B-shaped layer: 121 -> 116 us per call).
+__device__ __forceinline__ void list_item_of(int id, int nkv, int* item, int* kvhc) {
+  const int grp = id / (8 * nkv);
+  const int r = id - grp * 8 * nkv;
+  // with 1, 2 or 4 heads the group's slots repeat every 4 workgroups of an
+  // XCD, so the rotation advances once per 4 / nkv groups
+  const int div = (nkv < 4 && 4 % nkv == 0) ? 4 / nkv : 1;
+  *kvhc = ((r >> 3) + grp / div) % nkv;
+  *item = grp * 8 + (r & 7);
+}
+
 // Split-context partitions ("v2"): one (sequence, partition) work item for
 // one KV head x head chunk per workgroup; each wave runs its own softmax over
 // its units of the partition and the waves combine into the partition's
 // (max, sum, acc) workspace slot.
-//  list:  1-D grid over work items x (KV heads x chunks).  Linear id =
-//         (item / 8) * 8 * nkv + kvhc * 8 + item % 8: ids equal mod 8 share
-//         an XCD, so the KV heads of one item (the same token rows) do.
+//  list:  1-D grid over work items x (KV heads x chunks), list_item_of():
+//         the KV heads of one item (the same token rows) share an XCD, and
+//         each shader engine serves every KV head.
 //  dense: grid (partitions, KV heads x chunks, sequences), partitions fastest
 //         and their count odd: workgroups go to the 8 XCDs round-robin by
 //         linear id, and an odd stride rotates each sequence's partition p
@@ -967,11 +1036,8 @@ __global__ __launch_bounds__(kThreads) void split_kernel(AttnParams p) {
   extern __shared__ float lds[];
   int seq, kvhc, part;
   if (p.work_items) {
-    const int nkv = p.num_kv_heads * p.head_chunks;
-    const int grp = blockIdx.x / (8 * nkv);
-    const int r = blockIdx.x - grp * 8 * nkv;
-    kvhc = r >> 3;
-    const int item = grp * 8 + (r & 7);
+    int item;
+    list_item_of(blockIdx.x, p.num_kv_heads * p.head_chunks, &item, &kvhc);
     if (item >= p.num_work_items) return;          // uniform: whole workgroup
     seq = __builtin_amdgcn_readfirstlane(p.work_items[2 * item]);
     part = __builtin_amdgcn_readfirstlane(p.work_items[2 * item + 1]);
@@ -1009,8 +1075,9 @@ __global__ __launch_bounds__(kThreads) void split_kernel(AttnParams p) {
     // Issue order matters: loads complete in order for the wait counts, so q
     // goes first (waiting for it must not wait for the rings).
     typename W::VBuf vb[DEPTH];
+    float qmax = -__builtin_inff();
     {
-      uint4 qv[GT][W::KC];
+      uint4 qv[W::GTP][W::KC];
       w.load_q(qv, row0, nact);
       typename W::KBuf kb[DEPTH];
 #pragma unroll
@@ -1023,7 +1090,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(AttnParams p) {
 #pragma unroll
         for (int b = 0; b < DEPTH; ++b) w.load_v(vb[b], s, b);
       }
-      w.template logits<DEPTH>(qv, kb, s);
+      w.template logits<DEPTH>(qv, kb, s, qmax);
     }
     if constexpr (!EARLY_V) {
 #pragma unroll
@@ -1031,7 +1098,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(AttnParams p) {
     }
     wave_lds_sync();
     float alpha[GT];
-    w.softmax(s, m_w, l_w, alpha);
+    w.softmax(s, qmax, m_w, l_w, alpha);
     // acc is born here, after q is dead: the two never share registers
 #pragma unroll
     for (int hh = 0; hh < GT; ++hh)
@@ -1049,95 +1116,90 @@ __global__ __launch_bounds__(kThreads) void split_kernel(AttnParams p) {
                                  row0, nact, part);
 }
 
-// Merge of the partitions of one (sequence, q head) per workgroup:
+// Merge of the partitions of one (sequence, q head) by one wave:
 //   M = max_p m_p,  w_p = 2^(m_p - M),  out = sum_p w_p acc_p / sum_p w_p l_p
-// Partials arrive in batches of 64: thread t reads float4 column t % C4 of
-// partials t / C4, t / C4 + ROWS, ...  The first batch is requested together
-// with the maxima, before M is known, so a context of up to 64 partitions
-// costs one round trip to memory after its length; the batch's weights go
-// through LDS.
+// Lane j holds the max and sum of partitions j, j + 64, ...; the partials'
+// float4 columns are read PER partitions per load (lane: column lane % C4,
+// partition k0 + lane / C4 + PER * r), up to 64 partitions in one round
+// trip, requested together with the maxima before M is known.  A partition's
+// weight is its max minus M from the lane that loaded it (ds_bpermute).  One
+// wave per workgroup: every workgroup of a decode is resident at once and no
+// barrier is needed.
 template <int DT, int D>
-__global__ __launch_bounds__(kThreads) void merge_kernel(AttnParams p) {
+__global__ __launch_bounds__(64) void merge_wave_kernel(AttnParams p) {
   using F = Fmt<DT>;
-  constexpr int C4 = D / 4;                 // float4 columns of one partial
-  constexpr int ROWS = kThreads / C4;       // partials per load round
-  constexpr int BATCH = 64;
-  constexpr int R = BATCH / ROWS;           // load rounds per batch
-  __shared__ float s_w[BATCH];
-  __shared__ float s_m[kWaves];
-  __shared__ float s_l;
-  __shared__ float4 s_acc[kWaves][C4];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  constexpr int C4 = D / 4;            // float4 columns of one partial
+  constexpr int PER = 64 / C4;         // partitions per load (2 for D 128, 4 for D 64)
+  constexpr int R = 64 / PER;          // loads per lane for 64 partitions
+  const int lane = threadIdx.x;
   const int pair = blockIdx.x;
   const int seq = pair / p.num_q_heads;
-  int L = p.context_lens[seq];
+  int L = __builtin_amdgcn_readfirstlane(p.context_lens[seq]);
   L = max(0, min(L, p.mb * p.block_size));
   const int np = min((L + p.chunk - 1) / p.chunk, p.num_parts);
   uint16_t* out = static_cast<uint16_t*>(p.out) + static_cast<int64_t>(pair) * D;
-  if (np == 0) {                                   // uniform: whole workgroup
-    for (int d = tid; d < D; d += kThreads) out[d] = 0;
+  if (np == 0) {                                   // uniform
+    for (int d = lane; d < D; d += 64) out[d] = 0;
     return;
   }
   // partition k of (seq, head) sits in workspace row (seq * nP + k) * Hq + head
   const int64_t base = static_cast<int64_t>(seq) * p.num_parts * p.num_q_heads +
                        (pair - seq * p.num_q_heads);
-  const int64_t kstride = p.num_q_heads;
+  const int ks = p.num_q_heads;
   const float* pm = p.part_max + base;
   const float* ps = p.part_sum + base;
-  const float4* pa = reinterpret_cast<const float4*>(p.part_acc + base * D);
-  const int col = tid % C4, row = tid / C4;
+  const int col = lane % C4, row = lane / C4;
+  // a batch of 64 accumulator rows k0 .. k0 + 63 of the (seq, head) through
+  // one buffer resource: row k0 + j at byte j * Hq * D * 4, this lane's float4
+  // at col * 16.  The resource ends after row np - 1, so the loads of rows
+  // past it fetch nothing and return zeros (the bound applies to the per-lane
+  // offset, which therefore carries the row).  The host keeps 64 rows under
+  // 2 GiB (Hq * D < 2^23).
+  const uint32_t row_bytes = static_cast<uint32_t>(ks) * D * 4;
+  const uint32_t voff = static_cast<uint32_t>(row) * row_bytes + col * 16;
 
   float4 x[R];
   auto load_batch = [&](int k0) {
+    const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        p.part_acc + (base + static_cast<int64_t>(k0) * ks) * D, 0,
+        static_cast<int>(min(np - k0, 64) * row_bytes), 0x00020000);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const int k = k0 + row + r * ROWS;
-      x[r] = k < np ? pa[static_cast<int64_t>(k) * kstride * C4 + col]
-                    : make_float4(0.f, 0.f, 0.f, 0.f);
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(
+          rsrc, voff + static_cast<uint32_t>(PER * r) * row_bytes, 0, 0);
+      x[r] = make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]),
+                         __uint_as_float(v[3]));
     }
   };
   load_batch(0);
-  // maxima: thread t < 64 keeps m_t and l_t of the first batch
-  const float m0 = tid < np ? pm[tid * kstride] : -__builtin_inff();
-  const float l0 = tid < np ? ps[tid * kstride] : 0.f;
-  float m = m0;
-  for (int k = tid + kThreads; k < np; k += kThreads) m = fmaxf(m, pm[k * kstride]);
-  m = wave_max_all(m);
-  if (lane == 0) s_m[wave] = m;
-  __syncthreads();
-  const float M = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
+  const float m0 = lane < np ? pm[lane * ks] : -__builtin_inff();
+  const float l0 = lane < np ? ps[lane * ks] : 0.f;
+  float mloc = m0;
+  for (int k = lane + 64; k < np; k += 64) mloc = fmaxf(mloc, pm[k * ks]);
+  const float M = wave_max_all(mloc);
+  const float w0 = lane < np ? fast_exp2(m0 - M) : 0.f;   // weight of partition `lane`
+  float lloc = w0 * l0;
+  for (int k = lane + 64; k < np; k += 64) lloc += fast_exp2(pm[k * ks] - M) * ps[k * ks];
+  const float lt = wave_sum_all(lloc);
 
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  float l = 0.f;                                   // wave 0 only
-  for (int k0 = 0; k0 < np; k0 += BATCH) {
-    if (tid < BATCH) {
-      const int k = k0 + tid;
-      float wk = 0.f;
-      if (k < np) {
-        const float mk = k0 == 0 ? m0 : pm[k * kstride];
-        const float lk = k0 == 0 ? l0 : ps[k * kstride];
-        wk = fast_exp2(mk - M);
-        l += wk * lk;
-      }
-      s_w[tid] = wk;
+  for (int k0 = 0; k0 < np; k0 += 64) {
+    float wl = w0;                                 // weights of partitions k0 + lane
+    if (k0 > 0) {                                  // uniform: only past 64 partitions
+      load_batch(k0);
+      wl = k0 + lane < np ? fast_exp2(pm[(k0 + lane) * ks] - M) : 0.f;
     }
-    __syncthreads();
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const float wk = s_w[row + r * ROWS];
+      // partition k0 + row + PER r: rows past np are zeros with weight 0
+      const float wk = __shfl(wl, row + PER * r);
       acc.x = fmaf(wk, x[r].x, acc.x);
       acc.y = fmaf(wk, x[r].y, acc.y);
       acc.z = fmaf(wk, x[r].z, acc.z);
       acc.w = fmaf(wk, x[r].w, acc.w);
     }
-    if (k0 + BATCH < np) {                         // uniform
-      __syncthreads();                             // s_w is rewritten for the next batch
-      load_batch(k0 + BATCH);
-    }
   }
-  // rows of one column inside a wave, then across the waves
+  // the rows of one column: lanes col, col + C4, ...
 #pragma unroll
   for (int off = C4; off < 64; off <<= 1) {
     acc.x += __shfl_xor(acc.x, off);
@@ -1145,25 +1207,10 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(AttnParams p) {
     acc.z += __shfl_xor(acc.z, off);
     acc.w += __shfl_xor(acc.w, off);
   }
-  if (lane < C4) s_acc[wave][lane] = acc;
-  if (wave == 0) {
-    l = wave_sum_all(l);
-    if (lane == 0) s_l = l;
-  }
-  __syncthreads();
-  if (tid < C4) {
-    float4 v = s_acc[0][tid];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) {
-      v.x += s_acc[w][tid].x;
-      v.y += s_acc[w][tid].y;
-      v.z += s_acc[w][tid].z;
-      v.w += s_acc[w][tid].w;
-    }
-    const float lt = s_l;
-    const uint32_t lo = F::narrow(v.x / lt) | (static_cast<uint32_t>(F::narrow(v.y / lt)) << 16);
-    const uint32_t hi = F::narrow(v.z / lt) | (static_cast<uint32_t>(F::narrow(v.w / lt)) << 16);
-    *reinterpret_cast<uint2*>(out + tid * 4) = make_uint2(lo, hi);
+  if (row == 0) {
+    const uint32_t lo = F::narrow(acc.x / lt) | (static_cast<uint32_t>(F::narrow(acc.y / lt)) << 16);
+    const uint32_t hi = F::narrow(acc.z / lt) | (static_cast<uint32_t>(F::narrow(acc.w / lt)) << 16);
+    *reinterpret_cast<uint2*>(out + col * 4) = make_uint2(lo, hi);
   }
 }
 
@@ -1192,7 +1239,7 @@ int launch_attn(int kind, const AttnParams& p, hipStream_t stream, hipEvent_t st
                 hipEvent_t stop) {
   if (kind == 2) {
     const dim3 grid(p.num_seqs * p.num_q_heads);
-    hipExtLaunchKernelGGL((merge_kernel<DT, D>), grid, dim3(kThreads), 0, stream, start, stop, 0, p);
+    hipExtLaunchKernelGGL((merge_wave_kernel<DT, D>), grid, dim3(64), 0, stream, start, stop, 0, p);
     return static_cast<int>(hipGetLastError());
   }
   switch (p.heads_per_wg) {

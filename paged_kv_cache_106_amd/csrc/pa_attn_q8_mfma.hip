@@ -90,13 +90,9 @@ __global__ __launch_bounds__(kThreadsM) void q8_mfma_split_kernel(AttnParams p) 
   extern __shared__ __align__(16) char lds[];
   int seq, kvhc, part;
   if (p.work_items) {
-    // work list: 8 consecutive items x the KV heads (x head chunks); the KV
-    // heads of an item are 8 workgroups apart, i.e. on one XCD
-    const int nkv = p.num_kv_heads * p.head_chunks;
-    const int grp = blockIdx.x / (8 * nkv);
-    const int r = blockIdx.x - grp * 8 * nkv;
-    kvhc = r >> 3;
-    const int item = grp * 8 + (r & 7);
+    // the work-list grid of the vector kernels (list_item_of)
+    int item;
+    list_item_of(blockIdx.x, p.num_kv_heads * p.head_chunks, &item, &kvhc);
     if (item >= p.num_work_items) return;          // uniform: whole workgroup
     seq = __builtin_amdgcn_readfirstlane(p.work_items[2 * item]);
     part = __builtin_amdgcn_readfirstlane(p.work_items[2 * item + 1]);

@@ -270,6 +270,15 @@ def test_partitioned_rejects_an_empty_work_list():
                                       "bf16", 512, None, work_items=empty)
 
 
+def test_partitioned_rejects_head_rows_the_merge_cannot_address():
+    """The merge reads 64 partials of one (sequence, head) through a 32-bit
+    buffer range of 64 workspace rows of num_q_heads * head_dim floats: head
+    counts past that are refused up front."""
+    assert decode_part(Hq=65536, Hkv=8192) == _native.PA_ERR_UNSUPPORTED
+    assert "2^23" in L.pa_last_error().decode()
+    assert decode_part(Hq=32768, Hkv=4096, items=BAD, nitems=0) == _native.PA_ERR_INVALID_ARG
+
+
 def test_noalloc_decode_rejects_oversized_workspaces_on_host():
     """The no-allocation decode serves workspaces up to its scratch array's
     size; a larger request is refused before any device call."""
