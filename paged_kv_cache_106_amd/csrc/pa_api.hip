@@ -16,7 +16,6 @@ namespace pa {
 namespace {
 thread_local std::string g_last_error;
 
-constexpr int32_t kSingleChunk = 512;     // tokens per LDS pass of the single-pass kernel
 constexpr int32_t kMaxPartition = 1024;
 constexpr int32_t kMaxGrid = 65535;        // grid y / z limit
 

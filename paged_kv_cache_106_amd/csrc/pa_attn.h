@@ -264,10 +264,11 @@ template <int GT>
 constexpr bool kNarrow = GT >= PA_NARROW_MIN_GT;
 
 // LDS (floats): logits / probabilities [chunk][GTP], wave partial outputs
-// [kWaves][GT][D], wave maxima and sums [kWaves][GTP] each.
-__host__ __device__ constexpr size_t lds_floats(int D, int GT, int GTP, int chunk) {
-  return static_cast<size_t>(chunk) * GTP + static_cast<size_t>(kWaves) * GT * D +
-         2 * static_cast<size_t>(kWaves) * GTP;
+// [nw][GT][D], wave maxima and sums [nw][GTP] each, for nw waves.
+__host__ __device__ constexpr size_t lds_floats(int D, int GT, int GTP, int chunk,
+                                                int nw = kWaves) {
+  return static_cast<size_t>(chunk) * GTP + static_cast<size_t>(nw) * GT * D +
+         2 * static_cast<size_t>(nw) * GTP;
 }
 
 template <int N>
@@ -398,7 +399,7 @@ __device__ inline void wave_lds_sync() {
 // Per-wave pieces shared by the single-pass and split kernels.  Everything
 // here is wave-uniform except what a lane holds of q, K, V, the block ids
 // and the accumulators.
-template <int DT, int D, int GT, bool Q8 = false>
+template <int DT, int D, int GT, bool Q8 = false, int NW = kWaves>
 struct WaveAttn {
   using F = Fmt<DT>;
   using TL = Tile<D, GT, kNarrow<GT>>;
@@ -422,7 +423,7 @@ struct WaveAttn {
   using VBuf = UnitBuf<VVec, VLOADS, Q8 ? VLOADS : 0>;
 
   // Tokens [c0, c0 + n) of one sequence as one wave sees them: its units are
-  // u = wave, wave + 4, ... below ceil(n / UNIT), cnt of them.  Lane i of blk
+  // u = wave, wave + NW, ... below ceil(n / UNIT), cnt of them.  Lane i of blk
   // holds the physical block of the wave's unit i, fetched by one vector load
   // and read back with readlane when the unit's loads are issued.
   struct Span {
@@ -499,9 +500,9 @@ struct WaveAttn {
     s.c0 = c0;
     s.n = n;
     const int nunits = n > 0 ? (n + UNIT - 1) / UNIT : 0;
-    s.cnt = nunits > wave ? (nunits - wave + kWaves - 1) / kWaves : 0;
+    s.cnt = nunits > wave ? (nunits - wave + NW - 1) / NW : 0;
     s.blk = 0;
-    if (lane < s.cnt) s.blk = bt[(c0 + (wave + kWaves * lane) * UNIT) >> log2_bs];
+    if (lane < s.cnt) s.blk = bt[(c0 + (wave + NW * lane) * UNIT) >> log2_bs];
     return s;
   }
 
@@ -511,7 +512,7 @@ struct WaveAttn {
     const int j = max(0, min(i, s.cnt - 1));
     int blk = __builtin_amdgcn_readlane(s.blk, j);
     blk = static_cast<unsigned>(blk) < static_cast<unsigned>(num_blocks) ? blk : 0;
-    const int t0 = s.c0 + (wave + kWaves * j) * UNIT;
+    const int t0 = s.c0 + (wave + NW * j) * UNIT;
     return blk * block_bytes + static_cast<int64_t>(t0 & bs_mask) * tok_bytes;
   }
   // The same unit in a scale array [NB][Hkv][bs] (KV head offset excluded).
@@ -519,7 +520,7 @@ struct WaveAttn {
     const int j = max(0, min(i, s.cnt - 1));
     int blk = __builtin_amdgcn_readlane(s.blk, j);
     blk = static_cast<unsigned>(blk) < static_cast<unsigned>(num_blocks) ? blk : 0;
-    const int t0 = s.c0 + (wave + kWaves * j) * UNIT;
+    const int t0 = s.c0 + (wave + NW * j) * UNIT;
     return blk * sc_block_bytes + static_cast<int64_t>(t0 & bs_mask) * 4;
   }
 
@@ -583,11 +584,11 @@ struct WaveAttn {
     if constexpr (Q8) {
       // the lane's codes as exact 16-bit pairs, in dim order: pair m holds
       // dims 2m, 2m + 1 of the lane's KB
-      constexpr int NW = Words<KVec>::N;
-      uint32_t w[NW], kp[2 * NW];
+      constexpr int NWD = Words<KVec>::N;
+      uint32_t w[NWD], kp[2 * NWD];
       Words<KVec>::get(kx.d[j], w);
 #pragma unroll
-      for (int m = 0; m < NW; ++m) {
+      for (int m = 0; m < NWD; ++m) {
         kp[2 * m] = F::pack_int(code_at<0>(w[m]), code_at<1>(w[m]));
         kp[2 * m + 1] = F::pack_int(code_at<2>(w[m]), code_at<3>(w[m]));
       }
@@ -647,7 +648,7 @@ struct WaveAttn {
   // NaN).  qmax gathers the lane's largest logit (of head qhead).
   __device__ __forceinline__ void qk_unit(const uint4 (&qv)[GTP][KC], const KBuf& kx, int i,
                                           const Span& s, float& qmax) const {
-    const int u = wave + kWaves * i;
+    const int u = wave + NW * i;
     const bool tail = (u + 1) * UNIT > s.n;     // uniform: only the span's last unit
     const bool writer = (lane & 7) < GTP;
     auto finish = [&](float v, int tok) {
@@ -697,7 +698,7 @@ struct WaveAttn {
   // slots may hold NaN).
   __device__ __forceinline__ void pv_unit(float (&acc)[GT][VW], VBuf& vx,
                                           const Span& s, int i) const {
-    const int u = wave + kWaves * i;
+    const int u = wave + NW * i;
     if ((u + 1) * UNIT > s.n) {   // uniform: only the span's last unit
       asm volatile("");   // keeps this a branch (not selects on every unit)
 #pragma unroll
@@ -715,12 +716,12 @@ struct WaveAttn {
       for (int j = 0; j < VLOADS; ++j) {
         const int t = u * UNIT + j * VTOK + vrow;
         const float vs = vx.sc[j];   // 0 past the span
-        constexpr int NW = Words<VVec>::N;
-        uint32_t w[NW];
+        constexpr int NWD = Words<VVec>::N;
+        uint32_t w[NWD];
         Words<VVec>::get(vx.d[j], w);
         float vf[VW];
 #pragma unroll
-        for (int m = 0; m < NW; ++m) {
+        for (int m = 0; m < NWD; ++m) {
           vf[4 * m] = code_at<0>(w[m]);
           vf[4 * m + 1] = code_at<1>(w[m]);
           vf[4 * m + 2] = code_at<2>(w[m]);
@@ -791,7 +792,7 @@ struct WaveAttn {
   __device__ __forceinline__ void softmax(const Span& s, float qmax, float (&m_run)[GT],
                                           float (&l_run)[GT], float (&alpha)[GT]) const {
     const int wtok = s.cnt * UNIT;
-    auto tok_of = [&](int r) { return (wave + kWaves * (r / UNIT)) * UNIT + (r % UNIT); };
+    auto tok_of = [&](int r) { return (wave + NW * (r / UNIT)) * UNIT + (r % UNIT); };
     // lanes l, l ^ 8, ..., l ^ 56 hold the same head: the wave's max per head
     float mx = fmaxf(qmax, dpp<0x128>(qmax));   // row_ror:8
     {
@@ -850,7 +851,7 @@ struct WaveAttn {
 //   M = max_w m_w,  acc = sum_w 2^(m_w - M) acc_w,  l = sum_w 2^(m_w - M) l_w
 // (a wave without tokens has m_w = -inf and weight 0).  Split: (acc, M, l)
 // go to the partition's workspace slot; single pass: out = acc / l.
-template <int DT, int D, int GT, bool SPLIT>
+template <int DT, int D, int GT, bool SPLIT, int NW = kWaves>
 __device__ __forceinline__ void combine_waves(const AttnParams& p,
                                               float (&acc)[GT][Tile<D, GT, kNarrow<GT>>::VW],
                                               const float (&m_w)[GT], const float (&l_w)[GT],
@@ -861,8 +862,8 @@ __device__ __forceinline__ void combine_waves(const AttnParams& p,
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int vrow = lane / VL, vcol = lane % VL;
-  float* wmax = red + kWaves * GT * D;   // [kWaves][GTP]
-  float* wsum = wmax + kWaves * GTP;     // [kWaves][GTP]
+  float* wmax = red + NW * GT * D;   // [NW][GTP]
+  float* wsum = wmax + NW * GTP;     // [NW][GTP]
   // one head at a time: the scheduler would otherwise copy all GT * 8 values
   // before the first swap and hold twice the accumulators
 #pragma unroll
@@ -889,20 +890,20 @@ __device__ __forceinline__ void combine_waves(const AttnParams& p,
 
   // one float4 of one head per thread: GT * D / 4 <= 256 items, one pass
   constexpr int C4 = D / 4;
-  for (int idx = tid; idx < GT * C4; idx += kThreads) {
+  for (int idx = tid; idx < GT * C4; idx += (64 * NW)) {
     const int hh = idx / C4;
     const int c = idx - hh * C4;
     if (hh >= nact) break;
-    float mw[kWaves], M = -__builtin_inff();
+    float mw[NW], M = -__builtin_inff();
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
+    for (int w = 0; w < NW; ++w) {
       mw[w] = wmax[w * GTP + hh];
       M = fmaxf(M, mw[w]);
     }
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
     float lt = 0.f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
+    for (int w = 0; w < NW; ++w) {
       const float wt = fast_exp2(mw[w] - M);
       lt += wt * wsum[w * GTP + hh];
       const float4 r = *reinterpret_cast<const float4*>(red + (w * GT + hh) * D + c * 4);
@@ -930,16 +931,48 @@ __device__ __forceinline__ void combine_waves(const AttnParams& p,
   }
 }
 
-// Single-pass decode ("v1"): workgroup = (KV head x head chunk, sequence); it
-// walks the whole context in chunks of p.chunk tokens, each wave keeping its
-// own running max / sum / accumulator across chunks (rescaled by alpha),
-// and writes the normalised output.
-template <int DT, int D, int GT, bool Q8>
-__global__ __launch_bounds__(kThreads) void single_kernel(AttnParams p) {
-  using W = WaveAttn<DT, D, GT, Q8>;
+// Single-pass decode ("v1"): workgroup = (KV head x head chunk, sequence) of
+// NW waves; it walks the whole context in chunks of p.chunk tokens, each wave
+// keeping its own running max / sum / accumulator across chunks (rescaled by
+// alpha), and writes the normalised output.
+//
+// Longest context first: with up to one sequence per thread, grid row k
+// serves the sequence of rank k by decreasing context length (ties by
+// index), computed by every workgroup from the lengths (one per thread, ranks
+// by counting).  Workgroups start in grid order, so the long contexts, whose
+// workgroups set the end of the launch, start in the first wave of residency
+// and the short ones fill the slots freed late (LLaMA-13B-shaped layer, 32
+// sequences of 128..2048 tokens, 4 waves: 136.5 -> 113.2 us).  With more
+// sequences than threads the grid keeps index order.
+template <int DT, int D, int GT, bool Q8, int NW>
+__global__ __launch_bounds__(64 * NW) void single_kernel(AttnParams p) {
+  constexpr int NT = 64 * NW;
+  using W = WaveAttn<DT, D, GT, Q8, NW>;
   extern __shared__ float lds[];
+  __shared__ __attribute__((aligned(16))) int s_len[NT];
+  __shared__ __attribute__((aligned(16))) int s_ord[NT];
   const int kvhc = blockIdx.x;
-  const int seq = blockIdx.y;
+  int seq = blockIdx.y;
+  if (p.num_seqs <= NT) {                    // uniform
+    const int t = threadIdx.x;
+    const int cap = p.mb * p.block_size;
+    const int Lt = t < p.num_seqs ? max(0, min(p.context_lens[t], cap)) : -1;
+    s_len[t] = Lt;                                 // -1 past the batch: ranks below all
+    __syncthreads();
+    int rank = 0;
+    const int4* l4 = reinterpret_cast<const int4*>(s_len);
+    for (int j4 = 0; j4 < (p.num_seqs + 3) / 4; ++j4) {
+      const int4 v = l4[j4];
+      const int j = 4 * j4;
+      rank += (v.x > Lt) || (v.x == Lt && j < t);
+      rank += (v.y > Lt) || (v.y == Lt && j + 1 < t);
+      rank += (v.z > Lt) || (v.z == Lt && j + 2 < t);
+      rank += (v.w > Lt) || (v.w == Lt && j + 3 < t);
+    }
+    if (t < p.num_seqs) s_ord[rank] = t;           // a permutation of 0 .. S - 1
+    __syncthreads();
+    seq = s_ord[blockIdx.y];
+  }
   const int kvh = kvhc / p.head_chunks;
   const int hc = kvhc - kvh * p.head_chunks;
   const int head0 = kvh * p.group + hc * GT;
@@ -951,7 +984,7 @@ __global__ __launch_bounds__(kThreads) void single_kernel(AttnParams p) {
   if (L == 0) {                                    // uniform: whole workgroup
     uint16_t* out = static_cast<uint16_t*>(p.out);
     for (int hh = 0; hh < nact; ++hh)
-      for (int d = threadIdx.x; d < D; d += kThreads) out[(row0 + hh) * D + d] = 0;
+      for (int d = threadIdx.x; d < D; d += NT) out[(row0 + hh) * D + d] = 0;
     return;
   }
 
@@ -991,7 +1024,7 @@ __global__ __launch_bounds__(kThreads) void single_kernel(AttnParams p) {
     w.template values<kDepthSingle>(acc, vb, s);
     wave_lds_sync();                               // the next chunk rewrites this wave's rows
   }
-  combine_waves<DT, D, GT, false>(p, acc, m_run, l_run, lds + static_cast<size_t>(p.chunk) * W::GTP,
+  combine_waves<DT, D, GT, false, NW>(p, acc, m_run, l_run, lds + static_cast<size_t>(p.chunk) * W::GTP,
                                   row0, nact, 0);
 }
 
@@ -1218,17 +1251,19 @@ template <int DT, int D, int GT, bool Q8>
 int launch_attn_gt(int kind, const AttnParams& p, hipStream_t stream, hipEvent_t start,
                    hipEvent_t stop) {
   using TL = Tile<D, GT, kNarrow<GT>>;
-  const dim3 block(kThreads);
   const int nkv = p.num_kv_heads * p.head_chunks;
   if (kind == 0) {
-    const size_t lds = lds_floats(D, GT, TL::GTP, p.chunk) * sizeof(float);
+    constexpr int NW = kWavesSingle;
+    const size_t lds = lds_floats(D, GT, TL::GTP, p.chunk, NW) * sizeof(float);
     const dim3 grid(nkv, p.num_seqs, 1);
-    hipExtLaunchKernelGGL((single_kernel<DT, D, GT, Q8>), grid, block, lds, stream, start, stop, 0, p);
+    hipExtLaunchKernelGGL((single_kernel<DT, D, GT, Q8, NW>), grid, dim3(64 * NW), lds, stream,
+                          start, stop, 0, p);
   } else {
     const size_t lds = lds_floats(D, GT, TL::GTP, p.chunk) * sizeof(float);
     const dim3 grid = p.work_items ? dim3(((p.num_work_items + 7) / 8) * 8 * nkv, 1, 1)
                                    : dim3(p.grid_parts, nkv, p.num_seqs);
-    hipExtLaunchKernelGGL((split_kernel<DT, D, GT, Q8>), grid, block, lds, stream, start, stop, 0, p);
+    hipExtLaunchKernelGGL((split_kernel<DT, D, GT, Q8>), grid, dim3(kThreads), lds, stream, start,
+                          stop, 0, p);
   }
   return static_cast<int>(hipGetLastError());
 }

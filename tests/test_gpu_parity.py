@@ -173,6 +173,33 @@ def test_edge_lengths(Hq, Hkv, D, bs, dtype):
     free_gpu()
 
 
+@pytest.mark.parametrize("S", [512, 513, 700])
+def test_single_pass_order_by_length(S):
+    """The single-pass grid serves sequences longest first when there are no
+    more of them than threads in a workgroup (512) and in index order above
+    that: both orders, with tied and zero lengths, against the oracle."""
+    rng = np.random.default_rng(1000 + S)
+    lens = rng.integers(1, 97, S)
+    lens[: S // 3] = lens[S // 3: 2 * (S // 3)]          # many ties
+    s = spec(1, "full", num_seqs=S, num_q_heads=4, num_kv_heads=2, head_dim=64, block_size=16,
+             dtype="f16", fixed_lengths=tuple(int(x) for x in lens), num_blocks=0, seed=S)
+    w = make_workload(s)
+    zero = rng.random(S) < 0.1                            # these report no tokens
+    label = f"single order S={S}"
+    print(f"\n[{label}] zeros={int(zero.sum())} max={int(lens.max())}", flush=True)
+    g = gpu_side.build(w)
+    o = oracle_side.build(w)
+    ref32, refT = oracle.decode(o.q, o.key_cache, o.value_cache, o.block_tables, o.context_lens,
+                                w.scale, w.dtype, nthreads=ORACLE_THREADS)
+    g.step.context_lens[torch.from_numpy(np.flatnonzero(zero)).cuda()] = 0
+    torch.cuda.synchronize()
+    out = run_single(g, w)
+    assert np.all(out[zero] == 0), label
+    check_outputs(out[~zero], ref32[~zero], refT[~zero], w.dtype, label)
+    del g
+    free_gpu()
+
+
 def test_zero_length_and_empty_batch():
     w = workload(3, "small")
     g = gpu_side.build(w)
