@@ -336,7 +336,8 @@ pa_status pa_copy_blocks(void* key_cache, void* value_cache,
  *   max_query_len  >= every n_i (sizes the grid); a longer chunk is cut:
  *                  its first max_query_len rows are computed at their true
  *                  positions, the rest are left unwritten
- * Other arguments as for pa_decode.  Products run on the matrix cores with
+ * Other arguments as for pa_decode; block_size must be a power of two
+ * (PA_ERR_UNSUPPORTED otherwise).  Products run on the matrix cores with
  * fp32 accumulation; the softmax weights enter the P.V product as a 16-bit
  * part plus a 16-bit remainder (about 17 significant bits).  A chunk longer
  * than its context (n_i > context_lens[i]), or one whose rows fall outside

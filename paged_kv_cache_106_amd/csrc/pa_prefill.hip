@@ -23,8 +23,10 @@
 //                   result holds, in lane l, keys 4(l/16)+r of row l%16 ...
 //   online softmax  ... so each row's max and sum are a 4-lane exchange
 //                   (row swaps); keys past the row's position get weight 0
-//                   by select (only tiles that reach that far test it); the
-//                   accumulators are rescaled only when a row's max moved;
+//                   (only tiles that reach that far test it); a row's
+//                   reference max follows its running max only when that
+//                   passes it by more than 8 (in log2 units), so weights stay
+//                   below 2^8 and the accumulators are rarely rescaled;
 //   O^T += V^T P^T  v_mfma_f32_16x16x32 over 32 keys per product (A = 16 dims
 //                   of V^T, taken from the row-major V tile by the gfx950
 //                   transposing LDS read; B = P^T straight from the S^T
@@ -67,7 +69,7 @@ struct PrefillParams {
   const int32_t* query_start;  // [S + 1]
   const int32_t* seq_order;    // [S] dispatch order of the sequences, or NULL
   int32_t mb, num_seqs, num_tokens, max_query_len;
-  int32_t num_q_heads, num_kv_heads, group, block_size, num_blocks;
+  int32_t num_q_heads, num_kv_heads, group, block_size, log2_block_size, num_blocks;
   int32_t row_tiles;           // ceil(max_query_len * group / kRowsP)
   float scale_log2;
 };
@@ -152,8 +154,11 @@ __global__ __launch_bounds__(kThreadsP, 4) void prefill_kernel(PrefillParams p) 
   for (int ks = 0; ks < KS; ++ks) qb[ks] = *reinterpret_cast<const uint4*>(qp + 32 * ks);
 
   const int32_t* bt = p.block_tables + static_cast<int64_t>(seq) * p.mb;
-  const uint4* kc = static_cast<const uint4*>(p.k_cache);
-  const uint4* vc = static_cast<const uint4*>(p.v_cache);
+  const char* kbase = static_cast<const char*>(p.k_cache) + static_cast<int64_t>(kvh) * D * 2;
+  const char* vbase = static_cast<const char*>(p.v_cache) + static_cast<int64_t>(kvh) * D * 2;
+  const uint32_t tok_bytes = static_cast<uint32_t>(p.num_kv_heads) * D * 2;
+  const uint32_t blk_bytes = tok_bytes << p.log2_block_size;
+  const int bs_mask = (1 << p.log2_block_size) - 1;
   // Thread tid moves chunks c = tid + j * kThreadsP of each tile: key c / CPK,
   // dims 8 * (c % CPK) .. +8 (a wave reads whole 256-byte rows).  Its block
   // ids run one tile ahead of its loads, so a tile's K/V loads never wait for
@@ -162,7 +167,7 @@ __global__ __launch_bounds__(kThreadsP, 4) void prefill_kernel(PrefillParams p) 
     const int c = tid + j * kThreadsP;
     const int key = t * kKeyTile + c / CPK;
     if (c >= CHUNKS || key >= kend) return -1;
-    const int blk = bt[key / p.block_size];
+    const int blk = bt[key >> p.log2_block_size];
     return static_cast<unsigned>(blk) < static_cast<unsigned>(p.num_blocks) ? blk : 0;
   };
   auto load_tile = [&](int t, const int (&blk)[LOADS], uint4 (&kr)[LOADS], uint4 (&vr)[LOADS]) {
@@ -173,10 +178,10 @@ __global__ __launch_bounds__(kThreadsP, 4) void prefill_kernel(PrefillParams p) 
       vr[j] = make_uint4(0, 0, 0, 0);
       if (blk[j] >= 0) {
         const int key = t * kKeyTile + c / CPK;
-        const int64_t at = ((static_cast<int64_t>(blk[j]) * p.block_size + key % p.block_size) *
-                                p.num_kv_heads + kvh) * CPK + c % CPK;
-        kr[j] = kc[at];
-        vr[j] = vc[at];
+        const uint64_t at = static_cast<uint64_t>(static_cast<uint32_t>(blk[j])) * blk_bytes +
+                            (static_cast<uint32_t>(key & bs_mask) * tok_bytes + (c % CPK) * 16);
+        kr[j] = *reinterpret_cast<const uint4*>(kbase + at);
+        vr[j] = *reinterpret_cast<const uint4*>(vbase + at);
       }
     }
   };
@@ -234,24 +239,28 @@ __global__ __launch_bounds__(kThreadsP, 4) void prefill_kernel(PrefillParams p) 
       }
     }
     __builtin_amdgcn_s_setprio(0);
-    // online softmax of the row (base 2); keys past the row's position get
-    // weight 0, tested only on tiles that reach past the wave's first row
-    float x[4 * kMT];
-    const bool masked = t * kKeyTile + kKeyTile - 1 > wave_pos_min;   // uniform
+    // online softmax of the row (base 2, logits scale * log2 e * s); keys past
+    // the row's position get weight 0, on the tiles that reach past the wave's
+    // first row only; the max is taken on the raw scores (the scale is > 0)
+    if (t * kKeyTile + kKeyTile - 1 > wave_pos_min) {          // uniform
+      asm volatile("");   // keeps this a branch (not selects on every tile)
+      const int lim = pos - t * kKeyTile - 4 * lg;             // last visible offset
+#pragma unroll
+      for (int mt = 0; mt < kMT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (16 * mt + r > lim) s[mt][r] = -__builtin_inff();
+    }
+    float tmax = s[0][0];
 #pragma unroll
     for (int mt = 0; mt < kMT; ++mt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float v = s[mt][r] * p.scale_log2;
-        x[4 * mt + r] = (masked && t * kKeyTile + 16 * mt + 4 * lg + r > pos)
-                            ? -__builtin_inff() : v;
-      }
-    float tmax = x[0];
-#pragma unroll
-    for (int k = 1; k < 4 * kMT; ++k) tmax = fmaxf(tmax, x[k]);
-    const float m_new = fmaxf(m_run, row4_max(tmax));
-    // rescale the accumulators only when some row's max moved (uniform test)
-    if (__builtin_amdgcn_ballot_w64(m_new != m_run)) {
+      for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, s[mt][r]);
+    const float m_new = fmaxf(m_run, row4_max(tmax) * p.scale_log2);
+    // the reference max moves only when a row's max passes it by more than
+    // 8 (weights stay below 256; the normalisation at the end is exact in
+    // any reference), so after the first tiles the rescale is rare
+    if (__builtin_amdgcn_ballot_w64(m_new > m_run + 8.f)) {
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 while m_run is -inf
       l_lane *= alpha;
 #pragma unroll
@@ -260,10 +269,13 @@ __global__ __launch_bounds__(kThreadsP, 4) void prefill_kernel(PrefillParams p) 
     }
     float pr[4 * kMT];
 #pragma unroll
-    for (int k = 0; k < 4 * kMT; ++k) {
-      pr[k] = __builtin_amdgcn_exp2f(x[k] - m_run);   // exp2(-inf) = 0
-      l_lane += pr[k];
-    }
+    for (int mt = 0; mt < kMT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        // exp2(-inf) = 0
+        pr[4 * mt + r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mt][r], p.scale_log2, -m_run));
+        l_lane += pr[4 * mt + r];
+      }
     __builtin_amdgcn_s_setprio(1);
     // O^T += V^T P^T on 16x16x32 products: k-step ks takes the 32 keys of
     // S^T tiles 2ks and 2ks + 1, ordered so that lane group lg's 8 k values
@@ -341,6 +353,8 @@ extern "C" pa_status pa_prefill(void* out, const void* query, const void* key_ca
     return fail(PA_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
   if (block_size <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0)
     return fail(PA_ERR_INVALID_ARG, "block_size, num_blocks, max_blocks_per_seq must be positive");
+  if ((block_size & (block_size - 1)) != 0)
+    return fail(PA_ERR_UNSUPPORTED, "block_size must be a power of two");
   if (static_cast<int64_t>(max_blocks_per_seq) * block_size > INT32_MAX)
     return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq * block_size overflows int32");
   if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale is not finite");
@@ -381,6 +395,7 @@ extern "C" pa_status pa_prefill(void* out, const void* query, const void* key_ca
   p.num_kv_heads = num_kv_heads;
   p.group = static_cast<int32_t>(group);
   p.block_size = block_size;
+  p.log2_block_size = __builtin_ctz(static_cast<unsigned>(block_size));
   p.num_blocks = num_blocks;
   p.row_tiles = static_cast<int32_t>(row_tiles);
   p.scale_log2 = scale * 1.4426950408889634f;

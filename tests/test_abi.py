@@ -279,6 +279,15 @@ def test_partitioned_rejects_head_rows_the_merge_cannot_address():
     assert decode_part(Hq=32768, Hkv=4096, items=BAD, nitems=0) == _native.PA_ERR_INVALID_ARG
 
 
+def test_prefill_rejects_block_sizes_that_are_not_powers_of_two():
+    """The prefill kernel addresses pool rows with shifts: a block size that
+    is not a power of two is refused before any device call."""
+    st = L.pa_prefill(BAD, BAD, BAD, BAD, BAD, 8, BAD, BAD, None, 2, 8, 4, 8, 2, 128, 24, 10,
+                      0.088, 1, None, None, None)
+    assert st == _native.PA_ERR_UNSUPPORTED
+    assert "power of two" in L.pa_last_error().decode()
+
+
 def test_noalloc_decode_rejects_oversized_workspaces_on_host():
     """The no-allocation decode serves workspaces up to its scratch array's
     size; a larger request is refused before any device call."""
