@@ -1153,17 +1153,21 @@ __global__ __launch_bounds__(kThreads) void split_kernel(AttnParams p) {
 //   M = max_p m_p,  w_p = 2^(m_p - M),  out = sum_p w_p acc_p / sum_p w_p l_p
 // Lane j holds the max and sum of partitions j, j + 64, ...; the partials'
 // float4 columns are read PER partitions per load (lane: column lane % C4,
-// partition k0 + lane / C4 + PER * r), up to 64 partitions in one round
-// trip, requested together with the maxima before M is known.  A partition's
+// partition k0 + lane / C4 + PER * r), ROWS partitions (16 or 64) per round
+// trip, the first batch requested together with the maxima before M is
+// known.  ROWS = 16 serves launches of up to 16 partitions per sequence with
+// a quarter of the registers, so more of their (sequence, head) waves are
+// resident at once.  A partition's
 // weight is its max minus M from the lane that loaded it (ds_bpermute).  One
 // wave per workgroup: every workgroup of a decode is resident at once and no
 // barrier is needed.
-template <int DT, int D>
+template <int DT, int D, int ROWS>
 __global__ __launch_bounds__(64) void merge_wave_kernel(AttnParams p) {
   using F = Fmt<DT>;
   constexpr int C4 = D / 4;            // float4 columns of one partial
   constexpr int PER = 64 / C4;         // partitions per load (2 for D 128, 4 for D 64)
-  constexpr int R = 64 / PER;          // loads per lane for 64 partitions
+  constexpr int R = ROWS / PER;        // loads per lane for ROWS partitions
+  static_assert(ROWS % PER == 0 && ROWS <= 64, "batch of whole loads");
   const int lane = threadIdx.x;
   const int pair = blockIdx.x;
   const int seq = pair / p.num_q_heads;
@@ -1182,12 +1186,12 @@ __global__ __launch_bounds__(64) void merge_wave_kernel(AttnParams p) {
   const float* pm = p.part_max + base;
   const float* ps = p.part_sum + base;
   const int col = lane % C4, row = lane / C4;
-  // a batch of 64 accumulator rows k0 .. k0 + 63 of the (seq, head) through
-  // one buffer resource: row k0 + j at byte j * Hq * D * 4, this lane's float4
-  // at col * 16.  The resource ends after row np - 1, so the loads of rows
-  // past it fetch nothing and return zeros (the bound applies to the per-lane
-  // offset, which therefore carries the row).  The host keeps 64 rows under
-  // 2 GiB (Hq * D < 2^23).
+  // a batch of ROWS accumulator rows k0 .. k0 + ROWS - 1 of the (seq, head)
+  // through one buffer resource: row k0 + j at byte j * Hq * D * 4, this
+  // lane's float4 at col * 16.  The resource ends after row np - 1, so the
+  // loads of rows past it fetch nothing and return zeros (the bound applies
+  // to the per-lane offset, which therefore carries the row).  The host keeps
+  // 64 rows under 2 GiB (Hq * D < 2^23).
   const uint32_t row_bytes = static_cast<uint32_t>(ks) * D * 4;
   const uint32_t voff = static_cast<uint32_t>(row) * row_bytes + col * 16;
 
@@ -1195,7 +1199,7 @@ __global__ __launch_bounds__(64) void merge_wave_kernel(AttnParams p) {
   auto load_batch = [&](int k0) {
     const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(
         p.part_acc + (base + static_cast<int64_t>(k0) * ks) * D, 0,
-        static_cast<int>(min(np - k0, 64) * row_bytes), 0x00020000);
+        static_cast<int>(min(np - k0, ROWS) * row_bytes), 0x00020000);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const auto v = __builtin_amdgcn_raw_buffer_load_b128(
@@ -1216,9 +1220,9 @@ __global__ __launch_bounds__(64) void merge_wave_kernel(AttnParams p) {
   const float lt = wave_sum_all(lloc);
 
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int k0 = 0; k0 < np; k0 += 64) {
+  for (int k0 = 0; k0 < np; k0 += ROWS) {
     float wl = w0;                                 // weights of partitions k0 + lane
-    if (k0 > 0) {                                  // uniform: only past 64 partitions
+    if (k0 > 0) {                                  // uniform: only past ROWS partitions
       load_batch(k0);
       wl = k0 + lane < np ? fast_exp2(pm[(k0 + lane) * ks] - M) : 0.f;
     }
@@ -1274,7 +1278,10 @@ int launch_attn(int kind, const AttnParams& p, hipStream_t stream, hipEvent_t st
                 hipEvent_t stop) {
   if (kind == 2) {
     const dim3 grid(p.num_seqs * p.num_q_heads);
-    hipExtLaunchKernelGGL((merge_wave_kernel<DT, D>), grid, dim3(64), 0, stream, start, stop, 0, p);
+    if (p.num_parts <= 16)
+      hipExtLaunchKernelGGL((merge_wave_kernel<DT, D, 16>), grid, dim3(64), 0, stream, start, stop, 0, p);
+    else
+      hipExtLaunchKernelGGL((merge_wave_kernel<DT, D, 64>), grid, dim3(64), 0, stream, start, stop, 0, p);
     return static_cast<int>(hipGetLastError());
   }
   switch (p.heads_per_wg) {
