@@ -251,7 +251,8 @@ def recorded_traffic(config_id, block_size, int8=False):
     names = {(2, False): "decode_llama13b_mha_32seq_pmc.md",
              (3, False): "decode_qwen25_7b_gqa_64seq_pmc.md",
              (3, True): "decode_qwen25_7b_gqa_64seq_int8_pmc.md",
-             (4, False): "decode_7b_gqa_longctx_16seq_pmc.md"}
+             (4, False): "decode_7b_gqa_longctx_16seq_pmc.md",
+             (5, False): "decode_continuous_batch_256seq_pmc.md"}
     name = names.get((config_id, int8)) if block_size in (None, 16) else None
     return traffic_from_profile(name, "decode") if name else None
 
