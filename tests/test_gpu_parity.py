@@ -173,6 +173,36 @@ def test_edge_lengths(Hq, Hkv, D, bs, dtype):
     free_gpu()
 
 
+MERGE_CASES = [(16, 128, "bf16"), (17, 128, "bf16"), (64, 128, "bf16"), (65, 128, "bf16"),
+               (130, 128, "bf16"), (16, 64, "f16"), (65, 64, "f16")]
+
+
+@pytest.mark.parametrize("parts,D,dtype", MERGE_CASES,
+                         ids=[f"{a}parts-d{b}-{c}" for a, b, c in MERGE_CASES])
+def test_merge_batches(parts, D, dtype):
+    """The merge reads a sequence's partials in batches: 16 at a time when the
+    launch has at most 16 partitions per sequence, else 64.  Contexts of
+    exactly 16, 17, 64, 65 and 130 partitions of 16 tokens (and shorter
+    neighbours) cross both batch sizes and the batch boundaries; every output
+    against the oracle, work list and dense grid."""
+    P = 16
+    top = parts * P
+    lens = (top, top - 1, top - P + 1, max(1, top - 40 * P), 1, P + 1)
+    s = spec(1, "full", num_seqs=len(lens), num_q_heads=8, num_kv_heads=2, head_dim=D,
+             block_size=16, dtype=dtype, fixed_lengths=lens, num_blocks=0, seed=parts + D)
+    w = make_workload(s)
+    label = f"merge {parts} partitions D{D} {dtype}"
+    print(f"\n[{label}] lens={list(lens)}", flush=True)
+    g = gpu_side.build(w)
+    o = oracle_side.build(w)
+    ref32, refT = oracle.decode(o.q, o.key_cache, o.value_cache, o.block_tables, o.context_lens,
+                                w.scale, w.dtype, nthreads=ORACLE_THREADS)
+    check_outputs(run_partitioned(g, w, P), ref32, refT, w.dtype, label + " dense")
+    check_outputs(run_partitioned(g, w, P, listed=True), ref32, refT, w.dtype, label + " listed")
+    del g
+    free_gpu()
+
+
 @pytest.mark.parametrize("S", [512, 513, 700])
 def test_single_pass_order_by_length(S):
     """The single-pass grid serves sequences longest first when there are no
