@@ -7,28 +7,31 @@
 // KV head (G = Hq / Hkv, "LLM推理优化技术地图", §2.3 GQA) are served by the
 // same workgroup, so every K/V byte is read from HBM once for all of them.
 //
-// Workgroup = 4 waves = 256 lanes, one (sequence, KV head, head chunk[,
-// partition]).  Its tokens are cut into units of 16 and wave w takes units
-// w, w+4, ...; each wave runs its own softmax over its units, chunk by chunk
-// (the partition for the split kernel), in three phases:
+// Workgroup = NW waves (4 for the split kernel, 8 for the single-pass one),
+// one (sequence, KV head, head chunk[, partition]).  Its tokens are cut into
+// units of 16 and wave w takes units w, w + NW, ...; each wave runs its own
+// softmax over its units, chunk by chunk (the partition for the split
+// kernel), in three phases:
 //
 //  1. logits.  8 lanes per token (16 for groups of 5 or more heads, the
 //     narrow layout), each holding 16-byte pieces of the K row
 //     (buffer_load_dwordx4), take partial dot products with the matching q
 //     elements of every head of the group (v_dot2 on 16-bit pairs, fp32
-//     accumulate); a 3- or 4-step DPP sum finishes each dot product and the
-//     raw logits go to the wave's rows of LDS.
-//  2. softmax.  The wave scales them into the base-2 domain (scale * log2 e),
-//     takes its max per head, overwrites them with p = 2^(logit - max) and
-//     sums them.
+//     accumulate); a DPP reduce-scatter over each 8-lane group leaves every
+//     lane the finished dot product of one head, and the lanes that own a
+//     head store its logit, already in the base-2 domain
+//     (scale * log2 e * q.k), to the wave's rows of LDS and keep a running
+//     max of it.
+//  2. softmax.  The wave takes its max per head from those running maxima,
+//     overwrites the logits with p = 2^(logit - max) and sums them.
 //  3. P.V.  D/8 lanes per token, each holding 8 consecutive dims of the V
 //     row (D/4 lanes with 4 dims in the narrow layout), accumulate p * V for
 //     every head in fp32 registers.
 //
 // K and V stream through a ring of unit buffers per wave, every refill
 // issued on every path so that the wait counts track the ring.  At the end
-// the four waves' (max, sum, acc) meet in LDS and combine with the
-// log-sum-exp identity.  The single-pass kernel ("v1") keeps each wave's
+// the waves' (max, sum, acc) meet in LDS and combine with the log-sum-exp
+// identity.  The single-pass kernel ("v1") keeps each wave's
 // running max / sum / accumulator across chunks (rescaled by
 // 2^(old max - new max)) and writes the normalised output; the split kernel
 // ("v2") stores (max, sum, acc) of its partition and the merge kernel
@@ -37,8 +40,8 @@
 // Loads use a wave-uniform block base and per-lane 32-bit offsets, with the
 // non-temporal cache policy (each K/V byte is read once).  A wave's
 // block ids arrive in one vector load (lane i: its unit i) and are read back
-// with readlane; tail tokens of the last block are masked by select (the
-// pools' unused slots may hold NaN).
+// with readlane; the tail tokens of a span's last unit get logit -inf and V
+// zero (the pools' unused slots may hold NaN).
 //
 // INT8 pools (Q8): the pools hold one signed byte per element and the rows'
 // fp32 scales sit in [NB][Hkv][bs] arrays (a row dequantises to scale x
