@@ -562,12 +562,21 @@ int32_t pa_alloc_refcount(const pa_allocator* a, int32_t block_id);
 
 /* Work list for pa_decode_partitioned from the host's context lengths:
  * every live (sequence, partition) pair of partition_size tokens (at most
- * max_parts per sequence; max_parts < 0: no limit), full partitions first in
- * sequence order, then each sequence's ragged last partition, longest first
- * (ties in sequence order), so the shortest work fills the end of the
- * launch.  Splitting the context into partitions follows the split-context
- * ("v2") kernel of "LLM推理优化：vLLM PagedAttention深度解析与工程实践", §4.1;
- * the order is this library's scheduling choice.
+ * max_parts per sequence; max_parts < 0: no limit), each exactly once.
+ * Order: the decode runs list position i on XCD i % 8, so the pairs are
+ * dealt to 8 queues, one per XCD.  With N pairs in all, each sequence is
+ * cut into runs of at most ceil(N / 8) consecutive partitions (one run for
+ * all but the longest contexts); runs go longest first (in tokens; ties in
+ * sequence order) to the queue holding the fewest tokens so far (ties: the
+ * lowest queue).  A queue lists its full partitions in that order, then its
+ * ragged ones longest first (ties in that order), so the shortest work ends
+ * the launch.  The output reads the queues round-robin: position 8j + x is
+ * queue x's item j while every queue has one; after that the queues still
+ * holding items take turns in the same order.  A sequence's partitions
+ * thus run on one XCD and share its L2.  Splitting the context into
+ * partitions follows the split-context ("v2") kernel of
+ * "LLM推理优化：vLLM PagedAttention深度解析与工程实践", §4.1; the order is
+ * this library's scheduling choice.
  *   context_lens  [num_seqs] int32, host memory
  *   items_out     [capacity][2] int32, host memory: (sequence, partition)
  * *n_out = the number of items; PA_ERR_INVALID_ARG if it exceeds capacity

@@ -489,42 +489,82 @@ pa_status pa_partition_work_items(const int32_t* context_lens, int32_t num_seqs,
   if (!n_out || num_seqs < 0 || partition_size <= 0 || capacity < 0 ||
       (num_seqs > 0 && !context_lens) || (capacity > 0 && !items_out))
     return invalid("pa_partition_work_items: bad argument");
-  struct Ragged {
-    int32_t ntok, seq, part;
+  // The decode's work-list grid runs item i on XCD i % 8 (workgroups go to
+  // the XCDs round-robin by id; the KV heads of an item share its XCD).  The
+  // partitions are dealt to one queue per XCD by whole sequences, longest
+  // first, each to the queue holding the fewest tokens so far; a sequence
+  // with more than an eighth of all partitions is cut into runs of that many
+  // so that one long context still spreads over every XCD.  A sequence's
+  // partitions thus share one XCD's L2 (its query rows and block-table row)
+  // and write one contiguous range of partials there.  Each queue lists its
+  // full partitions, then its ragged last partitions longest first, so the
+  // shortest work ends the launch.  The queues interleave (queue x at
+  // positions 8j + x) while every queue has items left; the rest follow in
+  // the same round-robin order, no longer pinned.
+  constexpr int kQueues = 8;
+  struct Item {
+    int32_t seq, part, ntok;
   };
-  std::vector<Ragged> ragged;
-  ragged.reserve(static_cast<size_t>(num_seqs));
+  struct Run {
+    int64_t tokens;
+    int32_t seq, p0, p1;
+  };
+  std::vector<int32_t> nparts(static_cast<size_t>(num_seqs), 0);
   int64_t n = 0;
-  // full partitions, sequence-major; the ragged last ones are set aside
   for (int32_t i = 0; i < num_seqs; ++i) {
     const int64_t L = context_lens[i];
     if (L <= 0) continue;
     int64_t np = (L + partition_size - 1) / partition_size;
     if (max_parts >= 0 && np > max_parts) np = max_parts;
-    for (int64_t p = 0; p < np; ++p) {
-      const int64_t ntok = std::min<int64_t>(partition_size, L - p * partition_size);
-      if (ntok < partition_size) {
-        ragged.push_back({static_cast<int32_t>(ntok), i, static_cast<int32_t>(p)});
-        continue;
-      }
-      if (n < capacity) {
-        items_out[2 * n] = i;
-        items_out[2 * n + 1] = static_cast<int32_t>(p);
-      }
-      ++n;
-    }
-  }
-  // then the ragged ones, longest first (ties in sequence order)
-  std::stable_sort(ragged.begin(), ragged.end(),
-                   [](const Ragged& x, const Ragged& y) { return x.ntok > y.ntok; });
-  for (const Ragged& r : ragged) {
-    if (n < capacity) {
-      items_out[2 * n] = r.seq;
-      items_out[2 * n + 1] = r.part;
-    }
-    ++n;
+    nparts[static_cast<size_t>(i)] = static_cast<int32_t>(np);
+    n += np;
   }
   if (n > INT32_MAX) return invalid("pa_partition_work_items: too many items");
+  const int64_t quota = std::max<int64_t>(1, (n + kQueues - 1) / kQueues);
+  std::vector<Run> runs;
+  for (int32_t i = 0; i < num_seqs; ++i) {
+    const int64_t L = context_lens[i];
+    for (int64_t p0 = 0; p0 < nparts[static_cast<size_t>(i)]; p0 += quota) {
+      const int64_t p1 = std::min<int64_t>(nparts[static_cast<size_t>(i)], p0 + quota);
+      runs.push_back({std::min<int64_t>(L, p1 * partition_size) - p0 * partition_size, i,
+                      static_cast<int32_t>(p0), static_cast<int32_t>(p1)});
+    }
+  }
+  // longest first; ties keep sequence order
+  std::stable_sort(runs.begin(), runs.end(),
+                   [](const Run& x, const Run& y) { return x.tokens > y.tokens; });
+  std::vector<Item> full[kQueues], ragged[kQueues];
+  int64_t load[kQueues] = {};
+  for (const Run& r : runs) {
+    int x = 0;
+    for (int k = 1; k < kQueues; ++k)
+      if (load[k] < load[x]) x = k;
+    load[x] += r.tokens;
+    const int64_t L = context_lens[r.seq];
+    for (int32_t p = r.p0; p < r.p1; ++p) {
+      const int32_t ntok =
+          static_cast<int32_t>(std::min<int64_t>(partition_size, L - int64_t{p} * partition_size));
+      (ntok == partition_size ? full[x] : ragged[x]).push_back({r.seq, p, ntok});
+    }
+  }
+  size_t longest = 0;
+  for (int x = 0; x < kQueues; ++x) {
+    std::stable_sort(ragged[x].begin(), ragged[x].end(),
+                     [](const Item& a, const Item& b) { return a.ntok > b.ntok; });
+    full[x].insert(full[x].end(), ragged[x].begin(), ragged[x].end());
+    longest = std::max(longest, full[x].size());
+  }
+  int64_t k = 0;
+  auto emit = [&](const Item& it) {
+    if (k < capacity) {
+      items_out[2 * k] = it.seq;
+      items_out[2 * k + 1] = it.part;
+    }
+    ++k;
+  };
+  for (size_t j = 0; j < longest; ++j)   // once a queue runs out, the rest shift
+    for (int x = 0; x < kQueues; ++x)
+      if (j < full[x].size()) emit(full[x][j]);
   *n_out = static_cast<int32_t>(n);
   if (n > capacity) return invalid("pa_partition_work_items: output too small");
   return PA_OK;

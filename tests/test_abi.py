@@ -117,16 +117,48 @@ def test_partitioned_rejects_on_host(kw, status):
 
 def test_partition_work_items():
     wl = pa.partition_work_items([1, 1024, 1025, 0, 512, 700], 512)
-    # full partitions first (sequence-major), then ragged ones by decreasing length
-    assert wl.tolist() == [[1, 0], [1, 1], [2, 0], [2, 1], [4, 0], [5, 0], [5, 1], [0, 0], [2, 2]]
+    # 9 partitions: runs of at most ceil(9 / 8) = 2; longest run first to the
+    # lightest of 8 queues: seq 1 -> q0, seq 2 [0, 2) -> q1, seq 5 -> q2 (full
+    # then ragged), seq 4 -> q3, seq 0 -> q4, seq 2 [2, 3) -> q5; round-robin
+    assert wl.tolist() == [[1, 0], [2, 0], [5, 0], [4, 0], [0, 0], [2, 2], [1, 1], [2, 1], [5, 1]]
     assert pa.partition_work_items([5000], 512, max_parts=4).tolist() == [[0, p] for p in range(4)]
 
 
+def _work_list_model(lens, P, cap):
+    """Plain-Python statement of the work list's definition: runs of at most
+    ceil(N / 8) partitions per sequence, longest first (stable) to the queue
+    with the fewest tokens; per queue its full partitions, then its ragged
+    ones longest first; queues read out round-robin."""
+    nparts = [min(-(-L // P), cap) if cap is not None else -(-L // P) for L in lens]
+    nparts = [n if L > 0 else 0 for n, L in zip(nparts, lens)]
+    quota = max(1, -(-sum(nparts) // 8))
+    runs = []
+    for i, (L, n) in enumerate(zip(lens, nparts)):
+        for p0 in range(0, n, quota):
+            p1 = min(n, p0 + quota)
+            runs.append((min(L, p1 * P) - p0 * P, i, p0, p1))
+    runs.sort(key=lambda r: -r[0])
+    queues = [([], []) for _ in range(8)]
+    load = [0] * 8
+    for tok, i, p0, p1 in runs:
+        x = load.index(min(load))
+        load[x] += tok
+        for part in range(p0, p1):
+            ntok = min(P, lens[i] - part * P)
+            queues[x][0 if ntok == P else 1].append((ntok, i, part))
+    qs = [full + sorted(rag, key=lambda t: -t[0]) for full, rag in queues]
+    out = []
+    for j in range(max(len(q) for q in qs)):
+        out += [[q[j][1], q[j][2]] for q in qs if j < len(q)]
+    return out
+
+
 def test_partition_work_items_random():
-    """The library's work list against a plain-Python statement of its
-    definition, on random lengths (zeros, exact multiples, partition caps)."""
+    """The library's work list against the plain-Python statement of its
+    definition, on random lengths (zeros, exact multiples, partition caps,
+    one dominant context), and every live partition exactly once."""
     rng = np.random.default_rng(7)
-    for _ in range(300):
+    for t in range(300):
         S = int(rng.integers(0, 40))
         P = int(rng.choice([16, 32, 512, 1024]))
         lens = [int(x) for x in rng.integers(0, 4 * P, S)]
@@ -136,19 +168,32 @@ def test_partition_work_items_random():
                 lens[i] = 0
             elif r < 0.2:
                 lens[i] = P * int(rng.integers(1, 4))
+        if S and t % 5 == 0:
+            lens[0] = int(rng.integers(20, 200)) * P + int(rng.integers(0, P))
         cap = None if rng.random() < 0.5 else int(rng.integers(1, 5))
-        full, ragged = [], []
-        for i, L in enumerate(lens):
-            nparts = -(-L // P)
-            if cap is not None:
-                nparts = min(nparts, cap)
-            for part in range(nparts):
-                ntok = min(P, L - part * P)
-                (full if ntok == P else ragged).append((ntok, i, part))
-        ragged.sort(key=lambda t: -t[0])          # stable: ties keep sequence order
-        want = [[i, part] for _, i, part in full + ragged]
         got = pa.partition_work_items(np.array(lens, np.int32), P, cap)
-        assert got.tolist() == want
+        assert got.tolist() == _work_list_model(lens, P, cap)
+        live = sorted((i, p) for i, L in enumerate(lens)
+                      for p in range(min(-(-L // P), cap) if cap is not None else -(-L // P)))
+        assert sorted(map(tuple, got.tolist())) == live
+
+
+def test_work_list_pins_sequences_to_one_xcd():
+    """Balanced batch (the Qwen2.5-7B-shaped layer's 64 lengths): every
+    sequence's partitions sit at positions of one residue mod 8 except the
+    few past the shortest queue, and the 8 queues carry nearly equal tokens."""
+    from workloads import workload
+    L = workload(3, "full").lengths.astype(np.int64)
+    P = 512
+    wl = pa.partition_work_items(L.astype(np.int32), P)
+    assert len(wl) == int(((L + P - 1) // P).sum())
+    per_x = np.zeros(8)
+    res = {}
+    for pos, (s, p) in enumerate(wl.tolist()):
+        per_x[pos % 8] += min(P, L[s] - p * P)
+        res.setdefault(s, set()).add(pos % 8)
+    assert sum(len(v) > 1 for v in res.values()) <= 8
+    assert per_x.max() / per_x.mean() < 1.02
 
 
 def test_workspace_size_formula():
