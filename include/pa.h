@@ -560,6 +560,11 @@ int32_t pa_alloc_num_free(const pa_allocator* a);
 /* Reference count of a physical block, or -1 for an invalid id. */
 int32_t pa_alloc_refcount(const pa_allocator* a, int32_t block_id);
 
+/* Blocks held by two or more sequences (reference count >= 2: shared
+ * prefixes, forks, prefix-cache hits), or -1 for a NULL allocator.  Kept
+ * current by every call that changes a reference count. */
+int32_t pa_alloc_num_shared_blocks(const pa_allocator* a);
+
 /* Work list for pa_decode_partitioned from the host's context lengths:
  * every live (sequence, partition) pair of partition_size tokens (at most
  * max_parts per sequence; max_parts < 0: no limit), each exactly once.

@@ -95,6 +95,7 @@ _sig("pa_alloc_slots", _i32, [_vp, _i64, _i32, _i32, _i64p])
 _sig("pa_alloc_num_tokens", _i32, [_vp, _i64])
 _sig("pa_alloc_num_free", _i32, [_vp])
 _sig("pa_alloc_refcount", _i32, [_vp, _i32])
+_sig("pa_alloc_num_shared_blocks", _i32, [_vp])
 _sig("pa_alloc_free_list", _i32, [_vp, _i32p, _i32, _i32p])
 _sig("pa_partition_work_items", _i32, [_vp, _i32, _i32, _i32, _vp, _i32, _i32p])
 
@@ -576,6 +577,9 @@ class Allocator:
 
     def refcount(self, block_id):
         return int(_lib.pa_alloc_refcount(self._h, int(block_id)))
+
+    def num_shared_blocks(self):
+        return int(_lib.pa_alloc_num_shared_blocks(self._h))
 
     def free_list(self):
         n = ctypes.c_int32()

@@ -49,6 +49,7 @@ struct pa_allocator {
   int32_t head = -1, tail = -1;
   int64_t count = 0;                // ids in the pool
   std::vector<int32_t> refcount;
+  int64_t shared = 0;               // blocks with refcount >= 2
   struct Seq {
     std::vector<int32_t> blocks;
     int32_t tokens = 0;
@@ -144,6 +145,13 @@ struct pa_allocator {
     if (have >= n) return 0;
     return (n - have + block_size - 1) / block_size;
   }
+  // every refcount change goes through here, keeping `shared` current
+  void set_ref(int32_t id, int32_t v) {
+    int32_t& rc = refcount[static_cast<size_t>(id)];
+    shared += static_cast<int64_t>(v > 1) - static_cast<int64_t>(rc > 1);
+    rc = v;
+  }
+  int32_t ref(int32_t id) const { return refcount[static_cast<size_t>(id)]; }
   // does one more token of s need a block from the pool (new or copy-on-write)?
   bool append_needs_block(const Seq* s) const {
     if (!s) return true;
@@ -160,13 +168,13 @@ struct pa_allocator {
     int32_t src = -1, dst = -1;
     if (idx >= s.blocks.size()) {
       const int32_t id = pop_front();
-      refcount[static_cast<size_t>(id)] = 1;
+      set_ref(id, 1);
       s.blocks.push_back(id);
     } else if (refcount[static_cast<size_t>(s.blocks[idx])] > 1) {
       src = s.blocks[idx];
       dst = pop_front();
-      refcount[static_cast<size_t>(src)] -= 1;
-      refcount[static_cast<size_t>(dst)] = 1;
+      set_ref(src, ref(src) - 1);
+      set_ref(dst, 1);
       s.blocks[idx] = dst;
     }
     s.tokens = static_cast<int32_t>(p + 1);
@@ -234,7 +242,7 @@ pa_status pa_alloc_allocate(pa_allocator* a, int64_t seq_id, int32_t num_tokens)
   pa_allocator::Seq& seq = a->seqs[seq_id];
   for (int64_t k = 0; k < need; ++k) {
     const int32_t id = a->pop_front();
-    a->refcount[static_cast<size_t>(id)] = 1;
+    a->set_ref(id, 1);
     seq.blocks.push_back(id);
   }
   if (num_tokens > seq.tokens) seq.tokens = num_tokens;
@@ -290,7 +298,7 @@ pa_status pa_alloc_share_prefix(pa_allocator* a, int64_t src_seq, int64_t dst_se
     return invalid("pa_alloc_share_prefix: prefix must be block-aligned and within the source");
   const size_t nblk = static_cast<size_t>(num_tokens / a->block_size);
   std::vector<int32_t> blocks(s->blocks.begin(), s->blocks.begin() + static_cast<long>(nblk));
-  for (int32_t id : blocks) a->refcount[static_cast<size_t>(id)] += 1;
+  for (int32_t id : blocks) a->set_ref(id, a->ref(id) + 1);
   pa_allocator::Seq& d = a->seqs[dst_seq];
   d.blocks = std::move(blocks);
   d.tokens = num_tokens;
@@ -304,7 +312,7 @@ pa_status pa_alloc_fork(pa_allocator* a, int64_t src_seq, int64_t dst_seq) {
   if (!s) return invalid("pa_alloc_fork: unknown source sequence");
   if (find(a, dst_seq)) return invalid("pa_alloc_fork: destination exists");
   pa_allocator::Seq copy = *s;
-  for (int32_t id : copy.blocks) a->refcount[static_cast<size_t>(id)] += 1;
+  for (int32_t id : copy.blocks) a->set_ref(id, a->ref(id) + 1);
   a->seqs[dst_seq] = std::move(copy);
   return PA_OK;
 }
@@ -319,9 +327,8 @@ pa_status pa_alloc_free(pa_allocator* a, int64_t seq_id) {
   for (size_t k = 0; k < nb; ++k) {
     // with caching on, deepest block first: a cached prefix leaves the pool end first
     const int32_t id = blocks[a->caching ? nb - 1 - k : k];
-    int32_t& rc = a->refcount[static_cast<size_t>(id)];
-    rc -= 1;
-    if (rc == 0) a->push_back(id);
+    a->set_ref(id, a->ref(id) - 1);
+    if (a->ref(id) == 0) a->push_back(id);
   }
   a->seqs.erase(it);
   return PA_OK;
@@ -385,6 +392,10 @@ int32_t pa_alloc_num_tokens(const pa_allocator* a, int64_t seq_id) {
 
 int32_t pa_alloc_num_free(const pa_allocator* a) {
   return a ? static_cast<int32_t>(a->count) : -1;
+}
+
+int32_t pa_alloc_num_shared_blocks(const pa_allocator* a) {
+  return a ? static_cast<int32_t>(a->shared) : -1;
 }
 
 int32_t pa_alloc_refcount(const pa_allocator* a, int32_t block_id) {
@@ -453,14 +464,13 @@ pa_status pa_alloc_allocate_prompt(pa_allocator* a, int64_t seq_id, const int32_
   pa_allocator::Seq& s = a->seqs[seq_id];
   s.blocks.reserve(static_cast<size_t>(nblk));
   for (int32_t b : hits) {
-    int32_t& rc = a->refcount[static_cast<size_t>(b)];
-    if (rc == 0) a->unlink(b);
-    rc += 1;
+    if (a->ref(b) == 0) a->unlink(b);
+    a->set_ref(b, a->ref(b) + 1);
     s.blocks.push_back(b);
   }
   for (int64_t k = static_cast<int64_t>(hits.size()); k < nblk; ++k) {
     const int32_t id = a->pop_front();
-    a->refcount[static_cast<size_t>(id)] = 1;
+    a->set_ref(id, 1);
     s.blocks.push_back(id);
   }
   // cache the prompt's other full blocks; a prefix cached already keeps its block

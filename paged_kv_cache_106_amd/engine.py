@@ -271,21 +271,23 @@ class DecodeStep:
         self.host_context_lens[:] = lens
 
     @staticmethod
-    def dense_grid(grid, max_parts, num_seqs, num_items, ratio):
+    def dense_grid(grid, max_parts, num_seqs, num_items, ratio, shared):
         """Whether the partitioned decode runs on its dense grid instead of
-        the work list.  The dense grid, (max_parts | 1) partitions per
-        (sequence, KV head) with empty ones exiting at once, puts partition p
-        of KV head k on XCD (p + 3k) mod 8 for every sequence, so sequences
-        that share prefix blocks read them through one XCD's L2 (~4 % faster
-        on 256 sequences sharing a 1024-token prefix); the work list has no
-        empty workgroups, which matters when one long sequence makes the
-        dense grid mostly empty.  "auto" takes the dense grid while it has at
+        the work list.  The work list has no empty workgroups and keeps each
+        sequence's partitions on one XCD.  The dense grid, (max_parts | 1)
+        partitions per (sequence, KV head) with empty ones exiting at once,
+        puts partition p of KV head k on XCD (p + 3k) mod 8 for every
+        sequence, so sequences that share prefix blocks read them through one
+        XCD's L2: with 256 sequences sharing a 1024-token prefix it is ~5 %
+        faster than the list, while without shared blocks the list is faster
+        (16 long contexts: ~1.5 %).  "auto" takes the dense grid when the
+        allocator holds shared blocks (`shared`) and the dense grid has at
         most `ratio` times the list's workgroups."""
         if grid == "dense":
             return True
         if grid == "list" or num_items <= 0:
             return False
-        return (max_parts | 1) * num_seqs <= ratio * num_items
+        return bool(shared) and (max_parts | 1) * num_seqs <= ratio * num_items
 
     def prepare(self):
         """a1: one slot per sequence from the host allocator, staged in pinned
@@ -313,7 +315,8 @@ class DecodeStep:
             fn, args = self._items_call
             pa._check(fn(*args))
             nitems = self._nitems.value
-            if self.dense_grid(self.grid, self.max_parts, self.S, nitems, self.DENSE_RATIO):
+            if self.dense_grid(self.grid, self.max_parts, self.S, nitems, self.DENSE_RATIO,
+                               self.grid == "auto" and self.cache.allocator.num_shared_blocks() > 0):
                 nitems = 0                          # no list: the decode takes the dense grid
             self.last_grid = "list" if nitems else "dense"
             self._num_items[b] = nitems

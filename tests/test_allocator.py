@@ -22,6 +22,7 @@ def same_state(a: pa.Allocator, m: BlockManagerModel):
     for b in range(m.num_blocks):
         assert a.refcount(b) == m.refcount[b]
     assert a.num_free() == len(m.free_blocks)
+    assert a.num_shared_blocks() == sum(1 for r in m.refcount if r >= 2)
 
 
 def test_worked_examples(golden_dir):

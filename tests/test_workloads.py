@@ -61,10 +61,10 @@ def test_engine_grid_choice():
     f = DecodeStep.dense_grid
     r = DecodeStep.DENSE_RATIO
     # Qwen-shaped layer (bench lengths): 57 partitions per sequence in the dense grid, 612 live
-    assert not f("auto", 56, 64, 612, r)
-    # long-context layer: every partition live (64 of 65)
-    assert f("auto", 65, 16, 1024, r)
-    # continuous batch: 11 partitions per sequence, 1212 live
-    assert f("auto", 11, 256, 1212, r)
-    assert not f("list", 11, 256, 1212, r) and f("dense", 56, 64, 612, r)
-    assert not f("auto", 11, 256, 0, r)
+    assert not f("auto", 56, 64, 612, r, False) and not f("auto", 56, 64, 612, r, True)
+    # long-context layer: every partition live (64 of 65), no shared blocks
+    assert not f("auto", 65, 16, 1024, r, False)
+    # continuous batch sharing a prefix: 11 partitions per sequence, 1212 live
+    assert f("auto", 11, 256, 1212, r, True)
+    assert not f("list", 11, 256, 1212, r, True) and f("dense", 56, 64, 612, r, False)
+    assert not f("auto", 11, 256, 0, r, True)
