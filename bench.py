@@ -200,8 +200,9 @@ def run_prefill(args):
 
 
 KERNEL_SOURCES = {
-    # the sources each kernel family is built and launched from
-    "decode": ("pa_attn*", "pa_internal.h", "pa_api.hip"),
+    # the sources each kernel family is built and launched from (for the
+    # decode also the work-list builder, which orders its workgroups)
+    "decode": ("pa_attn*", "pa_internal.h", "pa_api.hip", "pa_allocator.cpp"),
     "prefill": ("pa_prefill.hip", "pa_mfma.h", "pa_internal.h"),
 }
 
