@@ -569,13 +569,15 @@ int32_t pa_alloc_num_shared_blocks(const pa_allocator* a);
  * every live (sequence, partition) pair of partition_size tokens (at most
  * max_parts per sequence; max_parts < 0: no limit), each exactly once.
  * Order: the decode runs list position i on XCD i % 8, so the pairs are
- * dealt to 8 queues, one per XCD.  With N pairs in all, each sequence is
- * cut into runs of at most ceil(N / 8) consecutive partitions (one run for
- * all but the longest contexts); runs go longest first (in tokens; ties in
+ * dealt to 8 queues, one per XCD.  Each sequence is cut into runs of at most
+ * q consecutive partitions; runs go longest first (in tokens; ties in
  * sequence order) to the queue holding the fewest tokens so far (ties: the
- * lowest queue).  A queue lists its full partitions in that order, then its
- * ragged ones longest first (ties in that order), so the shortest work ends
- * the launch.  The output reads the queues round-robin: position 8j + x is
+ * lowest queue).  q starts at ceil(N / 8) for N pairs in all (one run for all
+ * but the longest contexts) and halves while the fullest queue holds more
+ * than 1.01x the mean tokens, down to 1; the q with the fullest queue
+ * lightest is taken (the larger q on a tie).  A queue lists its full
+ * partitions in that order, then its ragged ones longest first (ties in that
+ * order), so the shortest work ends the launch.  The output reads the queues round-robin: position 8j + x is
  * queue x's item j while every queue has one; after that the queues still
  * holding items take turns in the same order.  A sequence's partitions
  * thus run on one XCD and share its L2.  Splitting the context into

@@ -422,10 +422,11 @@ def pa_prefill(out, query, key_cache, value_cache, block_tables, context_lens, q
 def partition_work_items(context_lens, partition_size, max_parts=None, out=None):
     """Host-side work list for pa_decode_partitioned (pa_partition_work_items):
     (sequence, partition) for every live partition, dealt to one queue per
-    XCD (list position i runs on XCD i % 8) by whole sequences, longest first,
-    to the queue with the fewest tokens (contexts longer than an eighth of the
-    work are cut into runs); per queue the full partitions, then the ragged
-    ones by decreasing length; queues read out round-robin.  context_lens: int
+    XCD (list position i runs on XCD i % 8) in runs of one sequence's
+    partitions, longest first, to the queue with the fewest tokens (whole
+    sequences when that balances the queues to 1 %, shorter runs otherwise);
+    per queue the full partitions, then the ragged ones by decreasing length;
+    queues read out round-robin.  context_lens: int
     array [S].  Returns int32 [n][2] (a view of `out` if given)."""
     L = np.ascontiguousarray(context_lens, dtype=np.int32)
     if out is None:

@@ -501,13 +501,15 @@ pa_status pa_partition_work_items(const int32_t* context_lens, int32_t num_seqs,
     return invalid("pa_partition_work_items: bad argument");
   // The decode's work-list grid runs item i on XCD i % 8 (workgroups go to
   // the XCDs round-robin by id; the KV heads of an item share its XCD).  The
-  // partitions are dealt to one queue per XCD by whole sequences, longest
-  // first, each to the queue holding the fewest tokens so far; a sequence
-  // with more than an eighth of all partitions is cut into runs of that many
-  // so that one long context still spreads over every XCD.  A sequence's
-  // partitions thus share one XCD's L2 (its query rows and block-table row)
-  // and write one contiguous range of partials there.  Each queue lists its
-  // full partitions, then its ragged last partitions longest first, so the
+  // partitions are dealt to one queue per XCD in runs of consecutive
+  // partitions of one sequence, longest run first, each to the queue holding
+  // the fewest tokens so far.  Runs are whole sequences (up to an eighth of
+  // all partitions) when that balances the queues to within 1 %; otherwise
+  // the run length halves until it does (down to single partitions, where
+  // the dealing is as even as partitions allow).  A sequence's partitions
+  // thus share one XCD's L2 (its query rows and block-table row) and write
+  // one contiguous range of partials there.  Each queue lists its full
+  // partitions, then its ragged last partitions longest first, so the
   // shortest work ends the launch.  The queues interleave (queue x at
   // positions 8j + x) while every queue has items left; the rest follow in
   // the same round-robin order, no longer pinned.
@@ -520,7 +522,7 @@ pa_status pa_partition_work_items(const int32_t* context_lens, int32_t num_seqs,
     int32_t seq, p0, p1;
   };
   std::vector<int32_t> nparts(static_cast<size_t>(num_seqs), 0);
-  int64_t n = 0;
+  int64_t n = 0, total = 0;
   for (int32_t i = 0; i < num_seqs; ++i) {
     const int64_t L = context_lens[i];
     if (L <= 0) continue;
@@ -528,33 +530,57 @@ pa_status pa_partition_work_items(const int32_t* context_lens, int32_t num_seqs,
     if (max_parts >= 0 && np > max_parts) np = max_parts;
     nparts[static_cast<size_t>(i)] = static_cast<int32_t>(np);
     n += np;
+    total += std::min<int64_t>(L, np * partition_size);
   }
   if (n > INT32_MAX) return invalid("pa_partition_work_items: too many items");
-  const int64_t quota = std::max<int64_t>(1, (n + kQueues - 1) / kQueues);
   std::vector<Run> runs;
-  for (int32_t i = 0; i < num_seqs; ++i) {
-    const int64_t L = context_lens[i];
-    for (int64_t p0 = 0; p0 < nparts[static_cast<size_t>(i)]; p0 += quota) {
-      const int64_t p1 = std::min<int64_t>(nparts[static_cast<size_t>(i)], p0 + quota);
-      runs.push_back({std::min<int64_t>(L, p1 * partition_size) - p0 * partition_size, i,
-                      static_cast<int32_t>(p0), static_cast<int32_t>(p1)});
+  std::vector<int> queue_of;
+  auto deal = [&](int64_t quota) {   // runs of at most `quota` partitions -> queues; max load
+    runs.clear();
+    for (int32_t i = 0; i < num_seqs; ++i) {
+      const int64_t L = context_lens[i];
+      for (int64_t p0 = 0; p0 < nparts[static_cast<size_t>(i)]; p0 += quota) {
+        const int64_t p1 = std::min<int64_t>(nparts[static_cast<size_t>(i)], p0 + quota);
+        runs.push_back({std::min<int64_t>(L, p1 * partition_size) - p0 * partition_size, i,
+                        static_cast<int32_t>(p0), static_cast<int32_t>(p1)});
+      }
     }
+    // longest first; ties keep sequence order
+    std::stable_sort(runs.begin(), runs.end(),
+                     [](const Run& x, const Run& y) { return x.tokens > y.tokens; });
+    queue_of.assign(runs.size(), 0);
+    int64_t load[kQueues] = {};
+    for (size_t r = 0; r < runs.size(); ++r) {
+      int x = 0;
+      for (int k = 1; k < kQueues; ++k)
+        if (load[k] < load[x]) x = k;
+      load[x] += runs[r].tokens;
+      queue_of[r] = x;
+    }
+    return *std::max_element(load, load + kQueues);
+  };
+  // the longest runs that balance to within 1 %, else the best balance seen
+  // (the longer runs on a tie)
+  int64_t best_quota = 1, best_max = INT64_MAX;
+  for (int64_t quota = std::max<int64_t>(1, (n + kQueues - 1) / kQueues);; quota /= 2) {
+    const int64_t mx = deal(quota);
+    if (mx < best_max) {
+      best_max = mx;
+      best_quota = quota;
+    }
+    if (static_cast<double>(mx) * kQueues <= 1.01 * static_cast<double>(total) || quota == 1)
+      break;
   }
-  // longest first; ties keep sequence order
-  std::stable_sort(runs.begin(), runs.end(),
-                   [](const Run& x, const Run& y) { return x.tokens > y.tokens; });
+  deal(best_quota);
   std::vector<Item> full[kQueues], ragged[kQueues];
-  int64_t load[kQueues] = {};
-  for (const Run& r : runs) {
-    int x = 0;
-    for (int k = 1; k < kQueues; ++k)
-      if (load[k] < load[x]) x = k;
-    load[x] += r.tokens;
-    const int64_t L = context_lens[r.seq];
-    for (int32_t p = r.p0; p < r.p1; ++p) {
+  for (size_t r = 0; r < runs.size(); ++r) {
+    const Run& run = runs[r];
+    const int x = queue_of[r];
+    const int64_t L = context_lens[run.seq];
+    for (int32_t p = run.p0; p < run.p1; ++p) {
       const int32_t ntok =
           static_cast<int32_t>(std::min<int64_t>(partition_size, L - int64_t{p} * partition_size));
-      (ntok == partition_size ? full[x] : ragged[x]).push_back({r.seq, p, ntok});
+      (ntok == partition_size ? full[x] : ragged[x]).push_back({run.seq, p, ntok});
     }
   }
   size_t longest = 0;

@@ -117,32 +117,51 @@ def test_partitioned_rejects_on_host(kw, status):
 
 def test_partition_work_items():
     wl = pa.partition_work_items([1, 1024, 1025, 0, 512, 700], 512)
-    # 9 partitions: runs of at most ceil(9 / 8) = 2; longest run first to the
-    # lightest of 8 queues: seq 1 -> q0, seq 2 [0, 2) -> q1, seq 5 -> q2 (full
-    # then ragged), seq 4 -> q3, seq 0 -> q4, seq 2 [2, 3) -> q5; round-robin
-    assert wl.tolist() == [[1, 0], [2, 0], [5, 0], [4, 0], [0, 0], [2, 2], [1, 1], [2, 1], [5, 1]]
+    # 9 partitions, 3262 tokens: runs of ceil(9 / 8) = 2 leave a queue with
+    # 1024 tokens (> 1.01 x 3262 / 8), so single partitions, longest first, to
+    # the lightest queue: the six full ones to queues 0-5, (5, 1) to queue 6,
+    # (0, 0) and (2, 2) to queue 7; read out round-robin
+    assert wl.tolist() == [[1, 0], [1, 1], [2, 0], [2, 1], [4, 0], [5, 0], [5, 1], [0, 0], [2, 2]]
+    assert wl.tolist() == _work_list_model([1, 1024, 1025, 0, 512, 700], 512, None)
     assert pa.partition_work_items([5000], 512, max_parts=4).tolist() == [[0, p] for p in range(4)]
 
 
 def _work_list_model(lens, P, cap):
     """Plain-Python statement of the work list's definition: runs of at most
-    ceil(N / 8) partitions per sequence, longest first (stable) to the queue
-    with the fewest tokens; per queue its full partitions, then its ragged
-    ones longest first; queues read out round-robin."""
+    `quota` partitions per sequence, longest first (stable) to the queue with
+    the fewest tokens; quota = ceil(N / 8), halved until the largest queue
+    holds at most 1.01x the mean tokens (or quota 1; the best balance seen,
+    the longer runs on a tie); per queue its full partitions, then its
+    ragged ones longest first; queues read out round-robin."""
     nparts = [min(-(-L // P), cap) if cap is not None else -(-L // P) for L in lens]
     nparts = [n if L > 0 else 0 for n, L in zip(nparts, lens)]
-    quota = max(1, -(-sum(nparts) // 8))
-    runs = []
-    for i, (L, n) in enumerate(zip(lens, nparts)):
-        for p0 in range(0, n, quota):
-            p1 = min(n, p0 + quota)
-            runs.append((min(L, p1 * P) - p0 * P, i, p0, p1))
-    runs.sort(key=lambda r: -r[0])
+    total = sum(min(L, n * P) for L, n in zip(lens, nparts))
+
+    def deal(quota):
+        runs = []
+        for i, (L, n) in enumerate(zip(lens, nparts)):
+            for p0 in range(0, n, quota):
+                p1 = min(n, p0 + quota)
+                runs.append((min(L, p1 * P) - p0 * P, i, p0, p1))
+        runs.sort(key=lambda r: -r[0])
+        load, where = [0] * 8, []
+        for tok, *_ in runs:
+            x = load.index(min(load))
+            load[x] += tok
+            where.append(x)
+        return runs, where, max(load)
+
+    quota, best = max(1, -(-sum(nparts) // 8)), None
+    while True:
+        runs, where, mx = deal(quota)
+        if best is None or mx < best[0]:
+            best = (mx, quota)
+        if mx * 8.0 <= 1.01 * total or quota == 1:
+            break
+        quota = max(1, quota // 2)
+    runs, where, _ = deal(best[1])
     queues = [([], []) for _ in range(8)]
-    load = [0] * 8
-    for tok, i, p0, p1 in runs:
-        x = load.index(min(load))
-        load[x] += tok
+    for (tok, i, p0, p1), x in zip(runs, where):
         for part in range(p0, p1):
             ntok = min(P, lens[i] - part * P)
             queues[x][0 if ntok == P else 1].append((ntok, i, part))
@@ -194,6 +213,28 @@ def test_work_list_pins_sequences_to_one_xcd():
         res.setdefault(s, set()).add(pos % 8)
     assert sum(len(v) > 1 for v in res.values()) <= 8
     assert per_x.max() / per_x.mean() < 1.02
+
+
+def test_work_list_balances_few_equal_sequences():
+    """Nine equal contexts cannot be dealt whole to 8 XCDs evenly: the runs
+    shorten to single partitions, and the XCDs (list position mod 8) carry no
+    more tokens than with every sequence's partitions dealt round-robin."""
+    P, L = 512, 5000
+    wl = pa.partition_work_items(np.full(9, L, np.int32), P)
+    assert wl.tolist() == _work_list_model([L] * 9, P, None)
+
+    def per_xcd(items):
+        load = np.zeros(8)
+        for pos, (s, p) in enumerate(items):
+            load[pos % 8] += min(P, L - p * P)
+        return load
+
+    nparts = -(-L // P)
+    full = [(s, p) for s in range(9) for p in range(nparts - 1)]
+    rr = full + [(s, nparts - 1) for s in range(9)]       # round-robin by position
+    assert per_xcd(wl.tolist()).max() <= per_xcd(rr).max()
+    # whole sequences would have put two on one XCD: 2 x 5000 tokens
+    assert per_xcd(wl.tolist()).max() < 1.1 * 9 * L / 8
 
 
 def test_workspace_size_formula():
