@@ -250,13 +250,16 @@ int main(int argc, char** argv) {
   // the host work-list builder, with output buffers of exactly the stated
   // capacity (too small ones included: it must write only `capacity` items)
   for (int it = 0; it < 300; ++it) {
-    const int32_t ns = uni(0, 40);
+    // mostly small batches; some large ones, and some with one dominant
+    // context (the builder then cuts sequences into shorter runs)
+    const bool big = uni(0, 9) == 0;
+    const int32_t ns = big ? uni(0, 600) : uni(0, 40);
     const int32_t P = std::vector<int32_t>{16, 32, 64, 512, 1024}[uni(0, 4)];
     const int32_t max_parts = uni(0, 2) ? -1 : uni(1, 8);
     std::vector<int32_t> lens(ns);
     int64_t want = 0;
     for (int32_t i = 0; i < ns; ++i) {
-      lens[i] = uni(0, 5000);
+      lens[i] = (i == 0 && uni(0, 3) == 0) ? uni(0, 200000) : uni(0, 5000);
       int64_t parts = (lens[i] + P - 1) / P;
       if (max_parts >= 0 && parts > max_parts) parts = max_parts;
       want += parts;
