@@ -283,8 +283,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(decode attention would shard by sequence or by KV head; see the design notes)",
+        print("bench.py measures one GPU only: libpa has no multi-GPU path "
+              "(decode attention would shard by sequence or by KV head)",
               file=sys.stderr)
         sys.exit(2)
 

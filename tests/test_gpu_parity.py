@@ -39,7 +39,8 @@ def half_ulp(x, dtype):
 
 
 FP32_NOISE = 1e-4   # allowance for fp32 summation-order differences (outputs are O(1))
-# host threads for the oracle's full-size decodes (the GPU machine's CPU share is 16)
+# host threads for the oracle's full-size decodes (at most 16: the share of host
+# cores a one-GPU test host gives the run)
 ORACLE_THREADS = min(16, len(os.sched_getaffinity(0)))
 
 
