@@ -110,15 +110,18 @@ void check_invariants(const pa_allocator* a, const std::vector<int64_t>& live, i
     CHECK(b >= 0 && b < nb, "%s: free id %d", after, b);
     if (b >= 0 && b < nb) ++in_free[b];
   }
-  int32_t distinct = 0;
+  int32_t distinct = 0, shared = 0;
   for (int32_t b = 0; b < nb; ++b) {
     CHECK(s.refcounts[b] == uses[b], "%s: block %d refcount %d, %d table entries", after, b,
           s.refcounts[b], uses[b]);
     CHECK(in_free[b] <= 1, "%s: block %d in the pool %d times", after, b, in_free[b]);
     CHECK(!(in_free[b] && uses[b]), "%s: block %d both free and referenced", after, b);
     if (uses[b]) ++distinct;
+    if (uses[b] >= 2) ++shared;
   }
   CHECK(static_cast<int32_t>(s.free_list.size()) == pa_alloc_num_free(a), "%s: num_free", after);
+  CHECK(shared == pa_alloc_num_shared_blocks(a), "%s: %d shared blocks, the allocator counts %d",
+        after, shared, pa_alloc_num_shared_blocks(a));
   CHECK(static_cast<int32_t>(s.free_list.size()) + distinct == nb,
         "%s: %zu free + %d referenced != %d blocks", after, s.free_list.size(), distinct, nb);
 }
